@@ -1,0 +1,234 @@
+"""FP64 CPU oracle for the selected-token log-probability path.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the bench's
+``cpu_baseline`` leg are the only users.  The product path (the HIP library and its
+binding) never imports, links or calls anything in this directory, and this directory
+shares no code with it.
+
+The arithmetic lives in ``logp_oracle.c`` (plain C, double precision, loops in column
+order, one block of rows per thread).  This module only builds that file with gcc and
+marshals numpy arrays into it.
+
+Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``):
+  forward, backward, tile_partials, merge, rne_bf16, count_bad_targets: pinned.
+  Rows whose valid target logit is -inf while other logits are finite, and rows that
+  hold NaN or +inf logits: parity unpinned (no closed form was written for them).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional
+
+import numpy as np
+
+TILE = 4096  # tile width used by the partial checker (same numeric value as the kernels')
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "logp_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblogp_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile ``logp_oracle.c`` into ``liblogp_oracle.so`` next to it (gcc, -O2)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-fPIC", "-shared", "-pthread",
+               "-fno-fast-math", "-ffp-contract=off", "-fvisibility=hidden",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def load_library(path: str):
+    """Load a compiled oracle shared object and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    _declare(lib)
+    return lib
+
+
+def _load(lib=None):
+    global _lib
+    if lib is not None:
+        return lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or \
+                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build()
+            _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def _declare(lib) -> None:
+    lib.oracle_rne_bf16.restype = ctypes.c_uint16
+    lib.oracle_rne_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_rne_bf16_array.restype = None
+    lib.oracle_rne_bf16_array.argtypes = [_P, _P, _I64]
+    lib.oracle_forward.restype = ctypes.c_int
+    lib.oracle_forward.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P,
+                                   ctypes.c_int]
+    lib.oracle_backward.restype = ctypes.c_int
+    lib.oracle_backward.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _P, _I64,
+                                    _P, _I64, ctypes.c_int]
+    lib.oracle_tile_partials.restype = ctypes.c_int
+    lib.oracle_tile_partials.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I64, _P,
+                                         _P, _P, ctypes.c_int]
+    lib.oracle_merge.restype = ctypes.c_int
+    lib.oracle_merge.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _P]
+    lib.oracle_count_bad_targets.restype = ctypes.c_int64
+    lib.oracle_count_bad_targets.argtypes = [_P, _P, _I64, _I64, _I64]
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _bits(logits) -> np.ndarray:
+    """BF16 logits as a C-contiguous uint16 array of raw bits, shape [n, ld]."""
+    try:
+        import torch
+        if isinstance(logits, torch.Tensor):
+            t = logits.detach()
+            if t.dtype != torch.bfloat16:
+                raise TypeError("oracle expects bfloat16 logits")
+            t = t.cpu().contiguous()
+            return t.view(torch.int16).numpy().view(np.uint16)
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(logits)
+    if a.dtype != np.uint16:
+        raise TypeError("oracle expects raw BF16 bits as uint16")
+    return a
+
+
+def _np(x, dtype) -> Optional[np.ndarray]:
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid arguments")
+
+
+# ------------------------------------------------------------------ entry points
+
+def rne_bf16(values, lib=None) -> np.ndarray:
+    """Round FP64 values to BF16 (nearest, ties to even) directly; returns uint16 bits."""
+    a = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load(lib).oracle_rne_bf16_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def forward(logits, targets, vocab_real: int, active=None, ignore_index: int = -100,
+            nthreads: Optional[int] = None, lib=None) -> dict:
+    """FP64 logp, LSE, row max M and row sum-exp S for every row."""
+    x = _bits(logits)
+    n, ld = (x.shape[0], x.shape[1]) if x.ndim == 2 else (0, vocab_real)
+    y = _np(targets, np.int64)
+    act = _np(active, np.uint8)
+    out = {k: np.empty(n, dtype=np.float64) for k in ("logp", "lse", "max", "sumexp")}
+    rc = _load(lib).oracle_forward(_ptr(x), ld, n, vocab_real, _ptr(y), _ptr(act), ignore_index,
+                                _ptr(out["logp"]), _ptr(out["lse"]), _ptr(out["max"]),
+                                _ptr(out["sumexp"]), nthreads or default_threads())
+    _check(rc, "forward")
+    return out
+
+
+def backward(logits, targets, grad, vocab_real: int, vocab_padded: Optional[int] = None,
+             active=None, ignore_index: int = -100, want_f64: bool = True,
+             want_bf16: bool = True, nthreads: Optional[int] = None, lib=None) -> dict:
+    """FP64 dlogits [n, vocab_padded] and/or its direct BF16 rounding (uint16 bits)."""
+    x = _bits(logits)
+    n, ld = x.shape
+    vocab_padded = vocab_real if vocab_padded is None else vocab_padded
+    y = _np(targets, np.int64)
+    act = _np(active, np.uint8)
+    g = _np(grad, np.float32)
+    d64 = np.empty((n, vocab_padded), dtype=np.float64) if want_f64 else None
+    db = np.empty((n, vocab_padded), dtype=np.uint16) if want_bf16 else None
+    rc = _load(lib).oracle_backward(_ptr(x), ld, n, vocab_real, vocab_padded, _ptr(y), _ptr(act),
+                                 ignore_index, _ptr(g), _ptr(d64), vocab_padded, _ptr(db),
+                                 vocab_padded, nthreads or default_threads())
+    _check(rc, "backward")
+    return {"d64": d64, "bf16": db}
+
+
+def num_tiles(vocab_padded: int, tile: int = TILE) -> int:
+    return -(-vocab_padded // tile)
+
+
+def tile_partials(logits, targets, vocab_real: int, vocab_padded: Optional[int] = None,
+                  active=None, ignore_index: int = -100, tile: int = TILE,
+                  nthreads: Optional[int] = None, lib=None) -> dict:
+    """FP64 per-tile (m, s, sel), each [n, ceil(vocab_padded / tile)]."""
+    x = _bits(logits)
+    n, ld = x.shape
+    vocab_padded = vocab_real if vocab_padded is None else vocab_padded
+    L = num_tiles(vocab_padded, tile)
+    y = _np(targets, np.int64)
+    act = _np(active, np.uint8)
+    out = {k: np.empty((n, L), dtype=np.float64) for k in ("max", "sumexp", "sel")}
+    rc = _load(lib).oracle_tile_partials(_ptr(x), ld, n, vocab_real, vocab_padded, tile, _ptr(y),
+                                      _ptr(act), ignore_index, _ptr(out["max"]),
+                                      _ptr(out["sumexp"]), _ptr(out["sel"]),
+                                      nthreads or default_threads())
+    _check(rc, "tile_partials")
+    return out
+
+
+def merge(m, s, sel, targets, vocab_real: int, active=None, ignore_index: int = -100,
+          tile: int = TILE, lib=None) -> dict:
+    """FP64 merge of per-tile partials in tile order -> logp, LSE."""
+    m = np.ascontiguousarray(m, dtype=np.float64)
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    sel = np.ascontiguousarray(sel, dtype=np.float64)
+    n, L = m.shape
+    y = _np(targets, np.int64)
+    act = _np(active, np.uint8)
+    out = {k: np.empty(n, dtype=np.float64) for k in ("logp", "lse")}
+    rc = _load(lib).oracle_merge(_ptr(m), _ptr(s), _ptr(sel), n, L, tile, vocab_real, _ptr(y),
+                              _ptr(act), ignore_index, _ptr(out["logp"]), _ptr(out["lse"]))
+    _check(rc, "merge")
+    return out
+
+
+def count_bad_targets(targets, vocab_real: int, active=None, ignore_index: int = -100,
+                      lib=None) -> int:
+    y = _np(targets, np.int64)
+    act = _np(active, np.uint8)
+    return int(_load(lib).oracle_count_bad_targets(_ptr(y), _ptr(act), y.size, vocab_real,
+                                                ignore_index))

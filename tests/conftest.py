@@ -1,0 +1,30 @@
+"""Shared pytest configuration: the ``gpu`` marker and repository imports."""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def _gpu_present() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available() and torch.cuda.device_count() > 0
+    except Exception:  # pragma: no cover
+        return False
+
+
+def pytest_collection_modifyitems(config, items):
+    if any("gpu" in item.keywords for item in items) and not _gpu_present():
+        skip = pytest.mark.skip(reason="no GPU visible to this process")
+        for item in items:
+            if "gpu" in item.keywords:
+                item.add_marker(skip)
