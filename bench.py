@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Bench of the selected-token log-probability hot path on one MI355X.
+
+One step = the whole path over one batch: logp_forward (tile loads, masking, tile max,
+tile sum-exp, selected logit, canonical merge) then logp_backward (BF16 dlogits), on the
+headline workload N=32768, V=151936, BF16 logits ~ N(0, 3^2) with 1% +30 spike rows,
+70% argmax / 30% uniform targets and g ~ N(0, 0.01^2).  Inputs and output buffers are
+resident in HBM before the timed region; the K timed steps are bracketed by
+torch.cuda.synchronize() and timed with HIP events on the stream the kernels run on.
+
+value = algorithmic bytes of one step / step time, in GB/s:
+    forward  2*N*V (logits once) + 24*N (targets, logp, LSE, stats)
+    backward 2*N_valid*V (logits once) + 2*N*V (dlogits) + 20*N (targets, g, stats)
+The roofline object reports the dominant kernel (the backward) against 8 TB/s.  The
+cpu_baseline object times the FP64 oracle on a bounded sample of the same rows.
+
+Extra flags: --profile-copy adds a plain device copy of known size (for scaling the
+hardware byte counters), --shard-path also times logp_partials + logp_merge.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PAGES_FWD_BWD_MS = 27.2  # fused kernel, B200, N=32768, V=151936, BF16 (context, not target)
+METRIC = "fwd+bwd ms and achieved HBM GB/s (% of peak), N=32768 V=151936 BF16"
+KERNEL_SOURCES = [os.path.join(ROOT, "deterministic_selected_token_amd", "csrc", f)
+                  for f in ("logp_kernels.hip", "logp_device.hpp")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_logp_backward_headline.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(n: int, n_valid: int, vocab_real: int, width: int, has_mask: bool):
+    mask = 1 if has_mask else 0
+    fwd = 2 * n * vocab_real + (24 + mask) * n
+    bwd = 2 * n_valid * vocab_real + 2 * n * width + (20 + mask) * n
+    return fwd, bwd
+
+
+def traffic_for_backward():
+    """Measured HBM bytes per backward launch from the committed counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("scaled_bytes_per_launch")
+
+
+def git_sha() -> str:
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                              capture_output=True, text=True, timeout=10).stdout.strip()
+    except Exception:
+        return ""
+
+
+def cpu_baseline(case, target_seconds: float) -> dict:
+    """The FP64 oracle (as it stands) on a bounded sample of the workload's rows."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    n = case.n
+    v = case.vocab_real
+
+    def run(rows):
+        idx = np.linspace(0, n - 1, rows).astype(np.int64)
+        host = case.logits[idx].cpu()
+        y = case.targets[idx].cpu().numpy()
+        g = case.grad[idx].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.forward(host, y, v, nthreads=threads)
+        oracle.backward(host, y, g, v, want_f64=False, want_bf16=True, nthreads=threads)
+        return time.perf_counter() - t0
+
+    rows = 16
+    dt = run(rows)
+    if dt < target_seconds / 4:
+        rows = int(min(n, max(rows, rows * target_seconds / max(dt, 1e-3))))
+        dt = run(rows)
+    fwd_b, bwd_b = algorithmic_bytes(rows, rows, v, v, False)
+    full_fwd, full_bwd = algorithmic_bytes(n, n, v, v, False)
+    gbs = (fwd_b + bwd_b) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {n} rows of the same workload, FP64 forward + backward "
+                      f"(dlogits rounded to BF16), {dt:.2f} s wall",
+            "ms_per_step_extrapolated": round((full_fwd + full_bwd) / (gbs * 1e9) * 1e3, 1)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample (0 disables it)")
+    ap.add_argument("--shard-path", action="store_true",
+                    help="also time logp_partials (4 shards) + logp_merge")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="run a 4 GiB device copy after the timed region (counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by rows or vocab tiles without any exchange in the hot loop, "
+              "see DESIGN.md", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: run as a single process (WORLD_SIZE > 1 is not supported)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import deterministic_selected_token_amd as dst
+    from workloads import headline_case
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print("bench: generating the headline workload", file=sys.stderr, flush=True)
+    case = headline_case(device=dev)
+    n, v = case.n, case.vocab_real
+    x, y, g = case.logits, case.targets, case.grad
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    stats = torch.empty((n, 2), dtype=torch.float32, device=dev)
+    dlogits = torch.empty((n, v), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dst.logp_forward(x, y, v, v, logp=logp, lse=lse, stats=stats, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dst.logp_backward(x, y, g, stats, v, v, dlogits=dlogits, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # peak memory of one step beyond the resident inputs and preallocated outputs: zero
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    step()
+    torch.cuda.synchronize()
+    step_extra = torch.cuda.max_memory_allocated() - base
+
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_ms = [a.elapsed_time(b) for a, b, _ in evs]
+    bwd_ms = [b.elapsed_time(c) for _, b, c in evs]
+    total_ms = evs[0][0].elapsed_time(evs[-1][2]) / args.steps
+
+    n_valid = n  # every headline row is active with an in-range target
+    fwd_b, bwd_b = algorithmic_bytes(n, n_valid, v, v, False)
+    value = (fwd_b + bwd_b) / (total_ms * 1e-3) / 1e9
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    achieved = bwd_b / (bwd_avg * 1e-3) / 1e9
+    traffic = traffic_for_backward()
+
+    extra = {}
+    if args.shard_path:
+        L = dst.logp_num_tiles(v)
+        partials = torch.empty((n, L, 3), dtype=torch.float32, device=dev)
+        layout = [(0, 13 * 4096), (13 * 4096, 26 * 4096), (26 * 4096, v)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for rep in range(2):
+            e[0].record(stream)
+            for c0, c1 in layout:
+                dst.logp_partials(x[:, c0:c1], y, v, v, c0, c1, partials, stream=stream)
+            e[1].record(stream)
+            dst.logp_merge(partials, y, v, stream=stream)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        extra["shard_path"] = {"shards": len(layout),
+                               "partials_ms": round(e[0].elapsed_time(e[1]), 4),
+                               "merge_ms": round(e[1].elapsed_time(e[2]), 4)}
+    if args.profile_copy:
+        src = torch.empty(1 << 31, dtype=torch.int16, device=dev)  # 4 GiB
+        dst_buf = torch.empty_like(src)
+        dst_buf.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_bytes_each_way"] = src.numel() * 2
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("bench: timing the oracle sample on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(PAGES_FWD_BWD_MS / total_ms, 3),
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "headline: N=32768 V=151936 bf16 logits ~N(0,3^2), 1% +30 "
+                               "spike rows, targets 70% argmax / 30% uniform, g ~N(0,0.01^2)",
+                   "n": n, "vocab": v, "logits_dtype": "bf16", "grad_dtype": "bf16",
+                   "fwd_ms": round(fwd_avg, 4), "bwd_ms": round(bwd_avg, 4),
+                   "wall_ms_per_step": round(wall_ms, 4),
+                   "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_b},
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "step_extra_bytes_beyond_outputs": int(step_extra),
+                   "device": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                   "torch": torch.__version__, "hip": torch.version.hip, "git": git_sha(),
+                   **extra},
+        "roofline": {"bound": "hbm", "kernel": "bwd_kernel (logp_backward)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bwd_b,
+                     "avg_launch_ms": round(bwd_avg, 4),
+                     "fwd_kernel": {"achieved": round(fwd_b / (fwd_avg * 1e-3) / 1e9, 2),
+                                    "avg_launch_ms": round(fwd_avg, 4),
+                                    "algorithmic_bytes_per_launch": fwd_b}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

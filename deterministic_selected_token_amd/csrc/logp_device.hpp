@@ -1,0 +1,212 @@
+// Device building blocks shared by every kernel of the selected-token log-probability
+// library, for gfx950 (CDNA4, wave64).
+//
+// This file IS the numerical contract: the tile shape and lane mapping, the per-tile
+// (max, sum-exp) reduction, the fixed lane tree, the canonical merge and the exp/log used
+// by them.  The fused forward, the shard-partials kernel and the merge kernel all call the
+// same functions below, so their results are bitwise identical.
+//
+// Sources: per-tile (m, s) partials and the merge M = max m_l, S = sum s_l exp(m_l - M),
+// LSE = M + log S follow RL-Kernel issue #241 ("[WS2] TP-aware deterministic logprob",
+// section "PR 3") and PR #314 ("[WS2][Logp] Deterministic config option", Tensor Parallel
+// doc, steps 1-6: fixed global tiles, identical tile shape on any rank, fixed merge order,
+// owner-copied target logit).  FP32 arithmetic for max / sum-exp / exp / log follows issue
+// #241, section Goal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace logp {
+
+constexpr int kTile = 4096;    // global tile width in columns
+constexpr int kWave = 64;      // lanes per wavefront
+constexpr int kLoads = 8;      // 16-byte loads per lane per tile
+constexpr int kVec = 8;        // BF16 values per 16-byte load
+constexpr int kPerLane = kLoads * kVec;  // 64 values per lane per tile
+static_assert(kWave * kPerLane == kTile, "a tile is exactly one wave's load footprint");
+constexpr int kLoadStride = kWave * kVec;  // 512 columns between a lane's consecutive loads
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.44269504088896340736f;       // fl32(log2 e)
+constexpr float kLog2eHi = 1.44269502162933349609375f;  // 0x3FB8AA3B = fl32(log2 e)
+constexpr float kLog2eLo = 1.925963033500011e-08f;      // fl32(log2 e - kLog2eHi)
+constexpr float kLn2 = 0.693147180559945309417f;
+
+// ------------------------------------------------------------------ BF16 unpacking
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load or store
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// The tile held by one wave: v[8*k + e] is column tile_start + 512*k + 8*lane + e.
+struct TileRegs {
+    float v[kPerLane];
+};
+
+__device__ __forceinline__ void unpack8(const u32x4& w, float* out) {
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+    out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z);
+    out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+}
+
+// Loads one tile of a row into registers.  `row` points at view column 0, `start` is the
+// tile's first view column and `lim` the number of real columns in the view: columns at
+// or past `lim` read as -inf and are never touched in memory.  VEC selects 16-byte loads
+// (requires a 16-byte aligned row start); otherwise every value is a 2-byte load.  Both
+// paths fill the registers identically, so results never depend on alignment.
+template <bool VEC>
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ row, int start, int lim,
+                                          int lane, TileRegs& t) {
+    const int base = start + kVec * lane;
+    if (start + kTile <= lim) {
+        if constexpr (VEC) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(row + base);
+            u32x4 w[kLoads];
+#pragma unroll
+            for (int k = 0; k < kLoads; ++k)
+                w[k] = __builtin_nontemporal_load(p + k * (kLoadStride / kVec));
+#pragma unroll
+            for (int k = 0; k < kLoads; ++k) unpack8(w[k], &t.v[k * kVec]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kLoads; ++k)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e)
+                    t.v[k * kVec + e] = bf16_to_f32(row[base + k * kLoadStride + e]);
+        }
+        return;
+    }
+    // Tile that ends past the last real column (or lies wholly in padding).
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const int c = base + k * kLoadStride;
+        if (VEC && c + kVec <= lim) {
+            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c));
+            unpack8(w, &t.v[k * kVec]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e)
+                t.v[k * kVec + e] = (c + e < lim) ? bf16_to_f32(row[c + e]) : kNegInf;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ lane tree
+
+// Pairwise tree over lanes 0..63 in index order: partners at xor 1, 2, 4, 8, 16, 32.
+// After each step both partners hold the same value (max and + are commutative), so every
+// lane ends with identical bits.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v = v + __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// ------------------------------------------------------------------ exp / log
+
+// exp(t) for the forward's sum-exp terms and merge weights: 2^(fl(t * log2 e)) on the
+// hardware exp2.  t <= 0 always; exp(-inf) = 0.
+__device__ __forceinline__ float fwd_exp(float t) { return __builtin_amdgcn_exp2f(t * kLog2e); }
+
+// Natural log used by the merge (accurate library logf).
+__device__ __forceinline__ float canon_log(float s) { return logf(s); }
+
+// exp(t) for the backward's softmax, t in [-128, 0]: t*log2(e) is carried as u + r with
+// u = fl(t * hi(log2 e)) and r = the exact product residual plus t * lo(log2 e); then
+// exp(t) = 2^u * 2^r ~= 2^u + 2^u * r * ln 2.  This removes the rounding of the exponent
+// argument (up to ~2^-17 absolute for |u| near 185) that a plain exp2(t*log2e) carries.
+__device__ __forceinline__ float bwd_exp(float t) {
+    const float u = t * kLog2eHi;
+    const float r0 = __builtin_fmaf(t, kLog2eHi, -u);
+    const float r = __builtin_fmaf(t, kLog2eLo, r0);
+    const float e0 = __builtin_amdgcn_exp2f(u);
+    return __builtin_fmaf(e0, r * kLn2, e0);
+}
+
+// ------------------------------------------------------------------ tile statistics
+
+// (m, s) of one tile held in registers: m = max over the tile (exact), s = sum of
+// exp(x - m) with each lane adding its 64 values in index order from +0, then the lane tree.
+// A tile with no real column gives the (-inf, 0) identity.
+__device__ __forceinline__ void tile_stats(const TileRegs& t, float& m, float& s) {
+    float lm = t.v[0];
+#pragma unroll
+    for (int i = 1; i < kPerLane; ++i) lm = fmaxf(lm, t.v[i]);
+    m = wave_max(lm);
+    float ls = 0.0f;
+    if (m != kNegInf) {
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) ls = ls + fwd_exp(t.v[i] - m);
+    }
+    s = wave_sum(ls);
+}
+
+// ------------------------------------------------------------------ canonical merge
+
+// Merge of per-tile (m_l, s_l), l in [0, L), read through `src.m(l)` / `src.s(l)` by one
+// wave: M = max m_l; w_l = 0 for an identity tile (m_l = -inf), else s_l * exp(m_l - M);
+// lane i adds w_i, w_{i+64}, ... in order from +0; the lane tree gives S.  Trailing
+// identity tiles add +0 to a lane's running sum and leave M unchanged, so S and M do not
+// depend on how many of them there are.
+template <class Src>
+__device__ __forceinline__ void canonical_merge(const Src& src, int L, int lane, float& M,
+                                                float& S) {
+    float lm = kNegInf;
+    for (int l = lane; l < L; l += kWave) lm = fmaxf(lm, src.m(l));
+    M = wave_max(lm);
+    float ls = 0.0f;
+    if (M != kNegInf) {
+        for (int l = lane; l < L; l += kWave) {
+            const float ml = src.m(l);
+            const float w = (ml == kNegInf) ? 0.0f : src.s(l) * fwd_exp(ml - M);
+            ls = ls + w;
+        }
+    }
+    S = wave_sum(ls);
+}
+
+struct RowResult {
+    float logp, lse, max, sumexp;
+};
+
+// LSE = M + log S; logp = (sel - M) - log S for a valid row, 0 for an invalid one.
+// M = -inf (no finite real logit) gives LSE = -inf and logp = -inf for a valid row.
+__device__ __forceinline__ RowResult finalize_row(float M, float S, bool valid, float sel) {
+    RowResult r;
+    r.max = M;
+    r.sumexp = S;
+    if (M == kNegInf) {
+        r.lse = kNegInf;
+        r.logp = valid ? kNegInf : 0.0f;
+    } else {
+        const float log_s = canon_log(S);
+        r.lse = M + log_s;
+        r.logp = valid ? (sel - M) - log_s : 0.0f;
+    }
+    return r;
+}
+
+// Row validity: active (or no mask), target != ignore_index and 0 <= target < vocab_real.
+__device__ __forceinline__ bool row_valid(const int64_t* __restrict__ targets,
+                                          const uint8_t* __restrict__ active,
+                                          int64_t ignore_index, int64_t vocab_real, int64_t row,
+                                          int64_t& y) {
+    y = targets[row];
+    if (active != nullptr && active[row] == 0) return false;
+    if (y == ignore_index) return false;
+    return y >= 0 && y < vocab_real;
+}
+
+}  // namespace logp

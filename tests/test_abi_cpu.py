@@ -1,0 +1,194 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/logp.h declares, and rejects bad arguments on the host before any HIP call."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "logp.h")
+PKG = os.path.join(ROOT, "deterministic_selected_token_amd")
+
+import deterministic_selected_token_amd as dst  # noqa: E402
+
+OK, NULL, SHAPE, SHARD = 0, 1, 2, 3
+T = 4096
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails host checks
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    return re.findall(r"^LOGP_API\s+[\w\s\*]+?\b(logp_\w+)\s*\(", text, flags=re.M)
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert sorted(names) == sorted(dst.EXPORTED)
+    lib = ctypes.CDLL(dst.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", dst.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(logp_\w+)$", out, flags=re.M))
+    assert exported == set(names)  # nothing else with the prefix leaks out
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert re.search(r"#define LOGP_TILE_COLS (\d+)", text).group(1) == str(dst.TILE_COLS)
+    assert re.search(r"#define LOGP_FWD_MAX_TILES (\d+)", text).group(1) == \
+        str(dst.FWD_MAX_TILES)
+    for code, name in dst.STATUS.items():
+        assert re.search(rf"{name}\s*=\s*{code}\b", text), name
+
+
+def test_library_is_built_for_gfx950():
+    # The offload bundle inside the shared object names its target.
+    blob = open(dst.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_num_tiles_and_status_strings():
+    assert dst.logp_num_tiles(151936) == 38
+    assert dst.logp_num_tiles(152064) == 38
+    assert dst.logp_num_tiles(159744) == 39
+    assert dst.logp_num_tiles(4096) == 1 and dst.logp_num_tiles(4097) == 2
+    assert dst.logp_num_tiles(1) == 1 and dst.logp_num_tiles(0) == 0
+    for code in range(8):
+        s = dst.logp_status_string(code)
+        assert s and (code == 0) == (s == "ok")
+    assert dst.logp_status_string(99) == "unknown status"
+
+
+def fwd(**kw):
+    a = dict(logits=FAKE, ld=152064, n=4, vocab_real=151936, vocab_padded=152064,
+             targets=FAKE, active=None, ignore_index=-100, logp=FAKE, lse=None, stats=None,
+             stream=None)
+    a.update(kw)
+    return dst.library().logp_forward(*a.values())
+
+
+def bwd(**kw):
+    a = dict(logits=FAKE, ld=151936, n=4, vocab_real=151936, vocab_padded=151936, col_begin=0,
+             col_end=151936, targets=FAKE, active=None, ignore_index=-100, grad=FAKE,
+             stats=FAKE, dlogits=FAKE, ld_out=151936, stream=None)
+    a.update(kw)
+    return dst.library().logp_backward(*a.values())
+
+
+def part(**kw):
+    a = dict(logits=FAKE, ld=159744, n=4, vocab_real=151936, vocab_padded=159744, col_begin=0,
+             col_end=159744, targets=FAKE, active=None, ignore_index=-100, partials=FAKE,
+             ldp=39, stream=None)
+    a.update(kw)
+    return dst.library().logp_partials(*a.values())
+
+
+def merge(**kw):
+    a = dict(partials=FAKE, ldp=39, n=4, num_tiles=39, vocab_real=151936, targets=FAKE,
+             active=None, ignore_index=-100, logp=FAKE, lse=None, stats=None, stream=None)
+    a.update(kw)
+    return dst.library().logp_merge(*a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n=-1), SHAPE), (dict(vocab_real=0), SHAPE), (dict(vocab_padded=100), SHAPE),
+    (dict(ld=152000), SHAPE), (dict(vocab_padded=2 ** 31 - T, ld=2 ** 31), SHAPE),
+    (dict(vocab_real=T * 4096 + 1, vocab_padded=T * 4096 + 1, ld=T * 4097), SHAPE),
+    (dict(n=2 ** 31), SHAPE),
+    (dict(n=0), OK), (dict(n=0, logits=None, targets=None, logp=None), OK),
+    (dict(logits=None), NULL), (dict(targets=None), NULL), (dict(logp=None), NULL),
+])
+def test_forward_host_validation(kw, want):
+    assert fwd(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n=-1), SHAPE), (dict(vocab_real=0), SHAPE), (dict(col_begin=-1), SHARD),
+    (dict(col_end=151937), SHARD), (dict(col_begin=100, col_end=99), SHARD),
+    (dict(ld=1000), SHAPE), (dict(ld_out=1000), SHAPE),
+    (dict(n=0), OK), (dict(col_begin=500, col_end=500), OK),
+    (dict(logits=None), NULL), (dict(stats=None), NULL), (dict(grad=None), NULL),
+    (dict(dlogits=None), NULL), (dict(targets=None), NULL),
+    # the backward accepts any sub-range, aligned or not: these fail later, not as SHARD
+    (dict(col_begin=3, col_end=1000, logits=None), NULL),
+])
+def test_backward_host_validation(kw, want):
+    assert bwd(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(col_begin=100), SHARD), (dict(col_begin=T, col_end=T + 100), SHARD),
+    (dict(col_begin=T, col_end=T), SHARD), (dict(col_end=159745), SHARD),
+    (dict(col_begin=-T), SHARD), (dict(ldp=38), SHAPE), (dict(ld=100), SHAPE),
+    (dict(vocab_padded=151935), SHAPE), (dict(n=0), OK),
+    (dict(partials=None), NULL), (dict(targets=None), NULL),
+    # valid shard bounds (interior multiples of T; the last may end at vocab_padded):
+    # with a NULL logits pointer they stop at the NULL check, after the shard check
+    (dict(col_begin=T * 38, col_end=159744, logits=None), NULL),
+    (dict(col_begin=T * 13, col_end=T * 26, logits=None), NULL),
+    (dict(vocab_padded=159000, col_begin=T * 38, col_end=159000, ld=159000, logits=None),
+     NULL),
+])
+def test_partials_host_validation(kw, want):
+    assert part(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(num_tiles=37), SHAPE), (dict(ldp=38), SHAPE), (dict(n=-2), SHAPE),
+    (dict(vocab_real=0), SHAPE), (dict(n=0), OK), (dict(partials=None), NULL),
+    (dict(logp=None), NULL),
+])
+def test_merge_host_validation(kw, want):
+    assert merge(**kw) == want
+
+
+def test_check_targets_host_validation():
+    lib = dst.library()
+    assert lib.logp_check_targets(FAKE, None, -1, 10, -100, FAKE, None) == SHAPE
+    assert lib.logp_check_targets(FAKE, None, 5, 0, -100, FAKE, None) == SHAPE
+    assert lib.logp_check_targets(FAKE, None, 5, 10, -100, None, None) == NULL
+    assert lib.logp_check_targets(None, None, 5, 10, -100, FAKE, None) == NULL
+
+
+def test_binding_rejects_cpu_tensors_without_calling_the_library():
+    import torch
+    x = torch.zeros((2, 8), dtype=torch.bfloat16)
+    y = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dst.logp_forward(x, y)
+    with pytest.raises(TypeError):
+        dst.logp_forward(x.float(), y)
+
+
+def test_product_path_never_imports_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "logp_oracle" not in text, f
+    text = open(HEADER).read()
+    assert "oracle" not in text.lower()
+
+
+def test_import_fails_loudly_without_the_library():
+    tmp = tempfile.mkdtemp(prefix="nolib_")
+    try:
+        dst_pkg = os.path.join(tmp, "deterministic_selected_token_amd")
+        os.makedirs(dst_pkg)
+        shutil.copy(os.path.join(PKG, "__init__.py"), dst_pkg)
+        r = subprocess.run([sys.executable, "-c", "import deterministic_selected_token_amd"],
+                           cwd=tmp, capture_output=True, text=True,
+                           env=dict(os.environ, PYTHONPATH=tmp))
+        assert r.returncode != 0 and "is missing: build it first" in r.stderr
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)

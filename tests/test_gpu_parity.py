@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path, called through the C ABI, against the FP64 oracle.
+
+Every case prints its name before touching the GPU.  Sizes are small enough for the
+oracle to finish in seconds while still spanning several 4096-column tiles and a ragged
+tail; the full-size workloads are checked on sampled rows (all rows for the forward).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import deterministic_selected_token_amd as dst
+import oracle
+from parity_checks import BackwardTally, bits_of, check_forward
+from workloads import headline_case, mid_case, random_case, tiny_case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg: str):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def run(case, dlogits=None):
+    """Forward then backward through the C ABI; returns GPU tensors."""
+    x = case.logits[:, :case.vocab_padded]
+    logp, lse, stats = dst.logp_forward(x, case.targets, case.vocab_real, case.vocab_padded,
+                                        active=case.active, ignore_index=case.ignore_index)
+    d = dst.logp_backward(x, case.targets, case.grad, stats, case.vocab_real,
+                          case.vocab_padded, active=case.active,
+                          ignore_index=case.ignore_index, dlogits=dlogits)
+    torch.cuda.synchronize()
+    return logp, lse, stats, d
+
+
+def full_check(case, rows=None, block=512):
+    """Forward on every row, backward element-wise on `rows` (default: all)."""
+    say(f"{case.name}: n={case.n} V={case.vocab_real} P={case.vocab_padded} ld={case.ld}")
+    logp, lse, stats, d = run(case)
+    host = case.logits.cpu()
+    y = case.targets.cpu().numpy()
+    act = None if case.active is None else case.active.cpu().numpy()
+    g = case.grad.cpu().numpy()
+    fwd = check_forward(host, y, case.vocab_real, act, case.ignore_index, logp.cpu().numpy(),
+                        lse.cpu().numpy(), stats.cpu().numpy(), case.name)
+    rows = np.arange(case.n) if rows is None else np.asarray(rows)
+    tally = BackwardTally()
+    for r0 in range(0, rows.size, block):
+        r = rows[r0:r0 + block]
+        rt = torch.from_numpy(r)
+        tally.add_block(host[rt], y[r], g[r], case.vocab_real, case.vocab_padded,
+                        None if act is None else act[r], case.ignore_index,
+                        bits_of(d[rt.to(DEV)]), case.name)
+    bwd = tally.finish(case.name)
+    say(f"{case.name}: fwd {fwd} bwd {bwd}")
+    return logp, lse, stats, d, fwd, bwd
+
+
+# ------------------------------------------------------------------ small and tiny
+
+def test_tiny_config():
+    case = tiny_case(device=DEV)
+    logp, lse, stats, d, _, _ = full_check(case)
+    r_eq = case.meta["equal_row"]
+    V = case.vocab_real
+    # a row of equal logits gives -log V (within a few FP32 ulps of it)
+    assert abs(float(logp[r_eq]) + np.log(V)) <= 2e-6
+    assert float(stats[r_eq, 1]) == V
+    ign = case.meta["ignored_rows"]
+    assert torch.all(logp[ign] == 0) and torch.all(d[ign].view(torch.int16) == 0)
+
+
+SMALL = [
+    # n, vocab_real, vocab_padded, ld, sigma, pad_fill, inactive, ignore, bad targets
+    (33, 10000, 10000, 10000, 3.0, float("-inf"), 0.0, 0.0, 0.0),      # ragged last tile
+    (37, 10007, 10007, 10007, 3.0, float("-inf"), 0.1, 0.1, 0.1),      # odd ld: 2-byte path
+    (16, 4096, 4096, 4096, 2.0, float("-inf"), 0.0, 0.0, 0.0),         # exactly one tile
+    (9, 1, 1, 1, 1.0, float("-inf"), 0.0, 0.0, 0.0),                   # V = 1
+    (12, 255, 255, 255, 3.0, float("-inf"), 0.0, 0.2, 0.0),
+    (12, 1031, 1031, 1031, 3.0, float("-inf"), 0.0, 0.0, 0.2),
+    (20, 8200, 8704, 8704, 3.0, 100.0, 0.2, 0.1, 0.15),                # padding holds +100
+    (25, 12288, 16384, 16400, 3.0, 7.0, 0.0, 0.0, 0.2),                # all-padding tile
+    (40, 151936, 152064, 152064, 3.0, float("-inf"), 0.05, 0.05, 0.05),  # Qwen shape
+    (3, 300, 300, 300, 40.0, float("-inf"), 0.0, 0.0, 0.0),            # very spread logits
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[f"n{s[0]}_v{s[1]}_p{s[2]}_ld{s[3]}" for s in SMALL])
+def test_small_shapes(spec):
+    n, v, p, ld, sigma, fill, inact, ign, bad = spec
+    case = random_case(n, v, p, ld=ld, sigma=sigma, seed=n * 7 + v, pad_fill=fill,
+                       inactive_frac=inact, ignore_frac=ign, bad_target_frac=bad, device=DEV)
+    full_check(case)
+
+
+def test_rows_of_minus_inf_and_masked_tails():
+    n, v = 6, 9000
+    x = torch.randn((n, v)) * 3
+    x[0, :] = float("-inf")                     # valid row with no finite logit
+    x[1, :] = float("-inf")                     # invalid row with no finite logit
+    x[2, 5000:] = float("-inf")                 # -inf masked vocab tail
+    x[3, :4096] = float("-inf")                 # a whole -inf tile
+    x[4, 1] = 50.0                              # dominant logit
+    logits = x.to(torch.bfloat16).to(DEV)
+    y = torch.tensor([3, -100, 17, 5000, 1, 8999], device=DEV)
+    g = torch.tensor([1.0, 1.0, -2.0, 0.5, 3.0, 1e-3], device=DEV)
+    say("minus-inf rows")
+    logp, lse, stats = dst.logp_forward(logits, y)
+    d = dst.logp_backward(logits, y, g, stats)
+    torch.cuda.synchronize()
+    assert float(logp[0]) == float("-inf") and float(lse[0]) == float("-inf")
+    assert float(stats[0, 0]) == float("-inf") and float(stats[0, 1]) == 0.0
+    assert float(logp[1]) == 0.0 and float(lse[1]) == float("-inf")
+    assert torch.all(d[:2].view(torch.int16) == 0)
+    assert torch.all(torch.isfinite(d.float()))
+    assert torch.all(d[2, 5000:].view(torch.int16) == 0)
+    host = logits.cpu()
+    check_forward(host[2:], y[2:].cpu().numpy(), v, None, -100, logp[2:].cpu().numpy(),
+                  lse[2:].cpu().numpy(), stats[2:].cpu().numpy(), "minus-inf rows")
+    t = BackwardTally()
+    t.add_block(host[2:], y[2:].cpu().numpy(), g[2:].cpu().numpy(), v, v, None, -100,
+                bits_of(d[2:]), "minus-inf rows")
+
+
+def test_invalid_rows_do_not_read_logits():
+    case = random_case(8, 5000, sigma=3.0, seed=3, device=DEV)
+    case.targets[[1, 4]] = -100
+    case.active = torch.ones(8, dtype=torch.uint8, device=DEV)
+    case.active[6] = 0
+    say("invalid rows hold NaN logits")
+    _, _, stats = dst.logp_forward(case.logits, case.targets, active=case.active)
+    poisoned = case.logits.clone()
+    poisoned[[1, 4, 6]] = float("nan")
+    d = dst.logp_backward(poisoned, case.targets, case.grad, stats, active=case.active)
+    torch.cuda.synchronize()
+    assert torch.all(d[[1, 4, 6]].view(torch.int16) == 0)
+    clean = dst.logp_backward(case.logits, case.targets, case.grad, stats, active=case.active)
+    assert torch.equal(d.view(torch.int16), clean.view(torch.int16))
+
+
+# ------------------------------------------------------------------ configured workloads
+
+def test_mid_config():
+    """N=4096, V=151936 padded to 152064 (-inf pads), 5% inactive rows, g = 1/N_active."""
+    case = mid_case(device=DEV)
+    full_check(case)
+
+
+def test_mid_config_garbage_padding_is_masked_by_index():
+    a = mid_case(device=DEV)
+    b = mid_case(device=DEV, pad_fill=100.0)
+    say("mid config, +100 in the padding columns")
+    ra, rb = run(a), run(b)
+    for u, w in zip(ra, rb):
+        assert torch.equal(u.view(torch.int32) if u.dtype == torch.float32 else
+                           u.view(torch.int16), w.view(torch.int32) if w.dtype == torch.float32
+                           else w.view(torch.int16))
+
+
+def test_headline_config_sampled():
+    """N=32768, V=151936: forward checked on every row, backward on 160 sampled rows
+    (all 328 spike rows' share of them included) against the oracle."""
+    case = headline_case(device=DEV)
+    rng = np.random.default_rng(0)
+    spike = np.asarray(case.meta["spike_row_index"][:32])
+    rows = np.unique(np.concatenate([rng.choice(case.n, 128, replace=False), spike,
+                                     [0, case.n - 1]]))
+    full_check(case, rows=rows, block=64)
+
+
+def test_pages_bench_workload_sampled():
+    """sigma = 1 logits, uniform targets, g = 1: the pull request's benchmark workload."""
+    case = headline_case(device=DEV, n=4096, pages_bench=True)
+    full_check(case, rows=np.arange(0, 4096, 64))

@@ -205,7 +205,8 @@ def headline_case(device="cuda", seed: int = 2, n: int = 32768, vocab: int = QWE
     targets = torch.where(take_argmax, amax, uniform)
     g = torch.randn((n,), generator=gen, device=device, dtype=torch.float32) * 0.01
     return Case("headline", logits, targets, None, g, vocab, vocab,
-                meta={"seed": seed, "sigma": 3.0, "spike_rows": n_spike})
+                meta={"seed": seed, "sigma": 3.0, "spike_rows": n_spike,
+                      "spike_row_index": sorted(spike_rows.cpu().tolist())})
 
 
 # -------------------------------------------------------------------------- shard
