@@ -28,10 +28,9 @@ static_assert(kWave * kPerLane == kTile, "a tile is exactly one wave's load foot
 constexpr int kLoadStride = kWave * kVec;  // 512 columns between a lane's consecutive loads
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kLog2e = 1.44269504088896340736f;       // fl32(log2 e)
-constexpr float kLog2eHi = 1.44269502162933349609375f;  // 0x3FB8AA3B = fl32(log2 e)
-constexpr float kLog2eLo = 1.925963033500011e-08f;      // fl32(log2 e - kLog2eHi)
-constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.44269504088896340736f;       // 0x3FB8AA3B = fl32(log2 e)
+constexpr float kLn2Hi = 0.693147182464599609375f;     // 0x3F317218 = fl32(ln 2)
+constexpr float kLn2Lo = -1.9046542e-09f;               // fl32(ln 2 - kLn2Hi)
 
 // ------------------------------------------------------------------ BF16 unpacking
 
@@ -123,16 +122,41 @@ __device__ __forceinline__ float fwd_exp(float t) { return __builtin_amdgcn_exp2
 // Natural log used by the merge (accurate library logf).
 __device__ __forceinline__ float canon_log(float s) { return logf(s); }
 
-// exp(t) for the backward's softmax, t in [-128, 0]: t*log2(e) is carried as u + r with
-// u = fl(t * hi(log2 e)) and r = the exact product residual plus t * lo(log2 e); then
-// exp(t) = 2^u * 2^r ~= 2^u + 2^u * r * ln 2.  This removes the rounding of the exponent
-// argument (up to ~2^-17 absolute for |u| near 185) that a plain exp2(t*log2e) carries.
-__device__ __forceinline__ float bwd_exp(float t) {
-    const float u = t * kLog2eHi;
-    const float r0 = __builtin_fmaf(t, kLog2eHi, -u);
-    const float r = __builtin_fmaf(t, kLog2eLo, r0);
-    const float e0 = __builtin_amdgcn_exp2f(u);
-    return __builtin_fmaf(e0, r * kLn2, e0);
+// exp(t) for the backward's softmax, returned as (2^u, delta) with exp(t) ~= 2^u (1 + delta):
+// u = fl(t * log2 e) and delta = t - u ln 2, formed with two FMAs (the first one is exact up
+// to a rounding far below 2^-24 of delta, since t - u*hi(ln 2) needs about 24 bits).  |delta|
+// stays below |t| 2^-24, so the dropped delta^2/2 term is under 2^-40 relative: the result
+// is within about one FP32 ulp of exp(t), where exp2(fl(t * log2 e)) alone is off by up to
+// |t| 2^-24 relative (tens of ulps near t = -40).
+struct ExpSplit {
+    float u, delta;
+};
+
+__device__ __forceinline__ ExpSplit bwd_exp_split(float t) {
+    ExpSplit r;
+    r.u = t * kLog2e;
+    const float d_hi = __builtin_fmaf(-r.u, kLn2Hi, t);
+    r.delta = __builtin_fmaf(-r.u, kLn2Lo, d_hi);
+    return r;
+}
+
+// -g/S * exp(x - M) for a tile in which every x - M >= -87 (so every exp is a normal float and
+// the single product rounds correctly even when it lands in the subnormal range).
+__device__ __forceinline__ float bwd_term(float x, float M, float neg_c) {
+    const ExpSplit s = bwd_exp_split(x - M);
+    const float e0 = __builtin_amdgcn_exp2f(s.u);
+    return __builtin_fmaf(e0, s.delta, e0) * neg_c;
+}
+
+// Same value for any x - M (including -inf).  Where 2^u would be subnormal (u < -126), where
+// the hardware exp2 returns zero, it is computed as 2^(u+64) (u + 64 is exact there) and
+// multiplied by neg_c_lo = neg_c * 2^-64, which rounds the product exactly as neg_c * e would.
+// For u >= -126 it performs the same operations as bwd_term, so both give identical bits.
+__device__ __forceinline__ float bwd_term_deep(float x, float M, float neg_c, float neg_c_lo) {
+    const ExpSplit s = bwd_exp_split(fmaxf(x - M, -150.0f));
+    const bool tiny = s.u < -126.0f;
+    const float e0 = __builtin_amdgcn_exp2f(tiny ? s.u + 64.0f : s.u);
+    return __builtin_fmaf(e0, s.delta, e0) * (tiny ? neg_c_lo : neg_c);
 }
 
 // ------------------------------------------------------------------ tile statistics

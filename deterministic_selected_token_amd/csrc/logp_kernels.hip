@@ -230,7 +230,8 @@ __global__ __launch_bounds__(kItemWaves* kWave) void bwd_kernel(
     TileRegs t;
     load_tile<VEC_IN>(logits + row * ld, start, lim, lane, t);
 
-    const float neg_c = -(g / S);  // -g/S, one rounding per row
+    const float neg_c = -(g / S);             // -g/S, one rounding per row
+    const float neg_c_lo = neg_c * 0x1p-64f;  // exact unless |g/S| < 2^-62
     const int64_t yl = y - col_begin;
     const bool has_target = yl >= start && yl < int64_t(start) + kTile && yl < lim;
     const int y_off = has_target ? static_cast<int>(yl - start) : 0;
@@ -238,14 +239,24 @@ __global__ __launch_bounds__(kItemWaves* kWave) void bwd_kernel(
     const int y_lane = (y_off % kLoadStride) / kVec;
     const int y_e = y_off % kVec;
 
+    // A tile whose every exp(x - M) is a normal float takes the short path; any lane holding
+    // x - M < -87 (a -inf, a padding column, a very low logit) sends the whole wave down the
+    // path that also handles subnormal results.  Both give the same bits wherever both apply.
+    float lmin = t.v[0];
+#pragma unroll
+    for (int i = 1; i < kPerLane; ++i) lmin = fminf(lmin, t.v[i]);
+    const bool deep = __any(lmin - M < -87.0f);
+
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
         float d[kVec];
+        if (!deep) {
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-            // exp underflows to 0 well before t = -128; the clamp keeps -inf logits finite
-            const float tt = fmaxf(t.v[k * kVec + e] - M, -128.0f);
-            d[e] = bwd_exp(tt) * neg_c;  // -g * p
+            for (int e = 0; e < kVec; ++e) d[e] = bwd_term(t.v[k * kVec + e], M, neg_c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e)
+                d[e] = bwd_term_deep(t.v[k * kVec + e], M, neg_c, neg_c_lo);
         }
         if (has_target && k == y_k && lane == y_lane) {
 #pragma unroll
