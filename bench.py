@@ -36,7 +36,7 @@ PAGES_FWD_BWD_MS = 27.2  # fused kernel, B200, N=32768, V=151936, BF16 (context,
 METRIC = "fwd+bwd ms and achieved HBM GB/s (% of peak), N=32768 V=151936 BF16"
 KERNEL_SOURCES = [os.path.join(ROOT, "deterministic_selected_token_amd", "csrc", f)
                   for f in ("logp_kernels.hip", "logp_device.hpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_logp_backward_headline.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bwd_kernels_headline_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -53,16 +53,17 @@ def algorithmic_bytes(n: int, n_valid: int, vocab_real: int, width: int, has_mas
     return fwd, bwd
 
 
-def traffic_for_backward():
-    """Measured HBM bytes per backward launch from the committed counter summary, or None
-    when the kernel sources changed since the counters were taken."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` ("fwd" or "bwd") from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by a 4 GiB copy), or None when the kernel sources have
+    changed since the counters were taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return rec.get("scaled_bytes_per_launch")
+    return rec.get("kernels", {}).get(kernel, {}).get("scaled_bytes_per_launch")
 
 
 def git_sha() -> str:
@@ -189,7 +190,6 @@ def main() -> int:
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     achieved = bwd_b / (bwd_avg * 1e-3) / 1e9
-    traffic = traffic_for_backward()
 
     extra = {}
     if args.shard_path:
@@ -247,12 +247,13 @@ def main() -> int:
                    **extra},
         "roofline": {"bound": "hbm", "kernel": "bwd_kernel (logp_backward)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("bwd"),
                      "algorithmic_bytes_per_launch": bwd_b,
                      "avg_launch_ms": round(bwd_avg, 4),
                      "fwd_kernel": {"achieved": round(fwd_b / (fwd_avg * 1e-3) / 1e9, 2),
                                     "avg_launch_ms": round(fwd_avg, 4),
-                                    "algorithmic_bytes_per_launch": fwd_b}},
+                                    "algorithmic_bytes_per_launch": fwd_b,
+                                    "traffic": measured_traffic("fwd")}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
