@@ -54,46 +54,52 @@ __device__ __forceinline__ void unpack8(const u32x4& w, float* out) {
     out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
 }
 
-// Loads one tile of a row into registers.  `row` points at view column 0, `start` is the
-// tile's first view column and `lim` the number of real columns in the view: columns at
-// or past `lim` read as -inf and are never touched in memory.  VEC selects 16-byte loads
-// (requires a 16-byte aligned row start); otherwise every value is a 2-byte load.  Both
-// paths fill the registers identically, so results never depend on alignment.
+constexpr uint32_t kNegInfBits = 0xFF80u;  // BF16 -inf
+
+// Raw BF16 bits of row[c], or -inf when c is at or past `lim` (never touched in memory).
+__device__ __forceinline__ uint32_t masked_bits(const uint16_t* __restrict__ row, int c, int lim) {
+    return c < lim ? static_cast<uint32_t>(row[c]) : kNegInfBits;
+}
+
+// Loads one tile of a row as raw BF16 bits: w[k] holds view columns
+// start + 512k + 8*lane + [0, 8).  `lim` is the number of real columns in the view: columns at
+// or past it read as -inf and are never touched in memory.  VEC allows 16-byte loads (it needs
+// a 16-byte aligned row start and is used for every 8 columns that are all real); otherwise
+// each value is a 2-byte load.  Both fill w[] with the same bits.  All loads of the tile are
+// issued before any of them is used.
 template <bool VEC>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ row, int start, int lim,
-                                          int lane, TileRegs& t) {
+__device__ __forceinline__ void load_tile_bits(const uint16_t* __restrict__ row, int start,
+                                               int lim, int lane, u32x4* w) {
     const int base = start + kVec * lane;
-    if (start + kTile <= lim) {
-        if constexpr (VEC) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(row + base);
-            u32x4 w[kLoads];
+    if (VEC && start + kTile <= lim) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + base);
 #pragma unroll
-            for (int k = 0; k < kLoads; ++k)
-                w[k] = __builtin_nontemporal_load(p + k * (kLoadStride / kVec));
-#pragma unroll
-            for (int k = 0; k < kLoads; ++k) unpack8(w[k], &t.v[k * kVec]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < kLoads; ++k)
-#pragma unroll
-                for (int e = 0; e < kVec; ++e)
-                    t.v[k * kVec + e] = bf16_to_f32(row[base + k * kLoadStride + e]);
-        }
+        for (int k = 0; k < kLoads; ++k)
+            w[k] = __builtin_nontemporal_load(p + k * (kLoadStride / kVec));
         return;
     }
-    // Tile that ends past the last real column (or lies wholly in padding).
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
         const int c = base + k * kLoadStride;
         if (VEC && c + kVec <= lim) {
-            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c));
-            unpack8(w, &t.v[k * kVec]);
+            w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c));
         } else {
-#pragma unroll
-            for (int e = 0; e < kVec; ++e)
-                t.v[k * kVec + e] = (c + e < lim) ? bf16_to_f32(row[c + e]) : kNegInf;
+            w[k].x = masked_bits(row, c + 0, lim) | (masked_bits(row, c + 1, lim) << 16);
+            w[k].y = masked_bits(row, c + 2, lim) | (masked_bits(row, c + 3, lim) << 16);
+            w[k].z = masked_bits(row, c + 4, lim) | (masked_bits(row, c + 5, lim) << 16);
+            w[k].w = masked_bits(row, c + 6, lim) | (masked_bits(row, c + 7, lim) << 16);
         }
     }
+}
+
+// The same tile as FP32 values (exact BF16 promotion; masked columns are -inf).
+template <bool VEC>
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ row, int start, int lim,
+                                          int lane, TileRegs& t) {
+    u32x4 w[kLoads];
+    load_tile_bits<VEC>(row, start, lim, lane, w);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) unpack8(w[k], &t.v[k * kVec]);
 }
 
 // ------------------------------------------------------------------ lane tree

@@ -29,7 +29,9 @@ using namespace logp;
 namespace {
 
 constexpr int kFwdWaves = 4;     // waves per forward workgroup (one row)
-constexpr int kItemWaves = 4;    // waves per workgroup of the per-(row, tile) kernels
+constexpr int kItemWaves = 4;    // waves per workgroup of the partials kernel
+constexpr int kBwdWaves = 16;    // waves per backward workgroup
+constexpr int kBwdTilesPerWave = 2;  // consecutive (row, tile) items per backward wave
 constexpr int kMergeWaves = 4;   // rows per merge workgroup
 constexpr int kCheckThreads = 1024;
 // Largest padded width: keeps vocab_padded + kTile below 2^31 so in-row column arithmetic
@@ -191,85 +193,128 @@ __device__ __forceinline__ void store8(uint16_t* out, int c, int width, const fl
     }
 }
 
+// Per-item (row, tile) state of the backward.
+struct BwdItem {
+    int64_t row, y;
+    int start;      // first view column of the tile
+    bool valid;     // row valid and its stats finite
+    float M, g, neg_c, neg_c_lo;
+};
+
+// Row-side inputs of one item: validity, (M, S), g and the per-row scale -g/S.  The stats and
+// g loads do not wait for the validity test (they are in bounds for every row), so one
+// memory round trip resolves all of them.
+__device__ __forceinline__ BwdItem bwd_item(int64_t item, int view_tiles,
+                                            const int64_t* __restrict__ targets,
+                                            const uint8_t* __restrict__ active,
+                                            int64_t ignore_index, int64_t vocab_real,
+                                            const float* __restrict__ grad,
+                                            const logp_stats_t* __restrict__ stats) {
+    BwdItem it;
+    it.row = item / view_tiles;
+    it.start = static_cast<int>(item - it.row * view_tiles) * kTile;
+    const float M = stats[it.row].max, S = stats[it.row].sumexp, g = grad[it.row];
+    it.valid = row_valid(targets, active, ignore_index, vocab_real, it.row, it.y) && M != kNegInf;
+    it.M = M;
+    it.g = g;
+    it.neg_c = -(g / S);                // -g/S, one rounding per row
+    it.neg_c_lo = it.neg_c * 0x1p-64f;  // exact unless |g/S| < 2^-62
+    return it;
+}
+
+// True when some value of the packed tile may lie below M - 87 (so exp(x - M) could fall
+// outside the normal range).  Works on raw BF16 bits: a negative value below the threshold
+// has larger unsigned bits than the threshold truncated toward zero, and false alarms only
+// select the slower path, which gives the same bits.
+__device__ __forceinline__ bool bwd_needs_deep(const u32x4* w, float M) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const float thr = M - 87.0f;
+    u16x2 mx = {0, 0};
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].x));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].y));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].z));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].w));
+    }
+    const unsigned t16 = 0x8000u | ((__float_as_uint(thr) >> 16) & 0x7FFFu);
+    return __any(thr >= 0.0f || mx.x > t16 || mx.y > t16);
+}
+
+// Gradient of the 8 columns at view column c of one item, from their logits v[0..7].
+template <bool DEEP>
+__device__ __forceinline__ void bwd_vec(const BwdItem& it, const float* v, int c, int lim,
+                                        bool partial, float* d) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e)
+        d[e] = DEEP ? bwd_term_deep(v[e], it.M, it.neg_c, it.neg_c_lo)
+                    : bwd_term(v[e], it.M, it.neg_c);
+    const int64_t yo = it.y - c;  // the target's offset from c (within this view)
+    if (yo >= 0 && yo < kVec) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+            if (e == yo) d[e] = it.g + d[e];  // g * (1 - p)
+    }
+    if (partial) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+            if (c + e >= lim) d[e] = 0.0f;  // padding and past-the-vocab columns
+    }
+}
+
 template <bool VEC_IN, bool VEC_OUT>
-__global__ __launch_bounds__(kItemWaves* kWave) void bwd_kernel(
+__global__ __launch_bounds__(kBwdWaves* kWave) void bwd_kernel(
     const uint16_t* logits, int64_t ld, int64_t n, int view_tiles, int width, int lim,
     int64_t col_begin, int64_t vocab_real, const int64_t* __restrict__ targets,
     const uint8_t* __restrict__ active, int64_t ignore_index, const float* __restrict__ grad,
     const logp_stats_t* __restrict__ stats, uint16_t* dlogits, int64_t ld_out) {
     // logits and dlogits may be the same buffer: every element is loaded into registers
     // before the lane that loaded it stores to it, and no other lane touches it.
-    const int64_t item = int64_t(blockIdx.x) * kItemWaves + wave_id();
-    if (item >= n * view_tiles) return;  // whole wave leaves; this kernel has no barrier
+    const int64_t first = (int64_t(blockIdx.x) * kBwdWaves + wave_id()) * kBwdTilesPerWave;
+    const int64_t total = n * view_tiles;
+    if (first >= total) return;  // whole wave leaves; this kernel has no barrier
     const int lane = lane_id();
-    const int64_t row = item / view_tiles;
-    const int j = static_cast<int>(item - row * view_tiles);
-    const int start = j * kTile;
-    const int base = start + kVec * lane;
-    uint16_t* out = dlogits + row * ld_out;
-    const bool full = start + kTile <= lim;  // every column of the tile is real
 
-    int64_t y;
-    bool valid = row_valid(targets, active, ignore_index, vocab_real, row, y);
-    float M = 0.0f, S = 1.0f, g = 0.0f;
-    if (valid) {
-        M = stats[row].max;
-        S = stats[row].sumexp;
-        g = grad[row];
-        valid = (M != kNegInf);  // no finite real logit: zero gradient, never NaN
-    }
-    if (!valid) {
-        float z[kVec];
+    BwdItem it[kBwdTilesPerWave];
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) z[e] = 0.0f;
+    for (int i = 0; i < kBwdTilesPerWave; ++i)
+        if (first + i < total)
+            it[i] = bwd_item(first + i, view_tiles, targets, active, ignore_index, vocab_real,
+                             grad, stats);
+    // Issue the loads of every tile this wave owns before computing any of them, so the
+    // second tile's bytes are in flight while the first is processed.  Invalid rows are not
+    // read.
+    u32x4 w[kBwdTilesPerWave][kLoads];
 #pragma unroll
-        for (int k = 0; k < kLoads; ++k) store8<VEC_OUT>(out, base + k * kLoadStride, width, z);
-        return;
-    }
-
-    TileRegs t;
-    load_tile<VEC_IN>(logits + row * ld, start, lim, lane, t);
-
-    const float neg_c = -(g / S);             // -g/S, one rounding per row
-    const float neg_c_lo = neg_c * 0x1p-64f;  // exact unless |g/S| < 2^-62
-    const int64_t yl = y - col_begin;
-    const bool has_target = yl >= start && yl < int64_t(start) + kTile && yl < lim;
-    const int y_off = has_target ? static_cast<int>(yl - start) : 0;
-    const int y_k = y_off / kLoadStride;
-    const int y_lane = (y_off % kLoadStride) / kVec;
-    const int y_e = y_off % kVec;
-
-    // A tile whose every exp(x - M) is a normal float takes the short path; any lane holding
-    // x - M < -87 (a -inf, a padding column, a very low logit) sends the whole wave down the
-    // path that also handles subnormal results.  Both give the same bits wherever both apply.
-    float lmin = t.v[0];
+    for (int i = 0; i < kBwdTilesPerWave; ++i)
+        if (first + i < total && it[i].valid)
+            load_tile_bits<VEC_IN>(logits + it[i].row * ld, it[i].start, lim, lane, w[i]);
 #pragma unroll
-    for (int i = 1; i < kPerLane; ++i) lmin = fminf(lmin, t.v[i]);
-    const bool deep = __any(lmin - M < -87.0f);
-
+    for (int i = 0; i < kBwdTilesPerWave; ++i) {
+        if (first + i >= total) break;
+        BwdItem t = it[i];
+        uint16_t* out = dlogits + t.row * ld_out;
+        const int base = t.start + kVec * lane;
+        if (!t.valid) {
+            float z[kVec];
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        float d[kVec];
-        if (!deep) {
+            for (int e = 0; e < kVec; ++e) z[e] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) d[e] = bwd_term(t.v[k * kVec + e], M, neg_c);
-        } else {
-#pragma unroll
-            for (int e = 0; e < kVec; ++e)
-                d[e] = bwd_term_deep(t.v[k * kVec + e], M, neg_c, neg_c_lo);
+            for (int k = 0; k < kLoads; ++k) store8<VEC_OUT>(out, base + k * kLoadStride, width, z);
+            continue;
         }
-        if (has_target && k == y_k && lane == y_lane) {
+        t.y -= col_begin;  // the target in view coordinates
+        const bool partial = t.start + kTile > lim;
+        const bool deep = bwd_needs_deep(w[i], t.M);  // masked columns (-inf) always count
 #pragma unroll
-            for (int e = 0; e < kVec; ++e)
-                if (e == y_e) d[e] = g + d[e];  // g * (1 - p)
+        for (int k = 0; k < kLoads; ++k) {
+            float v[kVec], d[kVec];
+            unpack8(w[i][k], v);
+            const int c = base + k * kLoadStride;
+            if (!deep) bwd_vec<false>(t, v, c, lim, partial, d);
+            else bwd_vec<true>(t, v, c, lim, partial, d);
+            store8<VEC_OUT>(out, c, width, d);
         }
-        const int c = base + k * kLoadStride;
-        if (!full) {
-#pragma unroll
-            for (int e = 0; e < kVec; ++e)
-                if (c + e >= lim) d[e] = 0.0f;  // padding and past-the-vocab columns
-        }
-        store8<VEC_OUT>(out, c, width, d);
     }
 }
 
@@ -424,10 +469,11 @@ logp_status_t check_vocab(int64_t n, int64_t vocab_real, int64_t vocab_padded) {
     return LOGP_OK;
 }
 
-// Grid size for one wave per (row, tile) item, or 0 if it does not fit a 1-D launch.
-uint32_t item_grid(int64_t n, int64_t tiles_per_row) {
+// Grid size for `items_per_block` (row, tile) items per workgroup, or 0 if it does not fit a
+// 1-D launch.
+uint32_t item_grid(int64_t n, int64_t tiles_per_row, int64_t items_per_block) {
     if (n > (int64_t(1) << 62) / tiles_per_row) return 0;
-    const int64_t blocks = ceil_div(n * tiles_per_row, kItemWaves);
+    const int64_t blocks = ceil_div(n * tiles_per_row, items_per_block);
     return blocks > 0x7FFFFFFF ? 0 : static_cast<uint32_t>(blocks);
 }
 
@@ -507,7 +553,7 @@ logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64
         return LOGP_ERR_NULL;
     const int64_t lim = std::max<int64_t>(0, std::min(vocab_real, col_end) - col_begin);
     const int64_t view_tiles = ceil_div(width, kTile);
-    const uint32_t grid = item_grid(n, view_tiles);
+    const uint32_t grid = item_grid(n, view_tiles, kBwdWaves * kBwdTilesPerWave);
     const uint64_t in_bytes = span_bytes(n, ld, lim, 2);
     const uint64_t out_bytes = span_bytes(n, ld_out, width, 2);
     if (grid == 0 || out_bytes == 0 || (lim > 0 && in_bytes == 0)) return LOGP_ERR_SHAPE;
@@ -540,7 +586,7 @@ logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64
                                 : reinterpret_cast<const void*>(&bwd_kernel<true, false>))
                         : (vout ? reinterpret_cast<const void*>(&bwd_kernel<false, true>)
                                 : reinterpret_cast<const void*>(&bwd_kernel<false, false>));
-    return launch(k, dim3(grid), dim3(kItemWaves * kWave), args, 0, stream);
+    return launch(k, dim3(grid), dim3(kBwdWaves * kWave), args, 0, stream);
 }
 
 logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
@@ -558,7 +604,7 @@ logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t n, int64
     if (n == 0) return LOGP_OK;
     if (logits == nullptr || targets == nullptr || partials == nullptr) return LOGP_ERR_NULL;
     const int64_t lim = std::max<int64_t>(0, std::min(vocab_real, col_end) - col_begin);
-    const uint32_t grid = item_grid(n, view_tiles);
+    const uint32_t grid = item_grid(n, view_tiles, kItemWaves);
     const uint64_t in_bytes = span_bytes(n, ld, lim, 2);
     const uint64_t part_bytes = span_bytes(n, ldp, view_tiles, sizeof(logp_partial_t));
     if (grid == 0 || part_bytes == 0 || (lim > 0 && in_bytes == 0)) return LOGP_ERR_SHAPE;
