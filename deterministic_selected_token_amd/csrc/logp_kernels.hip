@@ -318,6 +318,142 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_kernel(
     }
 }
 
+// Backward over a dense, 16-byte aligned view whose width is a multiple of 8 and at least
+// one tile: the view is treated as the flat sequence of its [n, width/8] 16-byte vectors and
+// every wave takes kBwdTilesPerWave chunks of 512 consecutive vectors (lane l holds vectors
+// 64k + l of a chunk, so each load instruction still covers 1 KiB of contiguous memory).
+// The element-wise formulas are those of bwd_kernel, so the bits are the same; this split
+// just gives every wave the same amount of work whatever the row width.  A chunk spans at
+// most two rows (width >= 4096 columns = 512 vectors).
+struct FlatRow {
+    bool valid;
+    float M, g, neg_c, neg_c_lo;
+    int y;         // target in view coordinates (any value when invalid)
+    unsigned t16;  // raw-bits threshold of the subnormal-safe path test
+};
+
+__device__ __forceinline__ FlatRow flat_row(int64_t row, int64_t col_begin, int64_t vocab_real,
+                                            const int64_t* __restrict__ targets,
+                                            const uint8_t* __restrict__ active,
+                                            int64_t ignore_index, const float* __restrict__ grad,
+                                            const logp_stats_t* __restrict__ stats) {
+    FlatRow r;
+    const float M = stats[row].max, S = stats[row].sumexp;
+    int64_t y;
+    r.valid = row_valid(targets, active, ignore_index, vocab_real, row, y) && M != kNegInf;
+    r.M = M;
+    r.g = grad[row];
+    r.neg_c = -(r.g / S);
+    r.neg_c_lo = r.neg_c * 0x1p-64f;
+    r.y = static_cast<int>(y - col_begin);
+    const float thr = M - 87.0f;
+    r.t16 = thr >= 0.0f ? 0u : (0x8000u | ((__float_as_uint(thr) >> 16) & 0x7FFFu));
+    return r;
+}
+
+template <bool DEEP>
+__device__ __forceinline__ void flat_vec(const FlatRow& r, const float* v, int col, int lim,
+                                         float* d) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e)
+        d[e] = DEEP ? bwd_term_deep(v[e], r.M, r.neg_c, r.neg_c_lo)
+                    : bwd_term(v[e], r.M, r.neg_c);
+    const int yo = r.y - col;
+    if (yo >= 0 && yo < kVec) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+            if (e == yo) d[e] = r.g + d[e];  // g * (1 - p)
+    }
+    if (col + kVec > lim) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+            if (col + e >= lim) d[e] = 0.0f;  // padding columns
+    }
+}
+
+__global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
+    const uint16_t* logits, int64_t ld, int64_t n, int vpr, int lim, int64_t col_begin,
+    int64_t vocab_real, const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
+    int64_t ignore_index, const float* __restrict__ grad, const logp_stats_t* __restrict__ stats,
+    uint16_t* dlogits, int64_t ld_out) {
+    // logits and dlogits may be the same buffer: each 16-byte vector is loaded and stored by
+    // the same lane, load first.
+    constexpr int kChunk = kWave * kLoads;  // 512 vectors per wave
+    const int64_t total = n * vpr;
+    const int64_t q0 = (int64_t(blockIdx.x) * kBwdWaves + wave_id()) * kChunk;
+    if (q0 >= total) return;  // whole wave leaves; this kernel has no barrier
+    const int lane = lane_id();
+
+    const int64_t row_a = q0 / vpr;
+    const int64_t sp = (row_a + 1) * vpr - q0;
+    const int split = sp < kChunk ? static_cast<int>(sp) : kChunk;  // vectors in row_a
+    const FlatRow ra = flat_row(row_a, col_begin, vocab_real, targets, active, ignore_index,
+                                grad, stats);
+    FlatRow rb = ra;
+    if (split < kChunk && row_a + 1 < n)
+        rb = flat_row(row_a + 1, col_begin, vocab_real, targets, active, ignore_index, grad,
+                      stats);
+
+    // issue every load of the wave before computing
+    u32x4 w[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const int idx = k * kWave + lane;
+        const bool in_b = idx >= split;
+        const int64_t row = row_a + (in_b ? 1 : 0);
+        const int col = static_cast<int>(q0 + idx - row * vpr) * kVec;
+        if (q0 + idx < total && (in_b ? rb.valid : ra.valid)) {
+            const uint16_t* src = logits + row * ld;
+            if (col + kVec <= lim) {
+                w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + col));
+            } else {
+                w[k].x = masked_bits(src, col + 0, lim) | (masked_bits(src, col + 1, lim) << 16);
+                w[k].y = masked_bits(src, col + 2, lim) | (masked_bits(src, col + 3, lim) << 16);
+                w[k].z = masked_bits(src, col + 4, lim) | (masked_bits(src, col + 5, lim) << 16);
+                w[k].w = masked_bits(src, col + 6, lim) | (masked_bits(src, col + 7, lim) << 16);
+            }
+        }
+    }
+    // subnormal-safe path if any valid vector may hold x < M - 87 of its own row
+    bool hit = false;
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const int idx = k * kWave + lane;
+        const bool in_b = idx >= split;
+        const bool valid = in_b ? rb.valid : ra.valid;
+        const unsigned t16 = in_b ? rb.t16 : ra.t16;
+        if (q0 + idx < total && valid) {
+            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+            u16x2 mx = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[k].x),
+                                                 __builtin_bit_cast(u16x2, w[k].y));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].z));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].w));
+            hit = hit || t16 == 0u || mx.x > t16 || mx.y > t16;
+        }
+    }
+    const bool deep = __any(hit);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const int idx = k * kWave + lane;
+        if (q0 + idx >= total) continue;
+        const bool in_b = idx >= split;
+        const int64_t row = row_a + (in_b ? 1 : 0);
+        const FlatRow r = in_b ? rb : ra;
+        const int col = static_cast<int>(q0 + idx - row * vpr) * kVec;
+        float d[kVec];
+        if (!r.valid) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) d[e] = 0.0f;
+        } else {
+            float v[kVec];
+            unpack8(w[k], v);
+            if (!deep) flat_vec<false>(r, v, col, lim, d);
+            else flat_vec<true>(r, v, col, lim, d);
+        }
+        store8<true>(dlogits + row * ld_out, col, vpr * kVec, d);
+    }
+}
+
 // --------------------------------------------------------------------- target check
 
 __global__ __launch_bounds__(kCheckThreads) void check_targets_kernel(
@@ -582,6 +718,18 @@ logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64
                     &ignore_index, &grad_logp, &stats, &dlogits, &ld_out};
     const bool vin = aligned16(logits) && (ld % kVec) == 0;
     const bool vout = aligned16(dlogits) && (ld_out % kVec) == 0;
+    if (vin && vout && width % kVec == 0 && width >= kTile) {
+        const int64_t vectors = n * (width / kVec);
+        const int64_t per_block = int64_t(kBwdWaves) * kWave * kLoads;  // 512 vectors per wave
+        const int64_t blocks = ceil_div(vectors, per_block);
+        if (blocks > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
+        int vpr = static_cast<int>(width / kVec), li = static_cast<int>(lim);
+        void* fargs[] = {&logits, &ld, &n, &vpr, &li, &col_begin, &vocab_real, &targets,
+                         &active, &ignore_index, &grad_logp, &stats, &dlogits, &ld_out};
+        return launch(reinterpret_cast<const void*>(&bwd_flat_kernel),
+                      dim3(static_cast<uint32_t>(blocks)), dim3(kBwdWaves * kWave), fargs, 0,
+                      stream);
+    }
     const void* k = vin ? (vout ? reinterpret_cast<const void*>(&bwd_kernel<true, true>)
                                 : reinterpret_cast<const void*>(&bwd_kernel<true, false>))
                         : (vout ? reinterpret_cast<const void*>(&bwd_kernel<false, true>)

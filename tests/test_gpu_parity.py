@@ -85,6 +85,8 @@ SMALL = [
     (25, 12288, 16384, 16400, 3.0, 7.0, 0.0, 0.0, 0.2),                # all-padding tile
     (40, 151936, 152064, 152064, 3.0, float("-inf"), 0.05, 0.05, 0.05),  # Qwen shape
     (3, 300, 300, 300, 40.0, float("-inf"), 0.0, 0.0, 0.0),            # very spread logits
+    (11, 9001, 9001, 9008, 3.0, float("-inf"), 0.1, 0.1, 0.1),         # aligned ld, odd width
+    (6, 20000, 20000, 20000, 30.0, float("-inf"), 0.0, 0.0, 0.0),      # subnormal gradients
 ]
 
 
