@@ -10,7 +10,8 @@ order, one block of rows per thread).  This module only builds that file with gc
 marshals numpy arrays into it.
 
 Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``):
-  forward, backward, tile_partials, merge, rne_bf16, count_bad_targets: pinned.
+  forward, backward, tile_partials (BF16, FP16 and FP32 logits; any inv_temperature),
+  merge, rne_bf16, rne_f16, count_bad_targets: pinned.
   Rows whose valid target logit is -inf while other logits are finite, and rows that
   hold NaN or +inf logits: parity unpinned (no closed form was written for them).
 """
@@ -88,6 +89,18 @@ def _declare(lib) -> None:
     lib.oracle_merge.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _P]
     lib.oracle_count_bad_targets.restype = ctypes.c_int64
     lib.oracle_count_bad_targets.argtypes = [_P, _P, _I64, _I64, _I64]
+    lib.oracle_rne_f16_array.restype = None
+    lib.oracle_rne_f16_array.argtypes = [_P, _P, _I64]
+    _F = ctypes.c_float
+    lib.oracle_forward_ex.restype = ctypes.c_int
+    lib.oracle_forward_ex.argtypes = [ctypes.c_int, _F, _P, _I64, _I64, _I64, _P, _P, _I64, _P,
+                                      _P, _P, _P, ctypes.c_int]
+    lib.oracle_backward_ex.restype = ctypes.c_int
+    lib.oracle_backward_ex.argtypes = [ctypes.c_int, _F, _P, _I64, _I64, _I64, _I64, _P, _P,
+                                       _I64, _P, _P, _I64, _P, _I64, ctypes.c_int]
+    lib.oracle_tile_partials_ex.restype = ctypes.c_int
+    lib.oracle_tile_partials_ex.argtypes = [ctypes.c_int, _F, _P, _I64, _I64, _I64, _I64, _I64,
+                                            _P, _P, _I64, _P, _P, _P, ctypes.c_int]
 
 
 def default_threads() -> int:
@@ -99,21 +112,39 @@ def default_threads() -> int:
 
 # ------------------------------------------------------------------ marshalling
 
-def _bits(logits) -> np.ndarray:
-    """BF16 logits as a C-contiguous uint16 array of raw bits, shape [n, ld]."""
+DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
+
+
+def _logits(logits):
+    """(C-contiguous array [n, ld], dtype name).  BF16 travels as raw uint16 bits."""
     try:
         import torch
         if isinstance(logits, torch.Tensor):
-            t = logits.detach()
-            if t.dtype != torch.bfloat16:
-                raise TypeError("oracle expects bfloat16 logits")
-            t = t.cpu().contiguous()
-            return t.view(torch.int16).numpy().view(np.uint16)
+            t = logits.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16), "bf16"
+            if t.dtype == torch.float16:
+                return t.numpy(), "f16"
+            if t.dtype == torch.float32:
+                return t.numpy(), "f32"
+            raise TypeError(f"oracle: unsupported logits dtype {t.dtype}")
     except ImportError:  # pragma: no cover
         pass
     a = np.ascontiguousarray(logits)
-    if a.dtype != np.uint16:
-        raise TypeError("oracle expects raw BF16 bits as uint16")
+    if a.dtype == np.uint16:
+        return a, "bf16"
+    if a.dtype == np.float16:
+        return a, "f16"
+    if a.dtype == np.float32:
+        return a, "f32"
+    raise TypeError("oracle expects BF16 bits (uint16), float16 or float32 logits")
+
+
+def _bits(logits) -> np.ndarray:
+    """BF16 logits as a C-contiguous uint16 array of raw bits, shape [n, ld]."""
+    a, dt = _logits(logits)
+    if dt != "bf16":
+        raise TypeError("oracle expects bfloat16 logits here")
     return a
 
 
@@ -148,43 +179,61 @@ def rne_bf16(values, lib=None) -> np.ndarray:
     return out
 
 
+def rne_f16(values, lib=None) -> np.ndarray:
+    """Round FP64 values to binary16 (nearest, ties to even) directly; returns uint16 bits."""
+    a = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load(lib).oracle_rne_f16_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
 def bf16_bits_to_f64(bits) -> np.ndarray:
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def forward(logits, targets, vocab_real: int, active=None, ignore_index: int = -100,
-            nthreads: Optional[int] = None, lib=None) -> dict:
-    """FP64 logp, LSE, row max M and row sum-exp S for every row."""
-    x = _bits(logits)
+            nthreads: Optional[int] = None, lib=None, inv_temperature: float = 1.0) -> dict:
+    """FP64 logp, LSE, row max M and row sum-exp S for every row.
+
+    ``logits``: BF16 (torch bfloat16 or raw uint16 bits), float16 or float32, [n, ld].
+    The scored logits are fl32(x * inv_temperature)."""
+    x, dt = _logits(logits)
     n, ld = (x.shape[0], x.shape[1]) if x.ndim == 2 else (0, vocab_real)
     y = _np(targets, np.int64)
     act = _np(active, np.uint8)
     out = {k: np.empty(n, dtype=np.float64) for k in ("logp", "lse", "max", "sumexp")}
-    rc = _load(lib).oracle_forward(_ptr(x), ld, n, vocab_real, _ptr(y), _ptr(act), ignore_index,
-                                _ptr(out["logp"]), _ptr(out["lse"]), _ptr(out["max"]),
-                                _ptr(out["sumexp"]), nthreads or default_threads())
+    rc = _load(lib).oracle_forward_ex(DTYPES[dt], float(np.float32(inv_temperature)), _ptr(x),
+                                      ld, n, vocab_real, _ptr(y), _ptr(act), ignore_index,
+                                      _ptr(out["logp"]), _ptr(out["lse"]), _ptr(out["max"]),
+                                      _ptr(out["sumexp"]), nthreads or default_threads())
     _check(rc, "forward")
     return out
 
 
 def backward(logits, targets, grad, vocab_real: int, vocab_padded: Optional[int] = None,
              active=None, ignore_index: int = -100, want_f64: bool = True,
-             want_bf16: bool = True, nthreads: Optional[int] = None, lib=None) -> dict:
-    """FP64 dlogits [n, vocab_padded] and/or its direct BF16 rounding (uint16 bits)."""
-    x = _bits(logits)
+             want_bf16: bool = True, nthreads: Optional[int] = None, lib=None,
+             inv_temperature: float = 1.0) -> dict:
+    """FP64 dlogits [n, vocab_padded] and its direct rounding to the logits' dtype.
+
+    Returns {"d64": float64 or None, "rounded": array in the logits' dtype (BF16 as uint16
+    bits) or None, "bf16": the same as "rounded" for BF16 logits}."""
+    x, dt = _logits(logits)
     n, ld = x.shape
     vocab_padded = vocab_real if vocab_padded is None else vocab_padded
     y = _np(targets, np.int64)
     act = _np(active, np.uint8)
     g = _np(grad, np.float32)
     d64 = np.empty((n, vocab_padded), dtype=np.float64) if want_f64 else None
-    db = np.empty((n, vocab_padded), dtype=np.uint16) if want_bf16 else None
-    rc = _load(lib).oracle_backward(_ptr(x), ld, n, vocab_real, vocab_padded, _ptr(y), _ptr(act),
-                                 ignore_index, _ptr(g), _ptr(d64), vocab_padded, _ptr(db),
-                                 vocab_padded, nthreads or default_threads())
+    out_dtype = {"bf16": np.uint16, "f16": np.float16, "f32": np.float32}[dt]
+    rounded = np.empty((n, vocab_padded), dtype=out_dtype) if want_bf16 else None
+    rc = _load(lib).oracle_backward_ex(DTYPES[dt], float(np.float32(inv_temperature)), _ptr(x),
+                                       ld, n, vocab_real, vocab_padded, _ptr(y), _ptr(act),
+                                       ignore_index, _ptr(g), _ptr(d64), vocab_padded,
+                                       _ptr(rounded), vocab_padded, nthreads or default_threads())
     _check(rc, "backward")
-    return {"d64": d64, "bf16": db}
+    return {"d64": d64, "rounded": rounded, "bf16": rounded if dt == "bf16" else None}
 
 
 def num_tiles(vocab_padded: int, tile: int = TILE) -> int:
@@ -193,19 +242,21 @@ def num_tiles(vocab_padded: int, tile: int = TILE) -> int:
 
 def tile_partials(logits, targets, vocab_real: int, vocab_padded: Optional[int] = None,
                   active=None, ignore_index: int = -100, tile: int = TILE,
-                  nthreads: Optional[int] = None, lib=None) -> dict:
+                  nthreads: Optional[int] = None, lib=None,
+                  inv_temperature: float = 1.0) -> dict:
     """FP64 per-tile (m, s, sel), each [n, ceil(vocab_padded / tile)]."""
-    x = _bits(logits)
+    x, dt = _logits(logits)
     n, ld = x.shape
     vocab_padded = vocab_real if vocab_padded is None else vocab_padded
     L = num_tiles(vocab_padded, tile)
     y = _np(targets, np.int64)
     act = _np(active, np.uint8)
     out = {k: np.empty((n, L), dtype=np.float64) for k in ("max", "sumexp", "sel")}
-    rc = _load(lib).oracle_tile_partials(_ptr(x), ld, n, vocab_real, vocab_padded, tile, _ptr(y),
-                                      _ptr(act), ignore_index, _ptr(out["max"]),
-                                      _ptr(out["sumexp"]), _ptr(out["sel"]),
-                                      nthreads or default_threads())
+    rc = _load(lib).oracle_tile_partials_ex(DTYPES[dt], float(np.float32(inv_temperature)),
+                                            _ptr(x), ld, n, vocab_real, vocab_padded, tile,
+                                            _ptr(y), _ptr(act), ignore_index, _ptr(out["max"]),
+                                            _ptr(out["sumexp"]), _ptr(out["sel"]),
+                                            nthreads or default_threads())
     _check(rc, "tile_partials")
     return out
 

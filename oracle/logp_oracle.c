@@ -31,6 +31,13 @@
  *   - The softmax in the gradient is exp(x_c - M) / S.
  *   - BF16 outputs are the round-to-nearest-even of the FP64 value, taken directly from
  *     FP64 (no FP32 intermediate, so no double rounding).
+ *   - Logits may also be FP16 or FP32 (the pull request's tests cover FP32/BF16/FP16,
+ *     section Tests); the gradient is returned in the logits' own dtype, rounded to
+ *     nearest-even straight from FP64.
+ *   - Temperature-scaled scoring scores z = fl32(x * inv_temperature), one FP32 product
+ *     per logit (the rounding of x / tau is frozen this way so that every consumer gets the
+ *     same z); logp and LSE are exact functions of z, and dlogits is
+ *     inv_temperature * g * (onehot - softmax(z)).  inv_temperature = 1 leaves x unchanged.
  */
 #include <math.h>
 #include <pthread.h>
@@ -48,6 +55,34 @@ static double bf16_bits_to_double(uint16_t b) {
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* An IEEE binary16 value from its bits: sign, 5 exponent bits (bias 15), 10 fraction bits. */
+static double f16_bits_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m == 0 ? INFINITY : NAN;
+    else
+        v = ldexp(1024.0 + m, e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+enum { DT_BF16 = 0, DT_F16 = 1, DT_F32 = 2 };
+
+/* Logit number `index` of a buffer of the given dtype, scaled: fl32(x * inv_temperature). */
+static double logit_at(const void* logits, int dtype, int64_t index, float inv_temperature) {
+    float x;
+    if (dtype == DT_BF16)
+        x = (float)bf16_bits_to_double(((const uint16_t*)logits)[index]);
+    else if (dtype == DT_F16)
+        x = (float)f16_bits_to_double(((const uint16_t*)logits)[index]);
+    else
+        x = ((const float*)logits)[index];
+    float z = x * inv_temperature; /* one correctly rounded FP32 product */
+    return (double)z;
 }
 
 /* Round a double to the nearest BF16 value, ties to even, straight from FP64.
@@ -74,6 +109,32 @@ ORACLE_API uint16_t oracle_rne_bf16(double d) {
 
 ORACLE_API void oracle_rne_bf16_array(const double* in, uint16_t* out, int64_t count) {
     for (int64_t i = 0; i < count; ++i) out[i] = oracle_rne_bf16(in[i]);
+}
+
+/* Round a double to the nearest binary16 value, ties to even, straight from FP64.
+ * 11 significant bits; normal range from 2^-14; subnormal spacing 2^-24; largest finite
+ * 65504, and everything from 65520 (the tie with 2^16) up rounds to infinity. */
+ORACLE_API uint16_t oracle_rne_f16(double d) {
+    if (isnan(d)) return (uint16_t)0x7E00;
+    uint16_t sign = signbit(d) ? 0x8000 : 0x0000;
+    double a = fabs(d);
+    if (isinf(a)) return sign | 0x7C00;
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);              /* a = f * 2^e, 0.5 <= f < 1 */
+    int q_exp = e - 11;              /* spacing of binary16 numbers in this binade */
+    if (q_exp < -24) q_exp = -24;    /* subnormal spacing below 2^-14 */
+    double v = ldexp(nearbyint(ldexp(a, -q_exp)), q_exp);
+    if (v > 65504.0) return sign | 0x7C00;
+    if (v < ldexp(1.0, -14)) return sign | (uint16_t)ldexp(v, 24); /* subnormal or zero */
+    int ev;
+    double f = frexp(v, &ev);        /* v = f * 2^ev, f in [0.5, 1) */
+    uint16_t mant = (uint16_t)(ldexp(f, 11) - 1024.0);
+    return sign | (uint16_t)((ev - 1 + 15) << 10) | mant;
+}
+
+ORACLE_API void oracle_rne_f16_array(const double* in, uint16_t* out, int64_t count) {
+    for (int64_t i = 0; i < count; ++i) out[i] = oracle_rne_f16(in[i]);
 }
 
 static int row_is_valid(const int64_t* targets, const uint8_t* active, int64_t ignore_index,
@@ -132,17 +193,28 @@ static int for_each_row(int64_t n, int nthreads, row_fn fn, void* ctx) {
 
 /* ------------------------------------------------------------------ row statistics */
 
+/* A row of logits: element c is logit_at(base, dtype, offset + c, inv_t). */
+typedef struct {
+    const void* base;
+    int dtype;
+    int64_t offset;
+    float inv_t;
+} row_t;
+
+static double row_x(const row_t* r, int64_t c) {
+    return logit_at(r->base, r->dtype, r->offset + c, r->inv_t);
+}
+
 /* M = max over real columns, S = sum exp(x_c - M) in column order (S = 0 if M = -inf). */
-static void row_max_sumexp(const uint16_t* row, int64_t vocab_real, double* M_out,
-                           double* S_out) {
+static void row_max_sumexp(const row_t* row, int64_t vocab_real, double* M_out, double* S_out) {
     double M = -INFINITY;
     for (int64_t c = 0; c < vocab_real; ++c) {
-        double x = bf16_bits_to_double(row[c]);
+        double x = row_x(row, c);
         if (x > M) M = x;
     }
     double S = 0.0;
     if (M != -INFINITY)
-        for (int64_t c = 0; c < vocab_real; ++c) S += exp(bf16_bits_to_double(row[c]) - M);
+        for (int64_t c = 0; c < vocab_real; ++c) S += exp(row_x(row, c) - M);
     *M_out = M;
     *S_out = S;
 }
@@ -150,7 +222,9 @@ static void row_max_sumexp(const uint16_t* row, int64_t vocab_real, double* M_ou
 /* ------------------------------------------------------------------------- forward */
 
 typedef struct {
-    const uint16_t* logits;
+    const void* logits;
+    int dtype;
+    float inv_t;
     int64_t ld, vocab_real;
     const int64_t* targets;
     const uint8_t* active;
@@ -160,9 +234,9 @@ typedef struct {
 
 static void fwd_row(void* p, int64_t t) {
     fwd_ctx* c = (fwd_ctx*)p;
-    const uint16_t* row = c->logits + t * c->ld;
+    row_t row = {c->logits, c->dtype, t * c->ld, c->inv_t};
     double M, S;
-    row_max_sumexp(row, c->vocab_real, &M, &S);
+    row_max_sumexp(&row, c->vocab_real, &M, &S);
     int valid = row_is_valid(c->targets, c->active, c->ignore_index, c->vocab_real, t);
     double lse, logp;
     if (M == -INFINITY) {
@@ -171,7 +245,7 @@ static void fwd_row(void* p, int64_t t) {
     } else {
         double log_s = log(S);
         lse = M + log_s;
-        logp = valid ? (bf16_bits_to_double(row[c->targets[t]]) - M) - log_s : 0.0;
+        logp = valid ? (row_x(&row, c->targets[t]) - M) - log_s : 0.0;
     }
     if (c->logp) c->logp[t] = logp;
     if (c->lse) c->lse[t] = lse;
@@ -179,22 +253,33 @@ static void fwd_row(void* p, int64_t t) {
     if (c->row_sumexp) c->row_sumexp[t] = S;
 }
 
-/* logits: [n, ld] BF16 bits; outputs [n] doubles (each nullable). */
+/* logits: [n, ld] of the given dtype (0 BF16, 1 FP16, 2 FP32); outputs [n] doubles (each
+ * nullable).  The scored logits are fl32(x * inv_temperature). */
+ORACLE_API int oracle_forward_ex(int dtype, float inv_temperature, const void* logits, int64_t ld,
+                                 int64_t n, int64_t vocab_real, const int64_t* targets,
+                                 const uint8_t* active, int64_t ignore_index, double* logp,
+                                 double* lse, double* row_max, double* row_sumexp, int nthreads) {
+    if (n < 0 || vocab_real < 1 || ld < vocab_real || dtype < 0 || dtype > 2) return 1;
+    if (n > 0 && (logits == NULL || targets == NULL)) return 1;
+    fwd_ctx c = {logits, dtype, inv_temperature, ld, vocab_real, targets, active, ignore_index,
+                 logp, lse, row_max, row_sumexp};
+    return for_each_row(n, nthreads, fwd_row, &c);
+}
+
 ORACLE_API int oracle_forward(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
                               const int64_t* targets, const uint8_t* active,
                               int64_t ignore_index, double* logp, double* lse, double* row_max,
                               double* row_sumexp, int nthreads) {
-    if (n < 0 || vocab_real < 1 || ld < vocab_real) return 1;
-    if (n > 0 && (logits == NULL || targets == NULL)) return 1;
-    fwd_ctx c = {logits, ld, vocab_real, targets, active, ignore_index,
-                 logp, lse, row_max, row_sumexp};
-    return for_each_row(n, nthreads, fwd_row, &c);
+    return oracle_forward_ex(DT_BF16, 1.0f, logits, ld, n, vocab_real, targets, active,
+                             ignore_index, logp, lse, row_max, row_sumexp, nthreads);
 }
 
 /* ------------------------------------------------------------------------ backward */
 
 typedef struct {
-    const uint16_t* logits;
+    const void* logits;
+    int dtype;
+    float inv_t;
     int64_t ld, vocab_real, vocab_padded;
     const int64_t* targets;
     const uint8_t* active;
@@ -202,59 +287,80 @@ typedef struct {
     const float* grad;
     double* d64;
     int64_t ld_d64;
-    uint16_t* d_bf16;
-    int64_t ld_bf16;
+    void* d_out; /* rounded to the logits' dtype */
+    int64_t ld_out;
 } bwd_ctx;
+
+static void store_rounded(void* out, int dtype, int64_t index, double v) {
+    if (dtype == DT_BF16)
+        ((uint16_t*)out)[index] = oracle_rne_bf16(v);
+    else if (dtype == DT_F16)
+        ((uint16_t*)out)[index] = oracle_rne_f16(v);
+    else
+        ((float*)out)[index] = (float)v; /* C's double -> float conversion rounds to nearest */
+}
 
 static void bwd_row(void* p, int64_t t) {
     bwd_ctx* c = (bwd_ctx*)p;
-    const uint16_t* row = c->logits + t * c->ld;
+    row_t row = {c->logits, c->dtype, t * c->ld, c->inv_t};
     double* d = c->d64 ? c->d64 + t * c->ld_d64 : NULL;
-    uint16_t* b = c->d_bf16 ? c->d_bf16 + t * c->ld_bf16 : NULL;
     int valid = row_is_valid(c->targets, c->active, c->ignore_index, c->vocab_real, t);
     double M = -INFINITY, S = 0.0;
-    if (valid) row_max_sumexp(row, c->vocab_real, &M, &S);
+    if (valid) row_max_sumexp(&row, c->vocab_real, &M, &S);
     if (!valid || M == -INFINITY) {
         for (int64_t col = 0; col < c->vocab_padded; ++col) {
             if (d) d[col] = 0.0;
-            if (b) b[col] = 0;
+            if (c->d_out) store_rounded(c->d_out, c->dtype, t * c->ld_out + col, 0.0);
         }
         return;
     }
-    double g = (double)c->grad[t];
+    /* d logits = d z / d x * d logp / d z = inv_temperature * g * (onehot - softmax(z)) */
+    double g = (double)c->grad[t] * (double)c->inv_t;
     int64_t y = c->targets[t];
     for (int64_t col = 0; col < c->vocab_padded; ++col) {
         double v = 0.0;
         if (col < c->vocab_real) {
-            double softmax = exp(bf16_bits_to_double(row[col]) - M) / S;
+            double softmax = exp(row_x(&row, col) - M) / S;
             double onehot = (col == y) ? 1.0 : 0.0;
             v = g * (onehot - softmax);
         }
         if (d) d[col] = v;
-        if (b) b[col] = oracle_rne_bf16(v);
+        if (c->d_out) store_rounded(c->d_out, c->dtype, t * c->ld_out + col, v);
     }
 }
 
-/* d64: [n, ld_d64] doubles, d_bf16: [n, ld_bf16] BF16 bits (each nullable); columns
+/* d64: [n, ld_d64] doubles, d_out: [n, ld_out] in the logits' dtype (each nullable); columns
  * [0, vocab_padded) of each row are written. */
+ORACLE_API int oracle_backward_ex(int dtype, float inv_temperature, const void* logits,
+                                  int64_t ld, int64_t n, int64_t vocab_real, int64_t vocab_padded,
+                                  const int64_t* targets, const uint8_t* active,
+                                  int64_t ignore_index, const float* grad, double* d64,
+                                  int64_t ld_d64, void* d_out, int64_t ld_out, int nthreads) {
+    if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real || ld < vocab_real) return 1;
+    if (dtype < 0 || dtype > 2) return 1;
+    if (d64 && ld_d64 < vocab_padded) return 1;
+    if (d_out && ld_out < vocab_padded) return 1;
+    if (n > 0 && (logits == NULL || targets == NULL || grad == NULL)) return 1;
+    bwd_ctx c = {logits, dtype, inv_temperature, ld, vocab_real, vocab_padded, targets, active,
+                 ignore_index, grad, d64, ld_d64, d_out, ld_out};
+    return for_each_row(n, nthreads, bwd_row, &c);
+}
+
 ORACLE_API int oracle_backward(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
                                int64_t vocab_padded, const int64_t* targets,
                                const uint8_t* active, int64_t ignore_index, const float* grad,
                                double* d64, int64_t ld_d64, uint16_t* d_bf16, int64_t ld_bf16,
                                int nthreads) {
-    if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real || ld < vocab_real) return 1;
-    if (d64 && ld_d64 < vocab_padded) return 1;
-    if (d_bf16 && ld_bf16 < vocab_padded) return 1;
-    if (n > 0 && (logits == NULL || targets == NULL || grad == NULL)) return 1;
-    bwd_ctx c = {logits, ld, vocab_real, vocab_padded, targets, active, ignore_index, grad,
-                 d64, ld_d64, d_bf16, ld_bf16};
-    return for_each_row(n, nthreads, bwd_row, &c);
+    return oracle_backward_ex(DT_BF16, 1.0f, logits, ld, n, vocab_real, vocab_padded, targets,
+                              active, ignore_index, grad, d64, ld_d64, d_bf16, ld_bf16, nthreads);
 }
 
 /* ---------------------------------------------------------------- tile partials */
 
 typedef struct {
-    const uint16_t* logits;
+    const void* logits;
+    int dtype;
+    float inv_t;
     int64_t ld, vocab_real, vocab_padded, tile, num_tiles;
     const int64_t* targets;
     const uint8_t* active;
@@ -264,7 +370,7 @@ typedef struct {
 
 static void part_row(void* p, int64_t t) {
     part_ctx* c = (part_ctx*)p;
-    const uint16_t* row = c->logits + t * c->ld;
+    row_t row = {c->logits, c->dtype, t * c->ld, c->inv_t};
     int valid = row_is_valid(c->targets, c->active, c->ignore_index, c->vocab_real, t);
     int64_t y = c->targets[t];
     for (int64_t l = 0; l < c->num_tiles; ++l) {
@@ -273,13 +379,13 @@ static void part_row(void* p, int64_t t) {
         if (hi > c->vocab_real) hi = c->vocab_real; /* padded columns are not part of it */
         double m = -INFINITY, s = 0.0;
         for (int64_t col = lo; col < hi; ++col) {
-            double x = bf16_bits_to_double(row[col]);
+            double x = row_x(&row, col);
             if (x > m) m = x;
         }
         if (m != -INFINITY)
-            for (int64_t col = lo; col < hi; ++col) s += exp(bf16_bits_to_double(row[col]) - m);
+            for (int64_t col = lo; col < hi; ++col) s += exp(row_x(&row, col) - m);
         double sel = 0.0;
-        if (valid && y >= lo && y < lo + c->tile) sel = bf16_bits_to_double(row[y]);
+        if (valid && y >= lo && y < lo + c->tile) sel = row_x(&row, y);
         c->m[t * c->num_tiles + l] = m;
         c->s[t * c->num_tiles + l] = s;
         c->sel[t * c->num_tiles + l] = sel;
@@ -290,17 +396,28 @@ static void part_row(void* p, int64_t t) {
  * columns of the tile (-inf when there are none), s_l = sum exp(x - m_l) (0 when
  * m_l = -inf), sel_l = x_y when the row is valid and y lies in the tile, else 0.
  * Outputs are [n, num_tiles] doubles, num_tiles = ceil(vocab_padded / tile). */
+ORACLE_API int oracle_tile_partials_ex(int dtype, float inv_temperature, const void* logits,
+                                       int64_t ld, int64_t n, int64_t vocab_real,
+                                       int64_t vocab_padded, int64_t tile,
+                                       const int64_t* targets, const uint8_t* active,
+                                       int64_t ignore_index, double* m, double* s, double* sel,
+                                       int nthreads) {
+    if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real || ld < vocab_real || tile < 1)
+        return 1;
+    if (dtype < 0 || dtype > 2) return 1;
+    if (n > 0 && (logits == NULL || targets == NULL || !m || !s || !sel)) return 1;
+    part_ctx c = {logits, dtype, inv_temperature, ld, vocab_real, vocab_padded, tile,
+                  (vocab_padded + tile - 1) / tile, targets, active, ignore_index, m, s, sel};
+    return for_each_row(n, nthreads, part_row, &c);
+}
+
 ORACLE_API int oracle_tile_partials(const uint16_t* logits, int64_t ld, int64_t n,
                                     int64_t vocab_real, int64_t vocab_padded, int64_t tile,
                                     const int64_t* targets, const uint8_t* active,
                                     int64_t ignore_index, double* m, double* s, double* sel,
                                     int nthreads) {
-    if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real || ld < vocab_real || tile < 1)
-        return 1;
-    if (n > 0 && (logits == NULL || targets == NULL || !m || !s || !sel)) return 1;
-    part_ctx c = {logits, ld, vocab_real, vocab_padded, tile,
-                  (vocab_padded + tile - 1) / tile, targets, active, ignore_index, m, s, sel};
-    return for_each_row(n, nthreads, part_row, &c);
+    return oracle_tile_partials_ex(DT_BF16, 1.0f, logits, ld, n, vocab_real, vocab_padded, tile,
+                                   targets, active, ignore_index, m, s, sel, nthreads);
 }
 
 /* Merge per-tile partials in tile order: M = max m_l, S = sum over tiles with

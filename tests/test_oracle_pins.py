@@ -382,18 +382,122 @@ def test_count_bad_targets():
     assert oracle.count_bad_targets(y, 10, ignore_index=-1) == 4  # -100 now bad, -1 not
 
 
+# ------------------------------------------------------------------ FP16 / FP32 logits
+
+def test_rne_f16_exact_bit_patterns():
+    cases = [
+        (0.0, 0x0000), (-0.0, 0x8000), (1.0, 0x3C00), (-2.0, 0xC000), (65504.0, 0x7BFF),
+        (65519.99, 0x7BFF), (65520.0, 0x7C00), (1e6, 0x7C00), (float("inf"), 0x7C00),
+        (2.0 ** -24, 0x0001), (2.0 ** -25, 0x0000), (1.5 * 2.0 ** -25, 0x0001),
+        (2.0 ** -14, 0x0400), (2.0 ** -14 - 2.0 ** -25, 0x0400),
+        (1.0 + 2.0 ** -11, 0x3C00), (1.0 + 3 * 2.0 ** -11, 0x3C02),
+        # above the tie by far less than a float32 ulp: a float32 step would tie to even
+        (1.0 + 2.0 ** -11 + 2.0 ** -40, 0x3C01),
+    ]
+    got = oracle.rne_f16([v for v, _ in cases])
+    for (v, want), g in zip(cases, got):
+        assert int(g) == want, (v, hex(int(g)), hex(want))
+
+
+def test_rne_f16_matches_numpy():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(100_000) * 10.0 ** rng.integers(-9, 5, 100_000),
+                        rng.uniform(-70000, 70000, 2000)])
+    with np.errstate(over="ignore"):  # values past 65520 round to inf on purpose
+        want = x.astype(np.float16).view(np.uint16)  # numpy rounds double -> half directly
+    got = oracle.rne_f16(x)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(x[i], hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def test_f16_decode_is_exact_for_every_finite_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = bits.view(np.float16)
+    keep = np.isfinite(vals)
+    x = vals[keep].reshape(-1, 1)  # one value per row: the single-column tile max is x
+    part = oracle.tile_partials(x, np.zeros(x.shape[0], np.int64), 1, tile=1)
+    assert np.array_equal(part["max"][:, 0], x[:, 0].astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_f16_f32_logits_match_torch_float64(dtype):
+    tdt = {"f16": torch.float16, "f32": torch.float32}[dtype]
+    for seed, (n, v) in enumerate([(6, 1), (7, 255), (5, 1031), (2, 151936)]):
+        gen = torch.Generator().manual_seed(seed)
+        x = (torch.randn((n, v), generator=gen) * 3).to(tdt)
+        y = torch.randint(0, v, (n,), generator=gen)
+        g = torch.randn((n,), generator=gen)
+        x64 = x.double().requires_grad_(True)
+        lsm = torch.log_softmax(x64, 1)
+        want = lsm.gather(1, y.view(-1, 1)).flatten()
+        (want * g.double()).sum().backward()
+        out = oracle.forward(x, y, v)
+        assert np.allclose(out["logp"], want.detach().numpy(), rtol=1e-13, atol=1e-12)
+        d = oracle.backward(x, y, g, v)
+        assert np.allclose(d["d64"], x64.grad.numpy(), rtol=1e-12, atol=1e-15)
+        npdt = np.float16 if dtype == "f16" else np.float32
+        assert d["rounded"].dtype == npdt
+        assert np.array_equal(d["rounded"], d["d64"].astype(npdt))  # numpy rounds to nearest
+
+
+# ------------------------------------------------------------------ temperature
+
+@pytest.mark.parametrize("inv_t", [1.0 / 0.7, 0.5, 3.0])
+def test_temperature_scores_fl32_products(inv_t):
+    it32 = np.float32(inv_t)
+    vals = [-3.5, -1.0, 0.0, 0.5, 2.0, 7.0, 0.1015625, -2.71875]
+    pairs = [(a, b) for a in vals for b in vals]
+    x = rows_bits(pairs)
+    z = bf16_bits_to_f64(x).astype(np.float32) * it32  # numpy float32 product: IEEE single
+    out = oracle.forward(x, np.zeros(len(pairs), np.int64), 2, inv_temperature=inv_t)
+    for i in range(len(pairs)):
+        want = -math.log1p(math.exp(float(z[i, 1]) - float(z[i, 0])))
+        assert out["logp"][i] == pytest.approx(want, rel=1e-15, abs=5e-16)
+    # a uniform row stays exactly -log V at any temperature
+    u = np.full((1, 300), bf16_bits([1.75])[0], dtype=np.uint16)
+    assert oracle.forward(u, np.array([7]), 300, inv_temperature=inv_t)["logp"][0] == \
+        -math.log(300)
+
+
+def test_temperature_gradient_is_chain_rule_of_scored_logits():
+    inv_t = np.float32(1.0 / 0.7)
+    case = random_case(6, 777, sigma=3.0, seed=51, grad_std=2.0)
+    z = (case.logits.float() * torch.tensor(inv_t)).double()  # fl32(x * inv_t), promoted
+    zz = z.clone().requires_grad_(True)
+    lsm = torch.log_softmax(zz, 1)
+    sel = lsm.gather(1, case.targets.view(-1, 1)).flatten()
+    (sel * case.grad.double()).sum().backward()
+    out = oracle.forward(case.logits, case.targets, 777, inv_temperature=float(inv_t))
+    assert np.allclose(out["logp"], sel.detach().numpy(), rtol=1e-13, atol=1e-12)
+    d = oracle.backward(case.logits, case.targets, case.grad, 777, inv_temperature=float(inv_t))
+    assert np.allclose(d["d64"], zz.grad.numpy() * float(inv_t), rtol=1e-12, atol=1e-15)
+    # tile partials of the scored logits merge to the direct LSE
+    part = oracle.tile_partials(case.logits, case.targets, 777, tile=100,
+                                inv_temperature=float(inv_t))
+    mg = oracle.merge(part["max"], part["sumexp"], part["sel"], case.targets, 777, tile=100)
+    assert np.allclose(mg["lse"], out["lse"], rtol=1e-13)
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 MUTATIONS = {
     "gradient sign": ("v = g * (onehot - softmax);", "v = g * (softmax - onehot);"),
     "dropped log S": ("- M) - log_s : 0.0;\n    }\n    if (c->logp)",
                       "- M) : 0.0;\n    }\n    if (c->logp)"),
-    "padded columns summed": ("row_max_sumexp(row, c->vocab_real, &M, &S);\n    int valid",
-                              "row_max_sumexp(row, c->ld, &M, &S);\n    int valid"),
+    "padded columns summed": ("row_max_sumexp(&row, c->vocab_real, &M, &S);\n    int valid",
+                              "row_max_sumexp(&row, c->ld, &M, &S);\n    int valid"),
     "target off by one": ("onehot = (col == y) ? 1.0 : 0.0;",
                           "onehot = (col == y + 1) ? 1.0 : 0.0;"),
-    "no max shift in gradient": ("exp(bf16_bits_to_double(row[col]) - M) / S;",
-                                 "exp(bf16_bits_to_double(row[col])) / S;"),
+    "no max shift in gradient": ("exp(row_x(&row, col) - M) / S;",
+                                 "exp(row_x(&row, col)) / S;"),
+    "f16 exponent bias": ("v = ldexp(1024.0 + m, e - 25);", "v = ldexp(1024.0 + m, e - 24);"),
+    "temperature missing in gradient": ("double g = (double)c->grad[t] * (double)c->inv_t;",
+                                        "double g = (double)c->grad[t];"),
+    "f16 rounded through float32": ("double v = ldexp(nearbyint(ldexp(a, -q_exp)), q_exp);",
+                                    "double v = ldexp(nearbyint(ldexp((double)(float)a, -q_exp)), q_exp);"),
+    "temperature product in double": ("float z = x * inv_temperature;",
+                                      "double z = (double)x * inv_temperature;"),
+    "f16 subnormal scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     "ignore index accepted": ("if (y == ignore_index) return 0;", ""),
     "round through float32": ("double q = ldexp(a, -q_exp);",
                               "double q = ldexp((double)(float)a, -q_exp);"),
@@ -439,6 +543,29 @@ def _pins(lib) -> list[str]:
             failed.append("uniform")
         if oracle.forward(x, np.array([1]), 9, ignore_index=1, lib=lib)["logp"][0] != 0.0:
             failed.append("ignore index")
+        # FP16: decode of every finite pattern and direct rounding
+        h = np.arange(65536, dtype=np.uint16).view(np.float16)
+        h = h[np.isfinite(h)].reshape(-1, 1)
+        pm = oracle.tile_partials(h, np.zeros(h.shape[0], np.int64), 1, tile=1, lib=lib)["max"]
+        if not np.array_equal(pm[:, 0], h[:, 0].astype(np.float64)):
+            failed.append("f16 decode")
+        if np.any(oracle.rne_f16([1.0 + 2.0 ** -11 + 2.0 ** -40, 2.0 ** -24, 65520.0],
+                                 lib=lib) != [0x3C01, 0x0001, 0x7C00]):
+            failed.append("f16 rne")
+        # temperature: scored logits fl32(x * inv_t) and the chain-rule factor
+        inv_t = np.float32(1.0 / 0.7)
+        xt = case.logits[:, :v].float()
+        z = (xt * torch.tensor(inv_t)).double().requires_grad_(True)
+        lz = torch.log_softmax(z, 1).gather(1, y_ok.view(-1, 1)).flatten()
+        (lz * case.grad.double() * (case.targets >= 0)).sum().backward()
+        ot = oracle.forward(case.logits, case.targets, v, lib=lib, inv_temperature=float(inv_t))
+        if not np.allclose(ot["logp"][ok_rows], lz.detach().numpy()[ok_rows], rtol=0,
+                           atol=1e-13):
+            failed.append("temperature logp")
+        dt = oracle.backward(case.logits, case.targets, case.grad, v, p, lib=lib,
+                             inv_temperature=float(inv_t))
+        if not np.allclose(dt["d64"][:, :v], z.grad.numpy() * float(inv_t), atol=1e-14):
+            failed.append("temperature grad")
     except Exception as e:  # a mutant may also crash; that counts as caught
         failed.append(f"exception {type(e).__name__}")
     return failed
