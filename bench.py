@@ -46,10 +46,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def algorithmic_bytes(n: int, n_valid: int, vocab_real: int, width: int, has_mask: bool):
+def algorithmic_bytes(n: int, n_valid: int, vocab_real: int, width: int, has_mask: bool,
+                      elem: int = 2):
     mask = 1 if has_mask else 0
-    fwd = 2 * n * vocab_real + (24 + mask) * n
-    bwd = 2 * n_valid * vocab_real + 2 * n * width + (20 + mask) * n
+    fwd = elem * n * vocab_real + (24 + mask) * n
+    bwd = elem * n_valid * vocab_real + elem * n * width + (20 + mask) * n
     return fwd, bwd
 
 
@@ -108,6 +109,54 @@ def cpu_baseline(case, target_seconds: float) -> dict:
             "ms_per_step_extrapolated": round((full_fwd + full_bwd) / (gbs * 1e9) * 1e3, 1)}
 
 
+def time_variants(dst, case, stream, steps: int) -> dict:
+    """fwd / bwd times of the _ex entry points for FP16, FP32 and a temperature of 0.7 on the
+    headline rows (FP16 / FP32 logits are the BF16 values widened: the same data)."""
+    import torch
+
+    out = {}
+    n, v = case.n, case.vocab_real
+    y, g = case.targets, case.grad
+    for name, tdt, inv_t in (("f16", torch.float16, 1.0), ("f32", torch.float32, 1.0),
+                             ("bf16_temperature_0.7", torch.bfloat16, 1.0 / 0.7)):
+        x = case.logits if tdt == torch.bfloat16 else case.logits.to(tdt)
+        d = torch.empty((n, v), dtype=tdt, device=x.device)
+        logp = torch.empty(n, dtype=torch.float32, device=x.device)
+        lse = torch.empty_like(logp)
+        stats = torch.empty((n, 2), dtype=torch.float32, device=x.device)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            dst.logp_forward_ex(x, y, v, v, inv_temperature=inv_t, logp=logp, lse=lse,
+                                stats=stats, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            dst.logp_backward_ex(x, y, g, stats, v, v, inv_temperature=inv_t, dlogits=d,
+                                 stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+
+        for _ in range(2):
+            step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        f_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+        b_ms = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+        fb, bb = algorithmic_bytes(n, n, v, v, False, elem=x.element_size())
+        out[name] = {"fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+                     "ms_per_step": round(f_ms + b_ms, 4),
+                     "gbs": round((fb + bb) / ((f_ms + b_ms) * 1e-3) / 1e9, 1),
+                     "fwd_gbs": round(fb / (f_ms * 1e-3) / 1e9, 1),
+                     "bwd_gbs": round(bb / (b_ms * 1e-3) / 1e9, 1)}
+        del x, d
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +166,9 @@ def main() -> int:
                     help="target wall time of the oracle sample (0 disables it)")
     ap.add_argument("--shard-path", action="store_true",
                     help="also time logp_partials (4 shards) + logp_merge")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time FP16 and FP32 logits and BF16 at temperature 0.7 on the "
+                         "same shape (reported under config.variants)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="run a 4 GiB device copy after the timed region (counter scaling)")
     args = ap.parse_args()
@@ -208,6 +260,8 @@ def main() -> int:
         extra["shard_path"] = {"shards": len(layout),
                                "partials_ms": round(e[0].elapsed_time(e[1]), 4),
                                "merge_ms": round(e[1].elapsed_time(e[2]), 4)}
+    if args.variants:
+        extra["variants"] = time_variants(dst, case, stream, args.steps)
     if args.profile_copy:
         src = torch.empty(1 << 31, dtype=torch.int16, device=dev)  # 4 GiB
         dst_buf = torch.empty_like(src)

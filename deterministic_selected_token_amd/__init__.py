@@ -7,7 +7,8 @@ computation runs in the HIP kernels; there is no CPU or PyTorch fallback, and im
 this package fails loudly when the library has not been built.
 
 Tensor conventions:
-  * logits: bfloat16 ``[n, width]`` with unit column stride; ``ld = logits.stride(0)``.
+  * logits: bfloat16 ``[n, width]`` with unit column stride; ``ld = logits.stride(0)``
+    (the ``_ex`` functions also take float16 and float32 logits and a temperature).
     A vocab shard is a column slice of the full buffer (``full[:, c0:c1]``).
   * targets: int64 ``[n]``; active: uint8/bool ``[n]`` or None; grad_logp: float32 ``[n]``.
   * stats: float32 ``[n, 2]`` = (M, S) per row; partials: float32 ``[n, L, 3]`` =
@@ -31,9 +32,12 @@ LIB_PATH = os.path.join(_HERE, "liblogp_mi355x.so")
 STATUS = {
     0: "LOGP_OK", 1: "LOGP_ERR_NULL", 2: "LOGP_ERR_SHAPE", 3: "LOGP_ERR_SHARD",
     4: "LOGP_ERR_DEVICE", 5: "LOGP_ERR_RANGE", 6: "LOGP_ERR_OVERLAP", 7: "LOGP_ERR_HIP",
+    8: "LOGP_ERR_ARG",
 }
+DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}  # logp_dtype_t values
 EXPORTED = ("logp_forward", "logp_backward", "logp_partials", "logp_merge", "logp_num_tiles",
-            "logp_check_targets", "logp_status_string")
+            "logp_check_targets", "logp_status_string", "logp_forward_ex", "logp_backward_ex",
+            "logp_partials_ex")
 
 
 class LogpError(RuntimeError):
@@ -54,8 +58,12 @@ def _load_library() -> ctypes.CDLL:
     lib.logp_partials.argtypes = [P, I64, I64, I64, I64, I64, I64, P, P, I64, P, I64, P]
     lib.logp_merge.argtypes = [P, I64, I64, I64, I64, P, P, I64, P, P, P, P]
     lib.logp_check_targets.argtypes = [P, P, I64, I64, I64, P, P]
+    F = ctypes.c_float
+    lib.logp_forward_ex.argtypes = [I32, F] + lib.logp_forward.argtypes
+    lib.logp_backward_ex.argtypes = [I32, F] + lib.logp_backward.argtypes
+    lib.logp_partials_ex.argtypes = [I32, F] + lib.logp_partials.argtypes
     for fn in ("logp_forward", "logp_backward", "logp_partials", "logp_merge",
-               "logp_check_targets"):
+               "logp_check_targets", "logp_forward_ex", "logp_backward_ex", "logp_partials_ex"):
         getattr(lib, fn).restype = I32
     lib.logp_num_tiles.argtypes = [I64]
     lib.logp_num_tiles.restype = I64
@@ -110,11 +118,12 @@ def _active(active, n: int, device) -> Optional[torch.Tensor]:
     return _rows("active", active, torch.uint8, n, device)
 
 
-def _matrix(name: str, t: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+def _matrix(name: str, t: torch.Tensor, dtype) -> torch.Tensor:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in allowed:
+        raise TypeError(f"{name} must be one of {allowed}, got {t.dtype}")
     if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit column stride")
     if t.device.type != "cuda":
@@ -136,12 +145,10 @@ def logp_status_string(status: int) -> str:
     return _lib.logp_status_string(int(status)).decode()
 
 
-def logp_forward(logits: torch.Tensor, targets: torch.Tensor, vocab_real: Optional[int] = None,
-                 vocab_padded: Optional[int] = None, active=None, ignore_index: int = -100,
-                 logp: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 stats: Optional[torch.Tensor] = None, stream=None):
-    """Selected-token logp, LSE and per-row (M, S) over whole rows -> (logp, lse, stats)."""
-    logits = _matrix("logits", logits, torch.bfloat16)
+def _forward(fn: str, logits, targets, vocab_real, vocab_padded, active, ignore_index, logp, lse,
+             stats, stream, inv_temperature):
+    ex = fn.endswith("_ex")
+    logits = _matrix("logits", logits, tuple(DTYPES) if ex else torch.bfloat16)
     n, width = logits.shape
     dev = logits.device
     vocab_padded = width if vocab_padded is None else int(vocab_padded)
@@ -158,20 +165,39 @@ def logp_forward(logits: torch.Tensor, targets: torch.Tensor, vocab_real: Option
     _rows("lse", lse, torch.float32, n, dev)
     if stats.shape != (n, 2) or stats.dtype != torch.float32 or not stats.is_contiguous():
         raise ValueError("stats must be a contiguous float32 [n, 2] tensor")
-    st = _lib.logp_forward(_ptr(logits), _ld(logits), n, vocab_real, vocab_padded,
-                           _ptr(targets), _ptr(active), int(ignore_index), _ptr(logp),
-                           _ptr(lse), _ptr(stats), _stream(dev, stream))
-    _check("logp_forward", st)
+    args = (_ptr(logits), _ld(logits), n, vocab_real, vocab_padded, _ptr(targets), _ptr(active),
+            int(ignore_index), _ptr(logp), _ptr(lse), _ptr(stats), _stream(dev, stream))
+    if ex:
+        st = _lib.logp_forward_ex(DTYPES[logits.dtype], float(inv_temperature), *args)
+    else:
+        st = _lib.logp_forward(*args)
+    _check(fn, st)
     return logp, lse, stats
 
 
-def logp_backward(logits: torch.Tensor, targets: torch.Tensor, grad_logp: torch.Tensor,
-                  stats: torch.Tensor, vocab_real: Optional[int] = None,
-                  vocab_padded: Optional[int] = None, col_begin: int = 0,
-                  col_end: Optional[int] = None, active=None, ignore_index: int = -100,
-                  dlogits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """BF16 dlogits over columns [col_begin, col_end) (``logits`` is that column view)."""
-    logits = _matrix("logits", logits, torch.bfloat16)
+def logp_forward(logits: torch.Tensor, targets: torch.Tensor, vocab_real: Optional[int] = None,
+                 vocab_padded: Optional[int] = None, active=None, ignore_index: int = -100,
+                 logp: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 stats: Optional[torch.Tensor] = None, stream=None):
+    """Selected-token logp, LSE and per-row (M, S) over whole BF16 rows -> (logp, lse, stats)."""
+    return _forward("logp_forward", logits, targets, vocab_real, vocab_padded, active,
+                    ignore_index, logp, lse, stats, stream, 1.0)
+
+
+def logp_forward_ex(logits: torch.Tensor, targets: torch.Tensor,
+                    vocab_real: Optional[int] = None, vocab_padded: Optional[int] = None,
+                    active=None, ignore_index: int = -100, inv_temperature: float = 1.0,
+                    logp: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    stats: Optional[torch.Tensor] = None, stream=None):
+    """logp_forward for BF16 / FP16 / FP32 logits scored as fl32(x * inv_temperature)."""
+    return _forward("logp_forward_ex", logits, targets, vocab_real, vocab_padded, active,
+                    ignore_index, logp, lse, stats, stream, inv_temperature)
+
+
+def _backward(fn: str, logits, targets, grad_logp, stats, vocab_real, vocab_padded, col_begin,
+              col_end, active, ignore_index, dlogits, stream, inv_temperature):
+    ex = fn.endswith("_ex")
+    logits = _matrix("logits", logits, tuple(DTYPES) if ex else torch.bfloat16)
     n, width = logits.shape
     dev = logits.device
     col_end = col_begin + width if col_end is None else int(col_end)
@@ -186,27 +212,48 @@ def logp_backward(logits: torch.Tensor, targets: torch.Tensor, grad_logp: torch.
             or stats.device != dev:
         raise ValueError("stats must be a contiguous float32 [n, 2] tensor on the logits device")
     if dlogits is None:
-        dlogits = torch.empty((n, col_end - col_begin), dtype=torch.bfloat16, device=dev)
-    dlogits = _matrix("dlogits", dlogits, torch.bfloat16)
+        dlogits = torch.empty((n, col_end - col_begin), dtype=logits.dtype, device=dev)
+    dlogits = _matrix("dlogits", dlogits, logits.dtype)
     if dlogits.shape[0] != n or dlogits.shape[1] < col_end - col_begin or dlogits.device != dev:
         raise ValueError("dlogits must be [n, >= col_end - col_begin] on the logits device")
-    st = _lib.logp_backward(_ptr(logits), _ld(logits), n, vocab_real, vocab_padded,
-                            int(col_begin), col_end, _ptr(targets), _ptr(active),
-                            int(ignore_index), _ptr(grad_logp), _ptr(stats), _ptr(dlogits),
-                            _ld(dlogits), _stream(dev, stream))
-    _check("logp_backward", st)
+    args = (_ptr(logits), _ld(logits), n, vocab_real, vocab_padded, int(col_begin), col_end,
+            _ptr(targets), _ptr(active), int(ignore_index), _ptr(grad_logp), _ptr(stats),
+            _ptr(dlogits), _ld(dlogits), _stream(dev, stream))
+    if ex:
+        st = _lib.logp_backward_ex(DTYPES[logits.dtype], float(inv_temperature), *args)
+    else:
+        st = _lib.logp_backward(*args)
+    _check(fn, st)
     return dlogits
 
 
-def logp_partials(logits: torch.Tensor, targets: torch.Tensor, vocab_real: int,
-                  vocab_padded: int, col_begin: int, col_end: int, partials: torch.Tensor,
-                  active=None, ignore_index: int = -100, stream=None) -> torch.Tensor:
-    """Write the (m, s, sel) partials of the shard [col_begin, col_end) into ``partials``.
+def logp_backward(logits: torch.Tensor, targets: torch.Tensor, grad_logp: torch.Tensor,
+                  stats: torch.Tensor, vocab_real: Optional[int] = None,
+                  vocab_padded: Optional[int] = None, col_begin: int = 0,
+                  col_end: Optional[int] = None, active=None, ignore_index: int = -100,
+                  dlogits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """BF16 dlogits over columns [col_begin, col_end) (``logits`` is that column view)."""
+    return _backward("logp_backward", logits, targets, grad_logp, stats, vocab_real,
+                     vocab_padded, col_begin, col_end, active, ignore_index, dlogits, stream, 1.0)
 
-    ``logits`` is the shard's column view; ``partials`` is the full float32 [n, L, 3]
-    buffer, whose tiles col_begin/TILE_COLS onward are written.
-    """
-    logits = _matrix("logits", logits, torch.bfloat16)
+
+def logp_backward_ex(logits: torch.Tensor, targets: torch.Tensor, grad_logp: torch.Tensor,
+                     stats: torch.Tensor, vocab_real: Optional[int] = None,
+                     vocab_padded: Optional[int] = None, col_begin: int = 0,
+                     col_end: Optional[int] = None, active=None, ignore_index: int = -100,
+                     inv_temperature: float = 1.0, dlogits: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """logp_backward for BF16 / FP16 / FP32 logits scored as fl32(x * inv_temperature);
+    dlogits has the logits' dtype and includes the factor inv_temperature."""
+    return _backward("logp_backward_ex", logits, targets, grad_logp, stats, vocab_real,
+                     vocab_padded, col_begin, col_end, active, ignore_index, dlogits, stream,
+                     inv_temperature)
+
+
+def _partials(fn: str, logits, targets, vocab_real, vocab_padded, col_begin, col_end, partials,
+              active, ignore_index, stream, inv_temperature):
+    ex = fn.endswith("_ex")
+    logits = _matrix("logits", logits, tuple(DTYPES) if ex else torch.bfloat16)
     n = logits.shape[0]
     dev = logits.device
     targets = _rows("targets", targets, torch.int64, n, dev)
@@ -219,11 +266,36 @@ def logp_partials(logits: torch.Tensor, targets: torch.Tensor, vocab_real: int,
         raise ValueError("col_begin must be a tile boundary inside the partials buffer")
     first = partials[:, col_begin // TILE_COLS]
     ldp = partials.stride(0) // 3 if partials.stride(0) % 3 == 0 else -1
-    st = _lib.logp_partials(_ptr(logits), _ld(logits), n, int(vocab_real), int(vocab_padded),
-                            int(col_begin), int(col_end), _ptr(targets), _ptr(active),
-                            int(ignore_index), first.data_ptr(), ldp, _stream(dev, stream))
-    _check("logp_partials", st)
+    args = (_ptr(logits), _ld(logits), n, int(vocab_real), int(vocab_padded), int(col_begin),
+            int(col_end), _ptr(targets), _ptr(active), int(ignore_index), first.data_ptr(), ldp,
+            _stream(dev, stream))
+    if ex:
+        st = _lib.logp_partials_ex(DTYPES[logits.dtype], float(inv_temperature), *args)
+    else:
+        st = _lib.logp_partials(*args)
+    _check(fn, st)
     return partials
+
+
+def logp_partials(logits: torch.Tensor, targets: torch.Tensor, vocab_real: int,
+                  vocab_padded: int, col_begin: int, col_end: int, partials: torch.Tensor,
+                  active=None, ignore_index: int = -100, stream=None) -> torch.Tensor:
+    """Write the (m, s, sel) partials of the shard [col_begin, col_end) into ``partials``.
+
+    ``logits`` is the shard's column view; ``partials`` is the full float32 [n, L, 3]
+    buffer, whose tiles col_begin/TILE_COLS onward are written.
+    """
+    return _partials("logp_partials", logits, targets, vocab_real, vocab_padded, col_begin,
+                     col_end, partials, active, ignore_index, stream, 1.0)
+
+
+def logp_partials_ex(logits: torch.Tensor, targets: torch.Tensor, vocab_real: int,
+                     vocab_padded: int, col_begin: int, col_end: int, partials: torch.Tensor,
+                     active=None, ignore_index: int = -100, inv_temperature: float = 1.0,
+                     stream=None) -> torch.Tensor:
+    """logp_partials for BF16 / FP16 / FP32 logits scored as fl32(x * inv_temperature)."""
+    return _partials("logp_partials_ex", logits, targets, vocab_real, vocab_padded, col_begin,
+                     col_end, partials, active, ignore_index, stream, inv_temperature)
 
 
 def logp_merge(partials: torch.Tensor, targets: torch.Tensor, vocab_real: int,
@@ -273,6 +345,7 @@ def logp_check_targets(targets: torch.Tensor, vocab_real: int, active=None,
     return bad_count
 
 
-__all__ = ["EXPORTED", "LIB_PATH", "LogpError", "STATUS", "TILE_COLS", "FWD_MAX_TILES",
-           "library", "logp_forward", "logp_backward", "logp_partials", "logp_merge",
+__all__ = ["DTYPES", "EXPORTED", "LIB_PATH", "LogpError", "STATUS", "TILE_COLS",
+           "FWD_MAX_TILES", "library", "logp_forward", "logp_forward_ex", "logp_backward",
+           "logp_backward_ex", "logp_partials", "logp_partials_ex", "logp_merge",
            "logp_num_tiles", "logp_check_targets", "logp_status_string"]

@@ -32,9 +32,42 @@ constexpr float kLog2e = 1.44269504088896340736f;       // 0x3FB8AA3B = fl32(log
 constexpr float kLn2Hi = 0.693147182464599609375f;     // 0x3F317218 = fl32(ln 2)
 constexpr float kLn2Lo = -1.9046542e-09f;               // fl32(ln 2 - kLn2Hi)
 
-// ------------------------------------------------------------------ BF16 unpacking
+// ------------------------------------------------------------------ logits dtypes
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load or store
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Logits (and dlogits) element types: BF16, FP16, FP32 (values match logp_dtype_t).
+enum class Dt : int { BF16 = 0, F16 = 1, F32 = 2 };
+
+template <Dt D>
+struct DtInfo;
+template <>
+struct DtInfo<Dt::BF16> {
+    using Storage = uint16_t;
+    static constexpr uint32_t kNegInfBits = 0xFF80u;
+};
+template <>
+struct DtInfo<Dt::F16> {
+    using Storage = uint16_t;
+    static constexpr uint32_t kNegInfBits = 0xFC00u;
+};
+template <>
+struct DtInfo<Dt::F32> {
+    using Storage = uint32_t;  // raw FP32 bits
+    static constexpr uint32_t kNegInfBits = 0xFF800000u;
+};
+
+// Eight consecutive logits as raw bits: one 16-byte vector for 2-byte types, two for FP32.
+template <Dt D>
+struct Raw8 {
+    u32x4 w;
+};
+template <>
+struct Raw8<Dt::F32> {
+    u32x4 w, w2;
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -42,64 +75,149 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
+// Exact widening of one element's raw bits to FP32.
+template <Dt D>
+__device__ __forceinline__ float elem_to_f32(uint32_t bits) {
+    if constexpr (D == Dt::BF16) {
+        return __uint_as_float(bits << 16);
+    } else if constexpr (D == Dt::F16) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+    } else {
+        return __uint_as_float(bits);
+    }
+}
+
+// The 8 values of a Raw8 as FP32 (exact).
+template <Dt D>
+__device__ __forceinline__ void unpack8(const Raw8<D>& r, float* out) {
+    if constexpr (D == Dt::BF16) {
+        out[0] = bf16_lo(r.w.x); out[1] = bf16_hi(r.w.x);
+        out[2] = bf16_lo(r.w.y); out[3] = bf16_hi(r.w.y);
+        out[4] = bf16_lo(r.w.z); out[5] = bf16_hi(r.w.z);
+        out[6] = bf16_lo(r.w.w); out[7] = bf16_hi(r.w.w);
+    } else if constexpr (D == Dt::F16) {
+        const uint32_t q[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2 h = __builtin_bit_cast(f16x2, q[i]);
+            out[2 * i] = static_cast<float>(h.x);
+            out[2 * i + 1] = static_cast<float>(h.y);
+        }
+    } else {
+        out[0] = __uint_as_float(r.w.x); out[1] = __uint_as_float(r.w.y);
+        out[2] = __uint_as_float(r.w.z); out[3] = __uint_as_float(r.w.w);
+        out[4] = __uint_as_float(r.w2.x); out[5] = __uint_as_float(r.w2.y);
+        out[6] = __uint_as_float(r.w2.z); out[7] = __uint_as_float(r.w2.w);
+    }
+}
+
+// Scored logit: x, or fl32(x * inv_t) for temperature-scaled scoring.  x * 1 = x exactly, so
+// the unscaled instantiations compute the same bits as a scaled call with inv_t = 1.
+template <bool SCALED>
+__device__ __forceinline__ float scored(float x, float inv_t) {
+    return SCALED ? x * inv_t : x;
+}
+
 // The tile held by one wave: v[8*k + e] is column tile_start + 512*k + 8*lane + e.
 struct TileRegs {
     float v[kPerLane];
 };
 
-__device__ __forceinline__ void unpack8(const u32x4& w, float* out) {
-    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
-    out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z);
-    out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+// Raw bits of row[c], or -inf when c is at or past `lim` (never touched in memory).
+template <Dt D>
+__device__ __forceinline__ uint32_t masked_bits(const typename DtInfo<D>::Storage* __restrict__ row,
+                                                int c, int lim) {
+    return c < lim ? static_cast<uint32_t>(row[c]) : DtInfo<D>::kNegInfBits;
 }
 
-constexpr uint32_t kNegInfBits = 0xFF80u;  // BF16 -inf
-
-// Raw BF16 bits of row[c], or -inf when c is at or past `lim` (never touched in memory).
-__device__ __forceinline__ uint32_t masked_bits(const uint16_t* __restrict__ row, int c, int lim) {
-    return c < lim ? static_cast<uint32_t>(row[c]) : kNegInfBits;
+// The 8 values at view columns [c, c+8) of a row (c a multiple of 8).  Columns at or past
+// `lim` (the number of real columns in the view) read as -inf and are never touched in
+// memory.  VEC allows 16-byte loads when all 8 are real (it needs 16-byte aligned rows);
+// otherwise each value is an element load.  Both fill r identically.
+template <Dt D, bool VEC>
+__device__ __forceinline__ void load8(const typename DtInfo<D>::Storage* __restrict__ row, int c,
+                                      int lim, Raw8<D>& r) {
+    if (VEC && c + kVec <= lim) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + c);
+        r.w = __builtin_nontemporal_load(p);
+        if constexpr (D == Dt::F32) r.w2 = __builtin_nontemporal_load(p + 1);
+        return;
+    }
+    if constexpr (D == Dt::F32) {
+        r.w.x = masked_bits<D>(row, c + 0, lim); r.w.y = masked_bits<D>(row, c + 1, lim);
+        r.w.z = masked_bits<D>(row, c + 2, lim); r.w.w = masked_bits<D>(row, c + 3, lim);
+        r.w2.x = masked_bits<D>(row, c + 4, lim); r.w2.y = masked_bits<D>(row, c + 5, lim);
+        r.w2.z = masked_bits<D>(row, c + 6, lim); r.w2.w = masked_bits<D>(row, c + 7, lim);
+    } else {
+        r.w.x = masked_bits<D>(row, c + 0, lim) | (masked_bits<D>(row, c + 1, lim) << 16);
+        r.w.y = masked_bits<D>(row, c + 2, lim) | (masked_bits<D>(row, c + 3, lim) << 16);
+        r.w.z = masked_bits<D>(row, c + 4, lim) | (masked_bits<D>(row, c + 5, lim) << 16);
+        r.w.w = masked_bits<D>(row, c + 6, lim) | (masked_bits<D>(row, c + 7, lim) << 16);
+    }
 }
 
-// Loads one tile of a row as raw BF16 bits: w[k] holds view columns
-// start + 512k + 8*lane + [0, 8).  `lim` is the number of real columns in the view: columns at
-// or past it read as -inf and are never touched in memory.  VEC allows 16-byte loads (it needs
-// a 16-byte aligned row start and is used for every 8 columns that are all real); otherwise
-// each value is a 2-byte load.  Both fill w[] with the same bits.  All loads of the tile are
-// issued before any of them is used.
-template <bool VEC>
-__device__ __forceinline__ void load_tile_bits(const uint16_t* __restrict__ row, int start,
-                                               int lim, int lane, u32x4* w) {
+// One tile of a row as raw bits: r[k] holds view columns start + 512k + 8*lane + [0, 8);
+// `start` is the tile's first view column.  All loads of the tile are issued before any of
+// them is used.
+template <Dt D, bool VEC>
+__device__ __forceinline__ void load_tile_raw(const typename DtInfo<D>::Storage* __restrict__ row,
+                                              int start, int lim, int lane, Raw8<D>* r) {
     const int base = start + kVec * lane;
-    if (VEC && start + kTile <= lim) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + base);
 #pragma unroll
-        for (int k = 0; k < kLoads; ++k)
-            w[k] = __builtin_nontemporal_load(p + k * (kLoadStride / kVec));
+    for (int k = 0; k < kLoads; ++k) load8<D, VEC>(row, base + k * kLoadStride, lim, r[k]);
+}
+
+// The same tile as FP32 values (exact widening; masked columns are -inf).  Scoring with a
+// temperature is applied later, in tile_stats.
+template <Dt D, bool VEC>
+__device__ __forceinline__ void load_tile(const typename DtInfo<D>::Storage* __restrict__ row,
+                                          int start, int lim, int lane, TileRegs& t) {
+    Raw8<D> r[kLoads];
+    load_tile_raw<D, VEC>(row, start, lim, lane, r);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) unpack8<D>(r[k], &t.v[k * kVec]);
+}
+
+// Round 8 gradients to the output dtype (nearest, ties to even) and store them at view
+// columns [c, c+8) of an output row: 16-byte stores when VEC and all 8 lie inside `width`,
+// element stores for the columns below `width` otherwise.
+template <Dt D, bool VEC>
+__device__ __forceinline__ void store8(typename DtInfo<D>::Storage* out, int c, int width,
+                                       const float* d) {
+    uint32_t q[8];
+    if constexpr (D == Dt::F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = __float_as_uint(d[e]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (D == Dt::BF16) {
+                bf16x2 v;
+                v.x = static_cast<__bf16>(d[2 * i]);
+                v.y = static_cast<__bf16>(d[2 * i + 1]);
+                q[i] = __builtin_bit_cast(uint32_t, v);
+            } else {
+                f16x2 v;
+                v.x = static_cast<_Float16>(d[2 * i]);
+                v.y = static_cast<_Float16>(d[2 * i + 1]);
+                q[i] = __builtin_bit_cast(uint32_t, v);
+            }
+        }
+    }
+    if (VEC && c + kVec <= width) {
+        u32x4* p = reinterpret_cast<u32x4*>(out + c);
+        __builtin_nontemporal_store(u32x4{q[0], q[1], q[2], q[3]}, p);
+        if constexpr (D == Dt::F32) __builtin_nontemporal_store(u32x4{q[4], q[5], q[6], q[7]}, p + 1);
         return;
     }
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        const int c = base + k * kLoadStride;
-        if (VEC && c + kVec <= lim) {
-            w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c));
-        } else {
-            w[k].x = masked_bits(row, c + 0, lim) | (masked_bits(row, c + 1, lim) << 16);
-            w[k].y = masked_bits(row, c + 2, lim) | (masked_bits(row, c + 3, lim) << 16);
-            w[k].z = masked_bits(row, c + 4, lim) | (masked_bits(row, c + 5, lim) << 16);
-            w[k].w = masked_bits(row, c + 6, lim) | (masked_bits(row, c + 7, lim) << 16);
-        }
+    for (int e = 0; e < kVec; ++e) {
+        if (c + e >= width) continue;
+        if constexpr (D == Dt::F32)
+            out[c + e] = q[e];
+        else
+            out[c + e] = static_cast<uint16_t>(e & 1 ? q[e / 2] >> 16 : q[e / 2] & 0xFFFFu);
     }
-}
-
-// The same tile as FP32 values (exact BF16 promotion; masked columns are -inf).
-template <bool VEC>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ row, int start, int lim,
-                                          int lane, TileRegs& t) {
-    u32x4 w[kLoads];
-    load_tile_bits<VEC>(row, start, lim, lane, w);
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) unpack8(w[k], &t.v[k * kVec]);
 }
 
 // ------------------------------------------------------------------ lane tree
@@ -146,20 +264,35 @@ __device__ __forceinline__ ExpSplit bwd_exp_split(float t) {
     return r;
 }
 
-// -g/S * exp(x - M) for a tile in which every x - M >= -87 (so every exp is a normal float and
-// the single product rounds correctly even when it lands in the subnormal range).
-__device__ __forceinline__ float bwd_term(float x, float M, float neg_c) {
-    const ExpSplit s = bwd_exp_split(x - M);
+// Rounding error of s = fl(a + b): a + b = s + err exactly (Knuth's two-sum, 6 operations).
+__device__ __forceinline__ float two_sum_err(float a, float b, float s) {
+    const float bb = s - a;
+    return (a - (s - bb)) + (b - bb);
+}
+
+// -g/S * exp(z - M) for a tile in which every z - M >= -87 (so every exp is a normal float and
+// the single product rounds correctly even when it lands in the subnormal range).  When z - M
+// is not exact in FP32 (FP32 logits, or scored ones z = fl32(x * inv_t)), TWO_SUM adds its
+// rounding error to delta, so the result is exp of the exact difference.
+template <bool TWO_SUM>
+__device__ __forceinline__ float bwd_term(float z, float M, float neg_c) {
+    const float t = z - M;
+    ExpSplit s = bwd_exp_split(t);
+    if (TWO_SUM) s.delta = s.delta + two_sum_err(z, -M, t);
     const float e0 = __builtin_amdgcn_exp2f(s.u);
     return __builtin_fmaf(e0, s.delta, e0) * neg_c;
 }
 
-// Same value for any x - M (including -inf).  Where 2^u would be subnormal (u < -126), where
+// Same value for any z - M (including -inf).  Where 2^u would be subnormal (u < -126), where
 // the hardware exp2 returns zero, it is computed as 2^(u+64) (u + 64 is exact there) and
 // multiplied by neg_c_lo = neg_c * 2^-64, which rounds the product exactly as neg_c * e would.
 // For u >= -126 it performs the same operations as bwd_term, so both give identical bits.
-__device__ __forceinline__ float bwd_term_deep(float x, float M, float neg_c, float neg_c_lo) {
-    const ExpSplit s = bwd_exp_split(fmaxf(x - M, -150.0f));
+template <bool TWO_SUM>
+__device__ __forceinline__ float bwd_term_deep(float z, float M, float neg_c, float neg_c_lo) {
+    const float t = z - M;
+    const bool finite = t > -150.0f;  // exp(t) underflows to 0 below; -inf lands here too
+    ExpSplit s = bwd_exp_split(finite ? t : -150.0f);
+    if (TWO_SUM) s.delta = s.delta + (finite ? two_sum_err(z, -M, t) : 0.0f);
     const bool tiny = s.u < -126.0f;
     const float e0 = __builtin_amdgcn_exp2f(tiny ? s.u + 64.0f : s.u);
     return __builtin_fmaf(e0, s.delta, e0) * (tiny ? neg_c_lo : neg_c);
@@ -167,18 +300,21 @@ __device__ __forceinline__ float bwd_term_deep(float x, float M, float neg_c, fl
 
 // ------------------------------------------------------------------ tile statistics
 
-// (m, s) of one tile held in registers: m = max over the tile (exact), s = sum of
-// exp(x - m) with each lane adding its 64 values in index order from +0, then the lane tree.
-// A tile with no real column gives the (-inf, 0) identity.
-__device__ __forceinline__ void tile_stats(const TileRegs& t, float& m, float& s) {
+// (m, s) of one tile of scored logits z = scored(x) held in registers as x: m = max z (exact),
+// s = sum of exp(z - m) with each lane adding its 64 values in index order from +0, then the
+// lane tree.  Rounding x * inv_t is monotone for inv_t > 0, so max z = scored(max x) exactly
+// and the max pass runs on x; z is formed once per value in the sum pass.  A tile with no
+// real column gives the (-inf, 0) identity.
+template <bool SCALED>
+__device__ __forceinline__ void tile_stats(const TileRegs& t, float inv_t, float& m, float& s) {
     float lm = t.v[0];
 #pragma unroll
     for (int i = 1; i < kPerLane; ++i) lm = fmaxf(lm, t.v[i]);
-    m = wave_max(lm);
+    m = scored<SCALED>(wave_max(lm), inv_t);
     float ls = 0.0f;
     if (m != kNegInf) {
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) ls = ls + fwd_exp(t.v[i] - m);
+        for (int i = 0; i < kPerLane; ++i) ls = ls + fwd_exp(scored<SCALED>(t.v[i], inv_t) - m);
     }
     s = wave_sum(ls);
 }

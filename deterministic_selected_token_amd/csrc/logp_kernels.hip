@@ -5,14 +5,20 @@
 //             the canonical merge (RL-Kernel issue #241, "PR 3"; PR #314 Tensor Parallel
 //             doc, steps 1-6).  One HBM pass over the logits, nothing else written but
 //             logp / LSE / (M, S).
-//   backward  one wave per (row, tile): read the tile once, write
-//             dlogits = g (onehot - exp(x - M) / S) rounded to BF16 straight from
-//             registers (PR #495 "zero-workspace backward for generic CUDA fused logp",
-//             Summary item 2: no FP32 [N, V] workspace; a single read instead of the
-//             three the pages' kernel needs, Results section).
+//   backward  dlogits = g (onehot - exp(x - M) / S) rounded to the logits' dtype straight
+//             from registers (PR #495 "zero-workspace backward for generic CUDA fused
+//             logp", Summary item 2: no FP32 [N, V] workspace; one read of the logits instead
+//             of the three its kernel needs, Results section).  Element-wise, so its work
+//             split is free: a flat walk over 16-byte vectors for aligned views, (row, tile)
+//             items otherwise.
 //   partials  one wave per (row, tile of the shard): the forward's tile reduction, written
 //             out as (m_l, s_l, sel_l) (issue #241, "PR6").
 //   merge     one wave per row over [L] partials: the forward's merge code.
+//
+// Every kernel is instantiated for BF16, FP16 and FP32 logits (PR #495, Tests: FP32 / BF16 /
+// FP16) and for temperature-scaled scoring, z = fl32(x * inv_temperature) (the rollout
+// temperatures of the provider experiment in PR #495's author reply); the unscaled
+// instantiations compute exactly what a scaled one computes with inv_temperature = 1.
 //
 // Host entry points validate every argument before launching and report failures as
 // status codes (see include/logp.h).
@@ -20,6 +26,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "logp.h"
 #include "logp_device.hpp"
@@ -28,25 +35,21 @@ using namespace logp;
 
 namespace {
 
-constexpr int kFwdWaves = 4;     // waves per forward workgroup (one row)
-constexpr int kItemWaves = 4;    // waves per workgroup of the partials kernel
-constexpr int kBwdWaves = 16;    // waves per backward workgroup
-constexpr int kBwdTilesPerWave = 2;  // consecutive (row, tile) items per backward wave
-constexpr int kMergeWaves = 4;   // rows per merge workgroup
+constexpr int kFwdWaves = 4;         // waves per forward workgroup (one row)
+constexpr int kItemWaves = 4;        // waves per workgroup of the partials kernel
+constexpr int kBwdWaves = 16;        // waves per backward workgroup
+constexpr int kBwdTilesPerWave = 2;  // consecutive (row, tile) items per tile-path wave
+// FP32 tiles take twice the registers: one item per wave and 512-thread workgroups keep them
+// clear of the register cap that 1024-thread workgroups impose (128 per lane).
+template <Dt D>
+constexpr int bwd_tiles_per_wave() { return D == Dt::F32 ? 1 : kBwdTilesPerWave; }
+template <Dt D>
+constexpr int bwd_tile_waves() { return D == Dt::F32 ? 8 : kBwdWaves; }
+constexpr int kMergeWaves = 4;       // rows per merge workgroup
 constexpr int kCheckThreads = 1024;
 // Largest padded width: keeps vocab_padded + kTile below 2^31 so in-row column arithmetic
 // never overflows a 32-bit int.
 constexpr int64_t kMaxCols = (int64_t(1) << 31) - 1 - kTile;
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Round two floats to BF16 (nearest, ties to even) and pack them, low element first.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16x2 v;
-    v.x = static_cast<__bf16>(lo);
-    v.y = static_cast<__bf16>(hi);
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -77,16 +80,17 @@ __device__ __forceinline__ void write_row(const RowResult& r, int64_t row, float
 
 // ---------------------------------------------------------------------------- forward
 
-template <bool VEC>
+template <Dt D, bool VEC, bool SCALED>
 __global__ __launch_bounds__(kFwdWaves* kWave) void fwd_kernel(
-    const uint16_t* __restrict__ logits, int64_t ld, int vocab_real,
-    const int64_t* __restrict__ targets, const uint8_t* __restrict__ active, int64_t ignore_index,
-    float* __restrict__ logp, float* __restrict__ lse, logp_stats_t* __restrict__ stats) {
+    const typename DtInfo<D>::Storage* __restrict__ logits, int64_t ld, int vocab_real,
+    float inv_t, const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
+    int64_t ignore_index, float* __restrict__ logp, float* __restrict__ lse,
+    logp_stats_t* __restrict__ stats) {
     extern __shared__ float2 slots[];  // (m_l, s_l) per real tile
     const int64_t row = blockIdx.x;
     const int wave = wave_id();
     const int lane = lane_id();
-    const uint16_t* __restrict__ x = logits + row * ld;
+    const typename DtInfo<D>::Storage* __restrict__ x = logits + row * ld;
     const int real_tiles = (vocab_real + kTile - 1) / kTile;
 
     // Wave 0 fetches the target and its logit first so the gather overlaps the streaming.
@@ -95,14 +99,14 @@ __global__ __launch_bounds__(kFwdWaves* kWave) void fwd_kernel(
     float sel = 0.0f;
     if (wave == 0) {
         valid = row_valid(targets, active, ignore_index, vocab_real, row, y);
-        if (valid) sel = bf16_to_f32(x[y]);
+        if (valid) sel = scored<SCALED>(elem_to_f32<D>(x[y]), inv_t);
     }
 
     for (int l = wave; l < real_tiles; l += kFwdWaves) {
         TileRegs t;
-        load_tile<VEC>(x, l * kTile, vocab_real, lane, t);
+        load_tile<D, VEC>(x, l * kTile, vocab_real, lane, t);
         float m, s;
-        tile_stats(t, m, s);
+        tile_stats<SCALED>(t, inv_t, m, s);
         if (lane == 0) slots[l] = make_float2(m, s);
     }
     __syncthreads();
@@ -117,30 +121,31 @@ __global__ __launch_bounds__(kFwdWaves* kWave) void fwd_kernel(
 
 // --------------------------------------------------------------------------- partials
 
-template <bool VEC>
+template <Dt D, bool VEC, bool SCALED>
 __global__ __launch_bounds__(kItemWaves* kWave) void partials_kernel(
-    const uint16_t* __restrict__ logits, int64_t ld, int64_t n, int view_tiles, int lim,
-    int64_t col_begin, int64_t col_end, int64_t vocab_real, const int64_t* __restrict__ targets,
-    const uint8_t* __restrict__ active, int64_t ignore_index, logp_partial_t* __restrict__ partials,
-    int64_t ldp) {
+    const typename DtInfo<D>::Storage* __restrict__ logits, int64_t ld, int64_t n,
+    int view_tiles, int lim, int64_t col_begin, int64_t col_end, int64_t vocab_real, float inv_t,
+    const int64_t* __restrict__ targets, const uint8_t* __restrict__ active, int64_t ignore_index,
+    logp_partial_t* __restrict__ partials, int64_t ldp) {
     const int64_t item = int64_t(blockIdx.x) * kItemWaves + wave_id();
     if (item >= n * view_tiles) return;  // whole wave leaves; this kernel has no barrier
     const int lane = lane_id();
     const int64_t row = item / view_tiles;
     const int j = static_cast<int>(item - row * view_tiles);
     const int start = j * kTile;
-    const uint16_t* __restrict__ x = logits + row * ld;
+    const typename DtInfo<D>::Storage* __restrict__ x = logits + row * ld;
 
     TileRegs t;
-    load_tile<VEC>(x, start, lim, lane, t);
+    load_tile<D, VEC>(x, start, lim, lane, t);
     float m, s;
-    tile_stats(t, m, s);
+    tile_stats<SCALED>(t, inv_t, m, s);
     if (lane == 0) {
         int64_t y;
         const bool valid = row_valid(targets, active, ignore_index, vocab_real, row, y);
         const int64_t g0 = col_begin + start;  // global column of this tile's first entry
         float sel = 0.0f;
-        if (valid && y >= g0 && y < g0 + kTile && y < col_end) sel = bf16_to_f32(x[y - col_begin]);
+        if (valid && y >= g0 && y < g0 + kTile && y < col_end)
+            sel = scored<SCALED>(elem_to_f32<D>(x[y - col_begin]), inv_t);
         logp_partial_t* out = partials + row * ldp + j;
         out->max = m;
         out->sumexp = s;
@@ -171,213 +176,177 @@ __global__ __launch_bounds__(kMergeWaves* kWave) void merge_kernel(
 
 // --------------------------------------------------------------------------- backward
 
-// Writes 8 consecutive outputs starting at view column c (c is a multiple of 8): one
-// 16-byte store when the vector path is allowed and all 8 lie inside the row, else
-// element-wise stores for the columns below `width`.
-template <bool VEC>
-__device__ __forceinline__ void store8(uint16_t* out, int c, int width, const float* d) {
-    if (VEC && c + kVec <= width) {
-        u32x4 w;
-        w.x = pack_bf16x2(d[0], d[1]);
-        w.y = pack_bf16x2(d[2], d[3]);
-        w.z = pack_bf16x2(d[4], d[5]);
-        w.w = pack_bf16x2(d[6], d[7]);
-        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(out + c));
-    } else {
-#pragma unroll
-        for (int e = 0; e < kVec; e += 2) {
-            const uint32_t w = pack_bf16x2(d[e], d[e + 1]);
-            if (c + e < width) out[c + e] = static_cast<uint16_t>(w & 0xFFFFu);
-            if (c + e + 1 < width) out[c + e + 1] = static_cast<uint16_t>(w >> 16);
-        }
-    }
-}
-
-// Per-item (row, tile) state of the backward.
-struct BwdItem {
-    int64_t row, y;
-    int start;      // first view column of the tile
-    bool valid;     // row valid and its stats finite
-    float M, g, neg_c, neg_c_lo;
+// Per-row constants of the backward.
+struct BwdRow {
+    bool valid;  // row valid and its stats finite
+    float M, g, neg_c, neg_c_lo;  // g is the scored upstream gradient g * inv_t
+    int64_t y;   // target in view coordinates
+    float thr;   // raw logits below this may need the subnormal-safe path (see below)
 };
 
-// Row-side inputs of one item: validity, (M, S), g and the per-row scale -g/S.  The stats and
-// g loads do not wait for the validity test (they are in bounds for every row), so one
-// memory round trip resolves all of them.
-__device__ __forceinline__ BwdItem bwd_item(int64_t item, int view_tiles,
-                                            const int64_t* __restrict__ targets,
-                                            const uint8_t* __restrict__ active,
-                                            int64_t ignore_index, int64_t vocab_real,
-                                            const float* __restrict__ grad,
-                                            const logp_stats_t* __restrict__ stats) {
-    BwdItem it;
-    it.row = item / view_tiles;
-    it.start = static_cast<int>(item - it.row * view_tiles) * kTile;
-    const float M = stats[it.row].max, S = stats[it.row].sumexp, g = grad[it.row];
-    it.valid = row_valid(targets, active, ignore_index, vocab_real, it.row, it.y) && M != kNegInf;
-    it.M = M;
-    it.g = g;
-    it.neg_c = -(g / S);                // -g/S, one rounding per row
-    it.neg_c_lo = it.neg_c * 0x1p-64f;  // exact unless |g/S| < 2^-62
-    return it;
+// The stats and g loads do not wait for the validity test (they are in bounds for every
+// row), so one memory round trip resolves all of them.
+template <bool SCALED>
+__device__ __forceinline__ BwdRow bwd_row(int64_t row, int64_t col_begin, int64_t vocab_real,
+                                          float inv_t, const int64_t* __restrict__ targets,
+                                          const uint8_t* __restrict__ active,
+                                          int64_t ignore_index, const float* __restrict__ grad,
+                                          const logp_stats_t* __restrict__ stats) {
+    BwdRow r;
+    const float M = stats[row].max, S = stats[row].sumexp;
+    int64_t y;
+    r.valid = row_valid(targets, active, ignore_index, vocab_real, row, y) && M != kNegInf;
+    r.M = M;
+    r.g = SCALED ? grad[row] * inv_t : grad[row];  // d z / d x = inv_t
+    r.neg_c = -(r.g / S);                          // -g/S, one rounding per row
+    r.neg_c_lo = r.neg_c * 0x1p-64f;               // exact unless |g/S| < 2^-62
+    r.y = y - col_begin;
+    // exp(z - M) may leave the normal range only where z - M < -87, i.e. for raw logits
+    // below (M - 87) / inv_t; the margin of one unit absorbs the roundings of z and of this
+    // quotient.  False alarms only select the slower path, which gives the same bits.
+    r.thr = SCALED ? (M - 86.0f) / inv_t : M - 87.0f;
+    return r;
 }
 
-// True when some value of the packed tile may lie below M - 87 (so exp(x - M) could fall
-// outside the normal range).  Works on raw BF16 bits: a negative value below the threshold
-// has larger unsigned bits than the threshold truncated toward zero, and false alarms only
-// select the slower path, which gives the same bits.
-__device__ __forceinline__ bool bwd_needs_deep(const u32x4* w, float M) {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    const float thr = M - 87.0f;
-    u16x2 mx = {0, 0};
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].x));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].y));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].z));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].w));
+// True when some value of the raw tile words may lie below `thr` (a per-lane threshold).
+// Works on raw bits: for a negative threshold, a value below it has larger unsigned
+// magnitude bits than the threshold rounded toward zero (RTZ keeps the test conservative).
+template <Dt D>
+__device__ __forceinline__ bool below_threshold(const Raw8<D>& r, float thr) {
+    if (!(thr < 0.0f)) return true;  // non-negative (or NaN) threshold: always the safe path
+    if constexpr (D == Dt::F32) {
+        const uint32_t t = __float_as_uint(thr);
+        const uint32_t m = std::max(std::max(std::max(r.w.x, r.w.y), std::max(r.w.z, r.w.w)),
+                                    std::max(std::max(r.w2.x, r.w2.y), std::max(r.w2.z, r.w2.w)));
+        return m > t;
+    } else {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        unsigned t16;
+        if constexpr (D == Dt::BF16) {
+            t16 = __float_as_uint(thr) >> 16;  // truncation = rounding toward zero
+        } else {
+            typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+            const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(thr, thr);  // round toward zero
+            t16 = __builtin_bit_cast(uint32_t, h) & 0xFFFFu;
+        }
+        u16x2 mx = __builtin_elementwise_max(__builtin_bit_cast(u16x2, r.w.x),
+                                             __builtin_bit_cast(u16x2, r.w.y));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, r.w.z));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, r.w.w));
+        return mx.x > t16 || mx.y > t16;
     }
-    const unsigned t16 = 0x8000u | ((__float_as_uint(thr) >> 16) & 0x7FFFu);
-    return __any(thr >= 0.0f || mx.x > t16 || mx.y > t16);
 }
 
-// Gradient of the 8 columns at view column c of one item, from their logits v[0..7].
-template <bool DEEP>
-__device__ __forceinline__ void bwd_vec(const BwdItem& it, const float* v, int c, int lim,
-                                        bool partial, float* d) {
+// Gradient of the 8 columns at view column c from their scored logits v[0..7].
+template <bool DEEP, bool TWO_SUM>
+__device__ __forceinline__ void bwd_vec(const BwdRow& r, const float* v, int c, int lim,
+                                        float* d) {
 #pragma unroll
     for (int e = 0; e < kVec; ++e)
-        d[e] = DEEP ? bwd_term_deep(v[e], it.M, it.neg_c, it.neg_c_lo)
-                    : bwd_term(v[e], it.M, it.neg_c);
-    const int64_t yo = it.y - c;  // the target's offset from c (within this view)
+        d[e] = DEEP ? bwd_term_deep<TWO_SUM>(v[e], r.M, r.neg_c, r.neg_c_lo)
+                    : bwd_term<TWO_SUM>(v[e], r.M, r.neg_c);
+    const int64_t yo = r.y - c;  // the target's offset from c
     if (yo >= 0 && yo < kVec) {
 #pragma unroll
         for (int e = 0; e < kVec; ++e)
-            if (e == yo) d[e] = it.g + d[e];  // g * (1 - p)
+            if (e == yo) d[e] = r.g + d[e];  // g * (1 - p)
     }
-    if (partial) {
+    if (c + kVec > lim) {
 #pragma unroll
         for (int e = 0; e < kVec; ++e)
             if (c + e >= lim) d[e] = 0.0f;  // padding and past-the-vocab columns
     }
 }
 
-template <bool VEC_IN, bool VEC_OUT>
-__global__ __launch_bounds__(kBwdWaves* kWave) void bwd_kernel(
-    const uint16_t* logits, int64_t ld, int64_t n, int view_tiles, int width, int lim,
-    int64_t col_begin, int64_t vocab_real, const int64_t* __restrict__ targets,
-    const uint8_t* __restrict__ active, int64_t ignore_index, const float* __restrict__ grad,
-    const logp_stats_t* __restrict__ stats, uint16_t* dlogits, int64_t ld_out) {
+template <Dt D, bool SCALED>
+__device__ __forceinline__ void bwd_compute_store(const BwdRow& r, const Raw8<D>& raw, bool deep,
+                                                  float inv_t, int c, int lim, float* d) {
+    // z - M is exact for unscaled BF16 / FP16 values (short significands); otherwise its
+    // rounding error is carried into the exponential.
+    constexpr bool kTwoSum = SCALED || D == Dt::F32;
+    float v[kVec];
+    unpack8<D>(raw, v);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) v[e] = scored<SCALED>(v[e], inv_t);
+    if (!deep) bwd_vec<false, kTwoSum>(r, v, c, lim, d);
+    else bwd_vec<true, kTwoSum>(r, v, c, lim, d);
+}
+
+// (row, tile) items: any alignment, any width.  Each wave owns kBwdTilesPerWave consecutive
+// items and issues all their loads before computing any of them.
+template <Dt D, bool VEC_IN, bool VEC_OUT, bool SCALED>
+__global__ __launch_bounds__(bwd_tile_waves<D>() * kWave) void bwd_kernel(
+    const typename DtInfo<D>::Storage* logits, int64_t ld, int64_t n, int view_tiles, int width,
+    int lim, int64_t col_begin, int64_t vocab_real, float inv_t,
+    const int64_t* __restrict__ targets, const uint8_t* __restrict__ active, int64_t ignore_index,
+    const float* __restrict__ grad, const logp_stats_t* __restrict__ stats,
+    typename DtInfo<D>::Storage* dlogits, int64_t ld_out) {
     // logits and dlogits may be the same buffer: every element is loaded into registers
     // before the lane that loaded it stores to it, and no other lane touches it.
-    const int64_t first = (int64_t(blockIdx.x) * kBwdWaves + wave_id()) * kBwdTilesPerWave;
+    constexpr int TPW = bwd_tiles_per_wave<D>();
+    const int64_t first = (int64_t(blockIdx.x) * bwd_tile_waves<D>() + wave_id()) * TPW;
     const int64_t total = n * view_tiles;
     if (first >= total) return;  // whole wave leaves; this kernel has no barrier
     const int lane = lane_id();
 
-    BwdItem it[kBwdTilesPerWave];
+    int64_t row[TPW];
+    int start[TPW];
+    BwdRow r[TPW];
 #pragma unroll
-    for (int i = 0; i < kBwdTilesPerWave; ++i)
-        if (first + i < total)
-            it[i] = bwd_item(first + i, view_tiles, targets, active, ignore_index, vocab_real,
-                             grad, stats);
-    // Issue the loads of every tile this wave owns before computing any of them, so the
-    // second tile's bytes are in flight while the first is processed.  Invalid rows are not
-    // read.
-    u32x4 w[kBwdTilesPerWave][kLoads];
-#pragma unroll
-    for (int i = 0; i < kBwdTilesPerWave; ++i)
-        if (first + i < total && it[i].valid)
-            load_tile_bits<VEC_IN>(logits + it[i].row * ld, it[i].start, lim, lane, w[i]);
-#pragma unroll
-    for (int i = 0; i < kBwdTilesPerWave; ++i) {
+    for (int i = 0; i < TPW; ++i) {
         if (first + i >= total) break;
-        BwdItem t = it[i];
-        uint16_t* out = dlogits + t.row * ld_out;
-        const int base = t.start + kVec * lane;
-        if (!t.valid) {
+        row[i] = (first + i) / view_tiles;
+        start[i] = static_cast<int>(first + i - row[i] * view_tiles) * kTile;
+        r[i] = bwd_row<SCALED>(row[i], col_begin, vocab_real, inv_t, targets, active, ignore_index,
+                               grad, stats);
+    }
+    Raw8<D> w[TPW][kLoads];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+        if (first + i < total && r[i].valid)  // invalid rows are not read
+            load_tile_raw<D, VEC_IN>(logits + row[i] * ld, start[i], lim, lane, w[i]);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        if (first + i >= total) break;
+        typename DtInfo<D>::Storage* out = dlogits + row[i] * ld_out;
+        const int base = start[i] + kVec * lane;
+        if (!r[i].valid) {
             float z[kVec];
 #pragma unroll
             for (int e = 0; e < kVec; ++e) z[e] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < kLoads; ++k) store8<VEC_OUT>(out, base + k * kLoadStride, width, z);
+            for (int k = 0; k < kLoads; ++k) store8<D, VEC_OUT>(out, base + k * kLoadStride, width, z);
             continue;
         }
-        t.y -= col_begin;  // the target in view coordinates
-        const bool partial = t.start + kTile > lim;
-        const bool deep = bwd_needs_deep(w[i], t.M);  // masked columns (-inf) always count
+        bool hit = false;
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) hit = hit || below_threshold<D>(w[i][k], r[i].thr);
+        const bool deep = __any(hit);  // masked columns (-inf) always count
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) {
-            float v[kVec], d[kVec];
-            unpack8(w[i][k], v);
+            float d[kVec];
             const int c = base + k * kLoadStride;
-            if (!deep) bwd_vec<false>(t, v, c, lim, partial, d);
-            else bwd_vec<true>(t, v, c, lim, partial, d);
-            store8<VEC_OUT>(out, c, width, d);
+            bwd_compute_store<D, SCALED>(r[i], w[i][k], deep, inv_t, c, lim, d);
+            store8<D, VEC_OUT>(out, c, width, d);
         }
     }
 }
 
-// Backward over a dense, 16-byte aligned view whose width is a multiple of 8 and at least
-// one tile: the view is treated as the flat sequence of its [n, width/8] 16-byte vectors and
-// every wave takes kBwdTilesPerWave chunks of 512 consecutive vectors (lane l holds vectors
-// 64k + l of a chunk, so each load instruction still covers 1 KiB of contiguous memory).
-// The element-wise formulas are those of bwd_kernel, so the bits are the same; this split
-// just gives every wave the same amount of work whatever the row width.  A chunk spans at
-// most two rows (width >= 4096 columns = 512 vectors).
-struct FlatRow {
-    bool valid;
-    float M, g, neg_c, neg_c_lo;
-    int y;         // target in view coordinates (any value when invalid)
-    unsigned t16;  // raw-bits threshold of the subnormal-safe path test
-};
-
-__device__ __forceinline__ FlatRow flat_row(int64_t row, int64_t col_begin, int64_t vocab_real,
-                                            const int64_t* __restrict__ targets,
-                                            const uint8_t* __restrict__ active,
-                                            int64_t ignore_index, const float* __restrict__ grad,
-                                            const logp_stats_t* __restrict__ stats) {
-    FlatRow r;
-    const float M = stats[row].max, S = stats[row].sumexp;
-    int64_t y;
-    r.valid = row_valid(targets, active, ignore_index, vocab_real, row, y) && M != kNegInf;
-    r.M = M;
-    r.g = grad[row];
-    r.neg_c = -(r.g / S);
-    r.neg_c_lo = r.neg_c * 0x1p-64f;
-    r.y = static_cast<int>(y - col_begin);
-    const float thr = M - 87.0f;
-    r.t16 = thr >= 0.0f ? 0u : (0x8000u | ((__float_as_uint(thr) >> 16) & 0x7FFFu));
-    return r;
-}
-
-template <bool DEEP>
-__device__ __forceinline__ void flat_vec(const FlatRow& r, const float* v, int col, int lim,
-                                         float* d) {
-#pragma unroll
-    for (int e = 0; e < kVec; ++e)
-        d[e] = DEEP ? bwd_term_deep(v[e], r.M, r.neg_c, r.neg_c_lo)
-                    : bwd_term(v[e], r.M, r.neg_c);
-    const int yo = r.y - col;
-    if (yo >= 0 && yo < kVec) {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e)
-            if (e == yo) d[e] = r.g + d[e];  // g * (1 - p)
-    }
-    if (col + kVec > lim) {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e)
-            if (col + e >= lim) d[e] = 0.0f;  // padding columns
-    }
-}
-
+// Dense, 16-byte aligned views whose width is a multiple of 8 and at least one tile: the
+// view is the flat sequence of its [n, width/8] 8-element vectors and every wave takes 512
+// consecutive vectors (lane l holds vectors 64k + l, so each load instruction still covers
+// contiguous memory).  Same element-wise formulas as bwd_kernel, so the same bits; this split
+// just gives every wave the same amount of work whatever the row width.  A wave's vectors
+// span at most two rows (width >= 4096 columns = 512 vectors).
+template <Dt D, bool SCALED>
 __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
-    const uint16_t* logits, int64_t ld, int64_t n, int vpr, int lim, int64_t col_begin,
-    int64_t vocab_real, const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
-    int64_t ignore_index, const float* __restrict__ grad, const logp_stats_t* __restrict__ stats,
-    uint16_t* dlogits, int64_t ld_out) {
-    // logits and dlogits may be the same buffer: each 16-byte vector is loaded and stored by
-    // the same lane, load first.
+    const typename DtInfo<D>::Storage* logits, int64_t ld, int64_t n, int vpr, int lim,
+    int64_t col_begin, int64_t vocab_real, float inv_t, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ active, int64_t ignore_index, const float* __restrict__ grad,
+    const logp_stats_t* __restrict__ stats, typename DtInfo<D>::Storage* dlogits,
+    int64_t ld_out) {
+    // logits and dlogits may be the same buffer: each vector is loaded and stored by the
+    // same lane, load first.
     constexpr int kChunk = kWave * kLoads;  // 512 vectors per wave
     const int64_t total = n * vpr;
     const int64_t q0 = (int64_t(blockIdx.x) * kBwdWaves + wave_id()) * kChunk;
@@ -387,49 +356,30 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
     const int64_t row_a = q0 / vpr;
     const int64_t sp = (row_a + 1) * vpr - q0;
     const int split = sp < kChunk ? static_cast<int>(sp) : kChunk;  // vectors in row_a
-    const FlatRow ra = flat_row(row_a, col_begin, vocab_real, targets, active, ignore_index,
-                                grad, stats);
-    FlatRow rb = ra;
+    const BwdRow ra = bwd_row<SCALED>(row_a, col_begin, vocab_real, inv_t, targets, active,
+                                      ignore_index, grad, stats);
+    BwdRow rb = ra;
     if (split < kChunk && row_a + 1 < n)
-        rb = flat_row(row_a + 1, col_begin, vocab_real, targets, active, ignore_index, grad,
-                      stats);
+        rb = bwd_row<SCALED>(row_a + 1, col_begin, vocab_real, inv_t, targets, active,
+                             ignore_index, grad, stats);
 
-    // issue every load of the wave before computing
-    u32x4 w[kLoads];
+    Raw8<D> w[kLoads];
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
         const int idx = k * kWave + lane;
         const bool in_b = idx >= split;
         const int64_t row = row_a + (in_b ? 1 : 0);
         const int col = static_cast<int>(q0 + idx - row * vpr) * kVec;
-        if (q0 + idx < total && (in_b ? rb.valid : ra.valid)) {
-            const uint16_t* src = logits + row * ld;
-            if (col + kVec <= lim) {
-                w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + col));
-            } else {
-                w[k].x = masked_bits(src, col + 0, lim) | (masked_bits(src, col + 1, lim) << 16);
-                w[k].y = masked_bits(src, col + 2, lim) | (masked_bits(src, col + 3, lim) << 16);
-                w[k].z = masked_bits(src, col + 4, lim) | (masked_bits(src, col + 5, lim) << 16);
-                w[k].w = masked_bits(src, col + 6, lim) | (masked_bits(src, col + 7, lim) << 16);
-            }
-        }
+        if (q0 + idx < total && (in_b ? rb.valid : ra.valid))
+            load8<D, true>(logits + row * ld, col, lim, w[k]);
     }
-    // subnormal-safe path if any valid vector may hold x < M - 87 of its own row
     bool hit = false;
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
         const int idx = k * kWave + lane;
         const bool in_b = idx >= split;
-        const bool valid = in_b ? rb.valid : ra.valid;
-        const unsigned t16 = in_b ? rb.t16 : ra.t16;
-        if (q0 + idx < total && valid) {
-            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-            u16x2 mx = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[k].x),
-                                                 __builtin_bit_cast(u16x2, w[k].y));
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].z));
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[k].w));
-            hit = hit || t16 == 0u || mx.x > t16 || mx.y > t16;
-        }
+        if (q0 + idx < total && (in_b ? rb.valid : ra.valid))
+            hit = hit || below_threshold<D>(w[k], in_b ? rb.thr : ra.thr);
     }
     const bool deep = __any(hit);
 #pragma unroll
@@ -438,19 +388,16 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
         if (q0 + idx >= total) continue;
         const bool in_b = idx >= split;
         const int64_t row = row_a + (in_b ? 1 : 0);
-        const FlatRow r = in_b ? rb : ra;
+        const BwdRow r = in_b ? rb : ra;
         const int col = static_cast<int>(q0 + idx - row * vpr) * kVec;
         float d[kVec];
         if (!r.valid) {
 #pragma unroll
             for (int e = 0; e < kVec; ++e) d[e] = 0.0f;
         } else {
-            float v[kVec];
-            unpack8(w[k], v);
-            if (!deep) flat_vec<false>(r, v, col, lim, d);
-            else flat_vec<true>(r, v, col, lim, d);
+            bwd_compute_store<D, SCALED>(r, w[k], deep, inv_t, col, lim, d);
         }
-        store8<true>(dlogits + row * ld_out, col, vpr * kVec, d);
+        store8<D, true>(dlogits + row * ld_out, col, vpr * kVec, d);
     }
 }
 
@@ -613,6 +560,55 @@ uint32_t item_grid(int64_t n, int64_t tiles_per_row, int64_t items_per_block) {
     return blocks > 0x7FFFFFFF ? 0 : static_cast<uint32_t>(blocks);
 }
 
+// Kernel selection: one pointer per (dtype, load/store path, scaled) combination.
+template <Dt D>
+const void* fwd_ptr(bool vec, bool scaled) {
+    if (vec) return scaled ? reinterpret_cast<const void*>(&fwd_kernel<D, true, true>)
+                           : reinterpret_cast<const void*>(&fwd_kernel<D, true, false>);
+    return scaled ? reinterpret_cast<const void*>(&fwd_kernel<D, false, true>)
+                  : reinterpret_cast<const void*>(&fwd_kernel<D, false, false>);
+}
+
+template <Dt D>
+const void* partials_ptr(bool vec, bool scaled) {
+    if (vec) return scaled ? reinterpret_cast<const void*>(&partials_kernel<D, true, true>)
+                           : reinterpret_cast<const void*>(&partials_kernel<D, true, false>);
+    return scaled ? reinterpret_cast<const void*>(&partials_kernel<D, false, true>)
+                  : reinterpret_cast<const void*>(&partials_kernel<D, false, false>);
+}
+
+template <Dt D, bool SCALED>
+const void* bwd_ptr(bool vin, bool vout) {
+    if (vin) return vout ? reinterpret_cast<const void*>(&bwd_kernel<D, true, true, SCALED>)
+                         : reinterpret_cast<const void*>(&bwd_kernel<D, true, false, SCALED>);
+    return vout ? reinterpret_cast<const void*>(&bwd_kernel<D, false, true, SCALED>)
+                : reinterpret_cast<const void*>(&bwd_kernel<D, false, false, SCALED>);
+}
+
+template <Dt D>
+const void* bwd_ptr(bool vin, bool vout, bool scaled, bool flat) {
+    if (flat) return scaled ? reinterpret_cast<const void*>(&bwd_flat_kernel<D, true>)
+                            : reinterpret_cast<const void*>(&bwd_flat_kernel<D, false>);
+    return scaled ? bwd_ptr<D, true>(vin, vout) : bwd_ptr<D, false>(vin, vout);
+}
+
+// Element size of a dtype, or 0 when the value is not a logp_dtype_t.
+int64_t elem_bytes(logp_dtype_t dtype) {
+    switch (dtype) {
+        case LOGP_DTYPE_BF16: return 2;
+        case LOGP_DTYPE_F16: return 2;
+        case LOGP_DTYPE_F32: return 4;
+    }
+    return 0;
+}
+
+bool valid_inv_temperature(float inv_t) { return std::isfinite(inv_t) && inv_t > 0.0f; }
+
+// 16-byte loads/stores need an aligned view start and rows that stay aligned.
+bool vec_ok(const void* p, int64_t ld, int64_t elem) {
+    return aligned16(p) && (ld * elem) % 16 == 0;
+}
+
 }  // namespace
 
 // ============================================================================ C ABI
@@ -637,14 +633,18 @@ const char* logp_status_string(logp_status_t status) {
         case LOGP_ERR_RANGE: return "an array extends past the end of its allocation";
         case LOGP_ERR_OVERLAP: return "an output overlaps an input or another output";
         case LOGP_ERR_HIP: return "the HIP runtime reported an error";
+        case LOGP_ERR_ARG:
+            return "unknown dtype, or inv_temperature not a finite positive number";
     }
     return "unknown status";
 }
 
-logp_status_t logp_forward(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
-                           int64_t vocab_padded, const int64_t* targets, const uint8_t* active,
-                           int64_t ignore_index, float* logp, float* lse, logp_stats_t* stats,
-                           hipStream_t stream) {
+logp_status_t logp_forward_ex(logp_dtype_t dtype, float inv_temperature, const void* logits,
+                              int64_t ld, int64_t n, int64_t vocab_real, int64_t vocab_padded,
+                              const int64_t* targets, const uint8_t* active, int64_t ignore_index,
+                              float* logp, float* lse, logp_stats_t* stats, hipStream_t stream) {
+    const int64_t eb = elem_bytes(dtype);
+    if (eb == 0 || !valid_inv_temperature(inv_temperature)) return LOGP_ERR_ARG;
     logp_status_t st = check_vocab(n, vocab_real, vocab_padded);
     if (st != LOGP_OK) return st;
     if (ld < vocab_padded || logp_num_tiles(vocab_padded) > LOGP_FWD_MAX_TILES)
@@ -652,7 +652,7 @@ logp_status_t logp_forward(const uint16_t* logits, int64_t ld, int64_t n, int64_
     if (n > 0x7FFFFFFF) return LOGP_ERR_SHAPE;  // one workgroup per row on a 1-D grid
     if (n == 0) return LOGP_OK;
     if (logits == nullptr || targets == nullptr || logp == nullptr) return LOGP_ERR_NULL;
-    const uint64_t lg_bytes = span_bytes(n, ld, vocab_real, 2);
+    const uint64_t lg_bytes = span_bytes(n, ld, vocab_real, eb);
     if (lg_bytes == 0) return LOGP_ERR_SHAPE;
     const Span in[] = {{logits, lg_bytes}, {targets, uint64_t(n) * 8},
                        {active, active ? uint64_t(n) : 0}};
@@ -665,19 +665,34 @@ logp_status_t logp_forward(const uint16_t* logits, int64_t ld, int64_t n, int64_
     if (!guard.ok()) return LOGP_ERR_HIP;
 
     int vr = static_cast<int>(vocab_real);
-    void* args[] = {&logits, &ld, &vr, &targets, &active, &ignore_index, &logp, &lse, &stats};
-    const bool vec = aligned16(logits) && (ld % kVec) == 0;
-    const void* k = vec ? reinterpret_cast<const void*>(&fwd_kernel<true>)
-                        : reinterpret_cast<const void*>(&fwd_kernel<false>);
+    float inv_t = inv_temperature;
+    void* args[] = {&logits, &ld, &vr, &inv_t, &targets, &active, &ignore_index, &logp, &lse,
+                    &stats};
+    const bool vec = vec_ok(logits, ld, eb);
+    const bool scaled = inv_temperature != 1.0f;
+    const void* k = dtype == LOGP_DTYPE_BF16 ? fwd_ptr<Dt::BF16>(vec, scaled)
+                    : dtype == LOGP_DTYPE_F16 ? fwd_ptr<Dt::F16>(vec, scaled)
+                                              : fwd_ptr<Dt::F32>(vec, scaled);
     const size_t lds = size_t(ceil_div(vocab_real, kTile)) * sizeof(float2);
     return launch(k, dim3(static_cast<uint32_t>(n)), dim3(kFwdWaves * kWave), args, lds, stream);
 }
 
-logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
-                            int64_t vocab_padded, int64_t col_begin, int64_t col_end,
-                            const int64_t* targets, const uint8_t* active, int64_t ignore_index,
-                            const float* grad_logp, const logp_stats_t* stats, uint16_t* dlogits,
-                            int64_t ld_out, hipStream_t stream) {
+logp_status_t logp_forward(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
+                           int64_t vocab_padded, const int64_t* targets, const uint8_t* active,
+                           int64_t ignore_index, float* logp, float* lse, logp_stats_t* stats,
+                           hipStream_t stream) {
+    return logp_forward_ex(LOGP_DTYPE_BF16, 1.0f, logits, ld, n, vocab_real, vocab_padded,
+                           targets, active, ignore_index, logp, lse, stats, stream);
+}
+
+logp_status_t logp_backward_ex(logp_dtype_t dtype, float inv_temperature, const void* logits,
+                               int64_t ld, int64_t n, int64_t vocab_real, int64_t vocab_padded,
+                               int64_t col_begin, int64_t col_end, const int64_t* targets,
+                               const uint8_t* active, int64_t ignore_index,
+                               const float* grad_logp, const logp_stats_t* stats, void* dlogits,
+                               int64_t ld_out, hipStream_t stream) {
+    const int64_t eb = elem_bytes(dtype);
+    if (eb == 0 || !valid_inv_temperature(inv_temperature)) return LOGP_ERR_ARG;
     logp_status_t st = check_vocab(n, vocab_real, vocab_padded);
     if (st != LOGP_OK) return st;
     if (col_begin < 0 || col_end < col_begin || col_end > vocab_padded) return LOGP_ERR_SHARD;
@@ -689,14 +704,16 @@ logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64
         return LOGP_ERR_NULL;
     const int64_t lim = std::max<int64_t>(0, std::min(vocab_real, col_end) - col_begin);
     const int64_t view_tiles = ceil_div(width, kTile);
-    const uint32_t grid = item_grid(n, view_tiles, kBwdWaves * kBwdTilesPerWave);
-    const uint64_t in_bytes = span_bytes(n, ld, lim, 2);
-    const uint64_t out_bytes = span_bytes(n, ld_out, width, 2);
+    const bool f32 = dtype == LOGP_DTYPE_F32;
+    const int tile_waves = f32 ? bwd_tile_waves<Dt::F32>() : bwd_tile_waves<Dt::BF16>();
+    const int tpw = f32 ? bwd_tiles_per_wave<Dt::F32>() : bwd_tiles_per_wave<Dt::BF16>();
+    const uint32_t grid = item_grid(n, view_tiles, tile_waves * tpw);
+    const uint64_t in_bytes = span_bytes(n, ld, lim, eb);
+    const uint64_t out_bytes = span_bytes(n, ld_out, width, eb);
     if (grid == 0 || out_bytes == 0 || (lim > 0 && in_bytes == 0)) return LOGP_ERR_SHAPE;
     // In place is allowed only as an exact alias with the same row stride.
     Span alias = {nullptr, 0};
-    if (static_cast<const void*>(dlogits) == static_cast<const void*>(logits) && ld_out == ld)
-        alias = {logits, in_bytes};
+    if (dlogits == logits && ld_out == ld) alias = {logits, in_bytes};
     const Span in[] = {{logits, in_bytes}, {targets, uint64_t(n) * 8},
                        {active, active ? uint64_t(n) : 0}, {grad_logp, uint64_t(n) * 4},
                        {stats, uint64_t(n) * 8}};
@@ -713,34 +730,48 @@ logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64
     DeviceGuard guard(device);
     if (!guard.ok()) return LOGP_ERR_HIP;
 
-    int vt = static_cast<int>(view_tiles), w = static_cast<int>(width), li = static_cast<int>(lim);
-    void* args[] = {&logits, &ld, &n, &vt, &w, &li, &col_begin, &vocab_real, &targets, &active,
-                    &ignore_index, &grad_logp, &stats, &dlogits, &ld_out};
-    const bool vin = aligned16(logits) && (ld % kVec) == 0;
-    const bool vout = aligned16(dlogits) && (ld_out % kVec) == 0;
-    if (vin && vout && width % kVec == 0 && width >= kTile) {
+    const bool vin = vec_ok(logits, ld, eb);
+    const bool vout = vec_ok(dlogits, ld_out, eb);
+    const bool scaled = inv_temperature != 1.0f;
+    const bool flat = vin && vout && width % kVec == 0 && width >= kTile;
+    const void* k = dtype == LOGP_DTYPE_BF16 ? bwd_ptr<Dt::BF16>(vin, vout, scaled, flat)
+                    : dtype == LOGP_DTYPE_F16 ? bwd_ptr<Dt::F16>(vin, vout, scaled, flat)
+                                              : bwd_ptr<Dt::F32>(vin, vout, scaled, flat);
+    float inv_t = inv_temperature;
+    int li = static_cast<int>(lim);
+    if (flat) {
         const int64_t vectors = n * (width / kVec);
-        const int64_t per_block = int64_t(kBwdWaves) * kWave * kLoads;  // 512 vectors per wave
-        const int64_t blocks = ceil_div(vectors, per_block);
+        const int64_t blocks = ceil_div(vectors, int64_t(kBwdWaves) * kWave * kLoads);
         if (blocks > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
-        int vpr = static_cast<int>(width / kVec), li = static_cast<int>(lim);
-        void* fargs[] = {&logits, &ld, &n, &vpr, &li, &col_begin, &vocab_real, &targets,
-                         &active, &ignore_index, &grad_logp, &stats, &dlogits, &ld_out};
-        return launch(reinterpret_cast<const void*>(&bwd_flat_kernel),
-                      dim3(static_cast<uint32_t>(blocks)), dim3(kBwdWaves * kWave), fargs, 0,
+        int vpr = static_cast<int>(width / kVec);
+        void* args[] = {&logits, &ld, &n, &vpr, &li, &col_begin, &vocab_real, &inv_t, &targets,
+                        &active, &ignore_index, &grad_logp, &stats, &dlogits, &ld_out};
+        return launch(k, dim3(static_cast<uint32_t>(blocks)), dim3(kBwdWaves * kWave), args, 0,
                       stream);
     }
-    const void* k = vin ? (vout ? reinterpret_cast<const void*>(&bwd_kernel<true, true>)
-                                : reinterpret_cast<const void*>(&bwd_kernel<true, false>))
-                        : (vout ? reinterpret_cast<const void*>(&bwd_kernel<false, true>)
-                                : reinterpret_cast<const void*>(&bwd_kernel<false, false>));
-    return launch(k, dim3(grid), dim3(kBwdWaves * kWave), args, 0, stream);
+    int vt = static_cast<int>(view_tiles), w = static_cast<int>(width);
+    void* args[] = {&logits, &ld, &n, &vt, &w, &li, &col_begin, &vocab_real, &inv_t, &targets,
+                    &active, &ignore_index, &grad_logp, &stats, &dlogits, &ld_out};
+    return launch(k, dim3(grid), dim3(tile_waves * kWave), args, 0, stream);
 }
 
-logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
+logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
                             int64_t vocab_padded, int64_t col_begin, int64_t col_end,
                             const int64_t* targets, const uint8_t* active, int64_t ignore_index,
-                            logp_partial_t* partials, int64_t ldp, hipStream_t stream) {
+                            const float* grad_logp, const logp_stats_t* stats, uint16_t* dlogits,
+                            int64_t ld_out, hipStream_t stream) {
+    return logp_backward_ex(LOGP_DTYPE_BF16, 1.0f, logits, ld, n, vocab_real, vocab_padded,
+                            col_begin, col_end, targets, active, ignore_index, grad_logp, stats,
+                            dlogits, ld_out, stream);
+}
+
+logp_status_t logp_partials_ex(logp_dtype_t dtype, float inv_temperature, const void* logits,
+                               int64_t ld, int64_t n, int64_t vocab_real, int64_t vocab_padded,
+                               int64_t col_begin, int64_t col_end, const int64_t* targets,
+                               const uint8_t* active, int64_t ignore_index,
+                               logp_partial_t* partials, int64_t ldp, hipStream_t stream) {
+    const int64_t eb = elem_bytes(dtype);
+    if (eb == 0 || !valid_inv_temperature(inv_temperature)) return LOGP_ERR_ARG;
     logp_status_t st = check_vocab(n, vocab_real, vocab_padded);
     if (st != LOGP_OK) return st;
     if (col_begin < 0 || col_end <= col_begin || col_end > vocab_padded ||
@@ -753,7 +784,7 @@ logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t n, int64
     if (logits == nullptr || targets == nullptr || partials == nullptr) return LOGP_ERR_NULL;
     const int64_t lim = std::max<int64_t>(0, std::min(vocab_real, col_end) - col_begin);
     const uint32_t grid = item_grid(n, view_tiles, kItemWaves);
-    const uint64_t in_bytes = span_bytes(n, ld, lim, 2);
+    const uint64_t in_bytes = span_bytes(n, ld, lim, eb);
     const uint64_t part_bytes = span_bytes(n, ldp, view_tiles, sizeof(logp_partial_t));
     if (grid == 0 || part_bytes == 0 || (lim > 0 && in_bytes == 0)) return LOGP_ERR_SHAPE;
     const Span in[] = {{logits, in_bytes}, {targets, uint64_t(n) * 8},
@@ -766,12 +797,24 @@ logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t n, int64
     if (!guard.ok()) return LOGP_ERR_HIP;
 
     int vt = static_cast<int>(view_tiles), li = static_cast<int>(lim);
-    void* args[] = {&logits, &ld, &n, &vt, &li, &col_begin, &col_end, &vocab_real, &targets,
-                    &active, &ignore_index, &partials, &ldp};
-    const bool vec = aligned16(logits) && (ld % kVec) == 0;
-    const void* k = vec ? reinterpret_cast<const void*>(&partials_kernel<true>)
-                        : reinterpret_cast<const void*>(&partials_kernel<false>);
+    float inv_t = inv_temperature;
+    void* args[] = {&logits, &ld, &n, &vt, &li, &col_begin, &col_end, &vocab_real, &inv_t,
+                    &targets, &active, &ignore_index, &partials, &ldp};
+    const bool vec = vec_ok(logits, ld, eb);
+    const bool scaled = inv_temperature != 1.0f;
+    const void* k = dtype == LOGP_DTYPE_BF16 ? partials_ptr<Dt::BF16>(vec, scaled)
+                    : dtype == LOGP_DTYPE_F16 ? partials_ptr<Dt::F16>(vec, scaled)
+                                              : partials_ptr<Dt::F32>(vec, scaled);
     return launch(k, dim3(grid), dim3(kItemWaves * kWave), args, 0, stream);
+}
+
+logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
+                            int64_t vocab_padded, int64_t col_begin, int64_t col_end,
+                            const int64_t* targets, const uint8_t* active, int64_t ignore_index,
+                            logp_partial_t* partials, int64_t ldp, hipStream_t stream) {
+    return logp_partials_ex(LOGP_DTYPE_BF16, 1.0f, logits, ld, n, vocab_real, vocab_padded,
+                            col_begin, col_end, targets, active, ignore_index, partials, ldp,
+                            stream);
 }
 
 logp_status_t logp_merge(const logp_partial_t* partials, int64_t ldp, int64_t n,

@@ -97,8 +97,18 @@ typedef enum {
                              stream belongs to another device */
     LOGP_ERR_RANGE = 5,   /* an array's extent runs past the end of its allocation */
     LOGP_ERR_OVERLAP = 6, /* an output overlaps an input or another output */
-    LOGP_ERR_HIP = 7      /* the HIP runtime reported an error (query or launch) */
+    LOGP_ERR_HIP = 7,     /* the HIP runtime reported an error (query or launch) */
+    LOGP_ERR_ARG = 8      /* unknown dtype, or inv_temperature not finite and positive */
 } logp_status_t;
+
+/* Element type of logits and dlogits for the _ex entry points (PR #495, Tests: the fused
+ * kernel is checked for FP32, BF16 and FP16 logits).  Values are widened exactly to FP32;
+ * dlogits is rounded to nearest-even in the same type. */
+typedef enum {
+    LOGP_DTYPE_BF16 = 0,
+    LOGP_DTYPE_F16 = 1,
+    LOGP_DTYPE_F32 = 2
+} logp_dtype_t;
 
 /* Forward over whole rows (issue #241 Background; PR #495 Summary).
  *   logits        [n, ld] BF16 bits, row t at logits + t*ld; columns [0, vocab_real) read.
@@ -112,10 +122,11 @@ typedef enum {
  * Results are bitwise equal to logp_partials over any tile-aligned shard split followed by
  * logp_merge.  A row whose real logits are all -inf has LSE -inf, stats (-inf, 0) and
  * logp -inf when valid (0 otherwise). */
-LOGP_API logp_status_t logp_forward(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
-                           int64_t vocab_padded, const int64_t* targets, const uint8_t* active,
-                           int64_t ignore_index, float* logp, float* lse, logp_stats_t* stats,
-                           hipStream_t stream);
+LOGP_API logp_status_t logp_forward(const uint16_t* logits, int64_t ld, int64_t n,
+                                    int64_t vocab_real, int64_t vocab_padded,
+                                    const int64_t* targets, const uint8_t* active,
+                                    int64_t ignore_index, float* logp, float* lse,
+                                    logp_stats_t* stats, hipStream_t stream);
 
 /* Backward (PR #495, Summary item 2: dlogits = g (onehot - softmax) written directly in the
  * logits dtype, no FP32 [N, V] workspace).
@@ -132,11 +143,12 @@ LOGP_API logp_status_t logp_forward(const uint16_t* logits, int64_t ld, int64_t 
  *              its logits are not read.  dlogits may be exactly the logits buffer (same
  *              pointer and ld_out == ld): each element is read before it is overwritten.
  */
-LOGP_API logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
-                            int64_t vocab_padded, int64_t col_begin, int64_t col_end,
-                            const int64_t* targets, const uint8_t* active, int64_t ignore_index,
-                            const float* grad_logp, const logp_stats_t* stats, uint16_t* dlogits,
-                            int64_t ld_out, hipStream_t stream);
+LOGP_API logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n,
+                                     int64_t vocab_real, int64_t vocab_padded, int64_t col_begin,
+                                     int64_t col_end, const int64_t* targets,
+                                     const uint8_t* active, int64_t ignore_index,
+                                     const float* grad_logp, const logp_stats_t* stats,
+                                     uint16_t* dlogits, int64_t ld_out, hipStream_t stream);
 
 /* Vocab-tile partials of one shard (issue #241, "PR6": rank-local (max, sumexp,
  * selected_logit) partials; PR #314 Tensor Parallel doc, steps 1-2).
@@ -148,10 +160,11 @@ LOGP_API logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t
  *              row t's entries start at partials + t*ldp.  Entries j in
  *              [0, ceil((col_end - col_begin) / LOGP_TILE_COLS)) are written.
  * A shard made only of padding yields (-inf, 0, 0) identity entries. */
-LOGP_API logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t n, int64_t vocab_real,
-                            int64_t vocab_padded, int64_t col_begin, int64_t col_end,
-                            const int64_t* targets, const uint8_t* active, int64_t ignore_index,
-                            logp_partial_t* partials, int64_t ldp, hipStream_t stream);
+LOGP_API logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t n,
+                                     int64_t vocab_real, int64_t vocab_padded, int64_t col_begin,
+                                     int64_t col_end, const int64_t* targets,
+                                     const uint8_t* active, int64_t ignore_index,
+                                     logp_partial_t* partials, int64_t ldp, hipStream_t stream);
 
 /* Fixed-order merge of per-tile partials (issue #241, "PR 3"; PR #314 Tensor Parallel
  * doc, steps 4-6).
@@ -162,9 +175,44 @@ LOGP_API logp_status_t logp_partials(const uint16_t* logits, int64_t ld, int64_t
  * Uses the same device code as the merge inside logp_forward, so the outputs are bitwise
  * equal to logp_forward's for the same logits. */
 LOGP_API logp_status_t logp_merge(const logp_partial_t* partials, int64_t ldp, int64_t n,
-                         int64_t num_tiles, int64_t vocab_real, const int64_t* targets,
-                         const uint8_t* active, int64_t ignore_index, float* logp, float* lse,
-                         logp_stats_t* stats, hipStream_t stream);
+                                  int64_t num_tiles, int64_t vocab_real, const int64_t* targets,
+                                  const uint8_t* active, int64_t ignore_index, float* logp,
+                                  float* lse, logp_stats_t* stats, hipStream_t stream);
+
+/* Extended forms: any logits dtype and temperature-scaled scoring.
+ *   dtype            element type of logits (and of dlogits in logp_backward_ex).
+ *   inv_temperature  1/tau, finite and > 0.  The scored logits are z = fl32(x * inv_temperature),
+ *                    one FP32 product per logit, so training and rollout code that use the same
+ *                    inv_temperature see the same z (temperatures 1.0 and 0.7 in the provider
+ *                    experiment of PR #495's author reply).  logp, LSE, stats and partials are
+ *                    those of z; dlogits = inv_temperature * g * (onehot - softmax(z)), with
+ *                    g * inv_temperature rounded once to FP32 per row.  With
+ *                    inv_temperature = 1 the results are bitwise those of the plain entry points.
+ * Every other argument is as in logp_forward / logp_backward / logp_partials; pointers to logits
+ * and dlogits are `void*` of the given dtype, and ld / ld_out count elements.  A view takes the
+ * 16-byte vector path when its start is 16-byte aligned and ld * element size is a multiple of
+ * 16; the results do not depend on which path runs. */
+LOGP_API logp_status_t logp_forward_ex(logp_dtype_t dtype, float inv_temperature,
+                                       const void* logits, int64_t ld, int64_t n,
+                                       int64_t vocab_real, int64_t vocab_padded,
+                                       const int64_t* targets, const uint8_t* active,
+                                       int64_t ignore_index, float* logp, float* lse,
+                                       logp_stats_t* stats, hipStream_t stream);
+LOGP_API logp_status_t logp_backward_ex(logp_dtype_t dtype, float inv_temperature,
+                                        const void* logits, int64_t ld, int64_t n,
+                                        int64_t vocab_real, int64_t vocab_padded,
+                                        int64_t col_begin, int64_t col_end,
+                                        const int64_t* targets, const uint8_t* active,
+                                        int64_t ignore_index, const float* grad_logp,
+                                        const logp_stats_t* stats, void* dlogits, int64_t ld_out,
+                                        hipStream_t stream);
+LOGP_API logp_status_t logp_partials_ex(logp_dtype_t dtype, float inv_temperature,
+                                        const void* logits, int64_t ld, int64_t n,
+                                        int64_t vocab_real, int64_t vocab_padded,
+                                        int64_t col_begin, int64_t col_end,
+                                        const int64_t* targets, const uint8_t* active,
+                                        int64_t ignore_index, logp_partial_t* partials,
+                                        int64_t ldp, hipStream_t stream);
 
 /* ceil(vocab_padded / LOGP_TILE_COLS); 0 when vocab_padded < 1. */
 LOGP_API int64_t logp_num_tiles(int64_t vocab_padded);
@@ -174,9 +222,9 @@ LOGP_API int64_t logp_num_tiles(int64_t vocab_padded);
  * whose target is neither ignore_index nor in [0, vocab_real).  Unlike the other entry
  * points it also launches for n == 0 (writing 0).  Asynchronous: the caller synchronizes
  * the stream before reading the count. */
-LOGP_API logp_status_t logp_check_targets(const int64_t* targets, const uint8_t* active, int64_t n,
-                                 int64_t vocab_real, int64_t ignore_index, int64_t* bad_count,
-                                 hipStream_t stream);
+LOGP_API logp_status_t logp_check_targets(const int64_t* targets, const uint8_t* active,
+                                          int64_t n, int64_t vocab_real, int64_t ignore_index,
+                                          int64_t* bad_count, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 LOGP_API const char* logp_status_string(logp_status_t status);

@@ -4,8 +4,10 @@ Tolerances (written here, used by every GPU parity test):
   * logp and LSE: |gpu - oracle| <= 1e-4 absolute, the bar the accuracy target sets for
     the selected-token logp.  Row max M is compared exactly (a max of BF16 values is
     exact in FP32); S to 2e-5 relative (FP32 sums of up to ~1.5e5 exp terms).
-  * dlogits (BF16): at least 99.99% of all N x vocab_real elements equal the
-    round-to-nearest-even of the FP64 value; the largest |gpu - d64| is at most
+  * dlogits (BF16, and FP16 outputs of FP16 logits): at least 99.99% of all
+    N x vocab_real elements equal the round-to-nearest-even of the FP64 value in the output
+    dtype, up to two elements of slack on small samples (FP32 outputs: every element within
+    16 FP32 spacings instead, the FP32 row sum S carrying a few spacings of shared error); the largest |gpu - d64| is at most
     max(1.5e-3 * max|d64|, 1.01 * E_floor), where E_floor = max|RNE(d64) - d64| is the
     error a perfectly rounded BF16 output already has (the pages show every correct
     implementation sharing that floor: the fused-backward pull request, author reply
@@ -34,12 +36,34 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def bf16_spacing(v: np.ndarray) -> np.ndarray:
-    """Spacing of BF16 numbers in the binade of |v| (2^-133 in the subnormal range)."""
+def host_values(t: torch.Tensor) -> np.ndarray:
+    """A dlogits tensor on the host in the oracle's layout for its dtype (BF16 as bits)."""
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return bits_of(t)
+    return t.cpu().numpy()
+
+
+# significant bits and smallest subnormal spacing of each output dtype
+PRECISION = {"bf16": (8, 2.0 ** -133), "f16": (11, 2.0 ** -24), "f32": (24, 2.0 ** -149)}
+
+
+def spacing(v: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Spacing of representable numbers of `dtype` in the binade of |v|."""
+    bits, smallest = PRECISION[dtype]
     a = np.abs(v)
     _, e = np.frexp(a)  # a = f 2^e, f in [0.5, 1)
-    sp = np.ldexp(np.ones_like(a), e - 8)
-    return np.maximum(sp, 2.0 ** -133)
+    sp = np.ldexp(np.ones_like(a), e - bits)
+    return np.maximum(sp, smallest)
+
+
+def bf16_spacing(v: np.ndarray) -> np.ndarray:
+    """Spacing of BF16 numbers in the binade of |v| (2^-133 in the subnormal range)."""
+    return spacing(v, "bf16")
+
+
+def as_f64(values: np.ndarray, dtype: str) -> np.ndarray:
+    return oracle.bf16_bits_to_f64(values) if dtype == "bf16" else values.astype(np.float64)
 
 
 def valid_rows(targets, active, vocab_real: int, ignore_index: int) -> np.ndarray:
@@ -87,44 +111,53 @@ class BackwardTally:
     notes: list = field(default_factory=list)
 
     def add_block(self, logits_host, targets, grad, vocab_real, vocab_padded, active,
-                  ignore_index, gpu_bits, what: str = ""):
+                  ignore_index, gpu_vals, what: str = "", inv_temperature: float = 1.0,
+                  ulps: float = 1.0):
+        """gpu_vals: dlogits on the host in the oracle's layout (BF16 as uint16 bits)."""
         ref = oracle.backward(logits_host, targets, grad, vocab_real, vocab_padded,
-                              active=active, ignore_index=ignore_index)
-        d64, rb = ref["d64"], ref["bf16"]
-        gpu_bits = np.asarray(gpu_bits, dtype=np.uint16)[:, :vocab_padded]
-        gv = oracle.bf16_bits_to_f64(gpu_bits)
+                              active=active, ignore_index=ignore_index,
+                              inv_temperature=inv_temperature)
+        d64, rb = ref["d64"], ref["rounded"]
+        dt = {np.uint16: "bf16", np.float16: "f16", np.float32: "f32"}[rb.dtype.type]
+        gpu_vals = np.asarray(gpu_vals)[:, :vocab_padded]
+        assert gpu_vals.dtype == rb.dtype, (what, gpu_vals.dtype, rb.dtype)
+        gv = as_f64(gpu_vals, dt)
         assert np.all(np.isfinite(gv)), what
         # padded columns and invalid rows: exactly +0
-        assert np.all(gpu_bits[:, vocab_real:] == 0), what
+        raw = gpu_vals.view(np.uint16 if dt != "f32" else np.uint32)
+        assert np.all(raw[:, vocab_real:] == 0), what
         v = valid_rows(targets, active, vocab_real, ignore_index)
-        assert np.all(gpu_bits[~v] == 0), what
-        real_g, real_r, real_d = gv[:, :vocab_real], rb[:, :vocab_real], d64[:, :vocab_real]
-        same = real_g == oracle.bf16_bits_to_f64(real_r)  # by value: +0 equals -0
+        assert np.all(raw[~v] == 0), what
+        real_g, real_d = gv[:, :vocab_real], d64[:, :vocab_real]
+        real_r = as_f64(rb[:, :vocab_real], dt)
+        same = real_g == real_r  # by value: +0 equals -0
         self.elements += real_g.size
         self.correctly_rounded += int(same.sum())
         err = np.abs(real_g - real_d)
         if err.size:
             self.max_err = max(self.max_err, float(err.max()))
             self.max_ref = max(self.max_ref, float(np.abs(real_d).max()))
-            self.floor = max(self.floor,
-                             float(np.abs(oracle.bf16_bits_to_f64(real_r) - real_d).max()))
-        # one BF16 spacing everywhere; the target element may add 2^-20 |g|
-        allow = bf16_spacing(real_d)
+            self.floor = max(self.floor, float(np.abs(real_r - real_d).max()))
+        # `ulps` spacings of the output dtype everywhere; the target element may add
+        # 2^-20 |g * inv_temperature| (1 - p is formed in FP32)
+        allow = ulps * spacing(real_d, dt)
         y = np.asarray(targets)
-        g = np.abs(np.asarray(grad, dtype=np.float64))
+        g = np.abs(np.asarray(grad, dtype=np.float64)) * float(np.float32(inv_temperature))
         rows = np.nonzero(v)[0]
         allow[rows, y[rows]] += 2.0 ** -20 * g[rows]
         bad = err > allow
         assert not bad.any(), (what, np.argwhere(bad)[:5].tolist(),
                                err[bad][:5].tolist(), allow[bad][:5].tolist())
 
-    def finish(self, what: str = "") -> dict:
+    def finish(self, what: str = "", min_correctly_rounded: float = CORRECTLY_ROUNDED_MIN) -> dict:
         frac = self.correctly_rounded / max(1, self.elements)
         gate = max(MAXERR_RATIO * self.max_ref, 1.01 * self.floor)
         out = {"elements": self.elements, "correctly_rounded": frac,
                "max_err": self.max_err, "max_ref": self.max_ref, "floor": self.floor,
                "max_err_over_max": self.max_err / self.max_ref if self.max_ref else 0.0,
                "floor_over_max": self.floor / self.max_ref if self.max_ref else 0.0}
-        assert frac >= CORRECTLY_ROUNDED_MIN, (what, out)
+        # a slack of two elements keeps the fraction meaningful on small samples
+        misrounded = self.elements - self.correctly_rounded
+        assert misrounded <= (1.0 - min_correctly_rounded) * self.elements + 2, (what, out)
         assert self.max_err <= gate, (what, out)
         return out

@@ -19,7 +19,7 @@ PKG = os.path.join(ROOT, "deterministic_selected_token_amd")
 
 import deterministic_selected_token_amd as dst  # noqa: E402
 
-OK, NULL, SHAPE, SHARD = 0, 1, 2, 3
+OK, NULL, SHAPE, SHARD, ARG = 0, 1, 2, 3, 8
 T = 4096
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails host checks
 
@@ -62,7 +62,7 @@ def test_num_tiles_and_status_strings():
     assert dst.logp_num_tiles(159744) == 39
     assert dst.logp_num_tiles(4096) == 1 and dst.logp_num_tiles(4097) == 2
     assert dst.logp_num_tiles(1) == 1 and dst.logp_num_tiles(0) == 0
-    for code in range(8):
+    for code in range(9):
         s = dst.logp_status_string(code)
         assert s and (code == 0) == (s == "ok")
     assert dst.logp_status_string(99) == "unknown status"
@@ -149,6 +149,37 @@ def test_partials_host_validation(kw, want):
 ])
 def test_merge_host_validation(kw, want):
     assert merge(**kw) == want
+
+
+@pytest.mark.parametrize("dtype,inv_t", [(3, 1.0), (-1, 1.0), (0, 0.0), (1, -2.0),
+                                         (2, float("nan")), (0, float("inf"))])
+def test_ex_entry_points_reject_bad_dtype_or_temperature(dtype, inv_t):
+    lib = dst.library()
+    fa = dict(logits=FAKE, ld=152064, n=4, vocab_real=151936, vocab_padded=152064,
+              targets=FAKE, active=None, ignore_index=-100, logp=FAKE, lse=None, stats=None,
+              stream=None)
+    assert lib.logp_forward_ex(dtype, inv_t, *fa.values()) == ARG
+    ba = dict(logits=FAKE, ld=151936, n=4, vocab_real=151936, vocab_padded=151936,
+              col_begin=0, col_end=151936, targets=FAKE, active=None, ignore_index=-100,
+              grad=FAKE, stats=FAKE, dlogits=FAKE, ld_out=151936, stream=None)
+    assert lib.logp_backward_ex(dtype, inv_t, *ba.values()) == ARG
+    pa = dict(logits=FAKE, ld=159744, n=4, vocab_real=151936, vocab_padded=159744,
+              col_begin=0, col_end=159744, targets=FAKE, active=None, ignore_index=-100,
+              partials=FAKE, ldp=39, stream=None)
+    assert lib.logp_partials_ex(dtype, inv_t, *pa.values()) == ARG
+
+
+def test_ex_entry_points_validate_like_the_plain_ones():
+    lib = dst.library()
+    for dtype in (0, 1, 2):
+        assert lib.logp_forward_ex(dtype, 0.7, FAKE, 152064, -1, 151936, 152064, FAKE, None,
+                                   -100, FAKE, None, None, None) == SHAPE
+        assert lib.logp_forward_ex(dtype, 0.7, None, 152064, 0, 151936, 152064, None, None,
+                                   -100, None, None, None, None) == OK
+        assert lib.logp_backward_ex(dtype, 1.5, FAKE, 100, 4, 100, 100, 50, 40, FAKE, None,
+                                    -100, FAKE, FAKE, FAKE, 100, None) == SHARD
+        assert lib.logp_partials_ex(dtype, 1.0, FAKE, 159744, 4, 151936, 159744, 100, 159744,
+                                    FAKE, None, -100, FAKE, 39, None) == SHARD
 
 
 def test_check_targets_host_validation():
