@@ -299,7 +299,7 @@ def main() -> int:
                    "device": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "torch": torch.__version__, "hip": torch.version.hip, "git": git_sha(),
                    **extra},
-        "roofline": {"bound": "hbm", "kernel": "bwd_kernel (logp_backward)",
+        "roofline": {"bound": "hbm", "kernel": "bwd_flat_kernel (logp_backward)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("bwd"),
                      "algorithmic_bytes_per_launch": bwd_b,

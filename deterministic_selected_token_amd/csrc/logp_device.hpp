@@ -270,23 +270,32 @@ __device__ __forceinline__ float two_sum_err(float a, float b, float s) {
     return (a - (s - bb)) + (b - bb);
 }
 
+// Rounding error of t = fl(z - M) when |z| <= M (Dekker's fast two-sum with the larger
+// operand -M first, 2 operations): z - M = t + err exactly.
+__device__ __forceinline__ float fast_two_sum_err(float z, float M, float t) {
+    return z - (t + M);
+}
+
 // -g/S * exp(z - M) for a tile in which every z - M >= -87 (so every exp is a normal float and
 // the single product rounds correctly even when it lands in the subnormal range).  When z - M
 // is not exact in FP32 (FP32 logits, or scored ones z = fl32(x * inv_t)), TWO_SUM adds its
-// rounding error to delta, so the result is exp of the exact difference.
+// rounding error to delta, so the result is exp of the exact difference; such tiles take
+// this path only when also |z| <= M, which the fast two-sum needs.
 template <bool TWO_SUM>
 __device__ __forceinline__ float bwd_term(float z, float M, float neg_c) {
     const float t = z - M;
     ExpSplit s = bwd_exp_split(t);
-    if (TWO_SUM) s.delta = s.delta + two_sum_err(z, -M, t);
+    if (TWO_SUM) s.delta = s.delta + fast_two_sum_err(z, M, t);
     const float e0 = __builtin_amdgcn_exp2f(s.u);
     return __builtin_fmaf(e0, s.delta, e0) * neg_c;
 }
 
-// Same value for any z - M (including -inf).  Where 2^u would be subnormal (u < -126), where
-// the hardware exp2 returns zero, it is computed as 2^(u+64) (u + 64 is exact there) and
-// multiplied by neg_c_lo = neg_c * 2^-64, which rounds the product exactly as neg_c * e would.
-// For u >= -126 it performs the same operations as bwd_term, so both give identical bits.
+// Same value for any z and M (z - M down to -inf), with the general two-sum.  Where 2^u
+// would be subnormal (u < -126), where the hardware exp2 returns zero, it is computed as
+// 2^(u+64) (u + 64 is exact there) and multiplied by neg_c_lo = neg_c * 2^-64, which rounds
+// the product exactly as neg_c * e would.  For u >= -126 it performs the same operations as
+// bwd_term (both two-sums give the exact error where the fast one applies), so both give
+// identical bits.
 template <bool TWO_SUM>
 __device__ __forceinline__ float bwd_term_deep(float z, float M, float neg_c, float neg_c_lo) {
     const float t = z - M;

@@ -177,16 +177,23 @@ __global__ __launch_bounds__(kMergeWaves* kWave) void merge_kernel(
 // --------------------------------------------------------------------------- backward
 
 // Per-row constants of the backward.
+// z - M is exact for unscaled BF16 / FP16 values (short significands, and M is one of
+// them); otherwise its rounding error is carried into the exponential.
+template <Dt D, bool SCALED>
+__host__ __device__ constexpr bool bwd_two_sum() {
+    return SCALED || D == Dt::F32;
+}
+
 struct BwdRow {
     bool valid;  // row valid and its stats finite
     float M, g, neg_c, neg_c_lo;  // g is the scored upstream gradient g * inv_t
     int64_t y;   // target in view coordinates
-    float thr;   // raw logits below this may need the subnormal-safe path (see below)
+    float thr;   // raw logits below this need the general path (see below)
 };
 
 // The stats and g loads do not wait for the validity test (they are in bounds for every
 // row), so one memory round trip resolves all of them.
-template <bool SCALED>
+template <Dt D, bool SCALED>
 __device__ __forceinline__ BwdRow bwd_row(int64_t row, int64_t col_begin, int64_t vocab_real,
                                           float inv_t, const int64_t* __restrict__ targets,
                                           const uint8_t* __restrict__ active,
@@ -205,6 +212,14 @@ __device__ __forceinline__ BwdRow bwd_row(int64_t row, int64_t col_begin, int64_
     // below (M - 87) / inv_t; the margin of one unit absorbs the roundings of z and of this
     // quotient.  False alarms only select the slower path, which gives the same bits.
     r.thr = SCALED ? (M - 86.0f) / inv_t : M - 87.0f;
+    if (bwd_two_sum<D, SCALED>()) {
+        // The fast two-sum of z - M needs |z| <= M: M >= 0 and z >= -M, which holds for raw
+        // logits at or above -(M / inv_t) (1 - 2^-20); the factor covers the roundings of
+        // the quotient and of z.  M < 0 sends every tile of the row to the general path.
+        const float far = M >= 0.0f ? -(SCALED ? M / inv_t : M) * (1.0f - 0x1p-20f)
+                                    : __builtin_inff();
+        r.thr = fmaxf(r.thr, far);
+    }
     return r;
 }
 
@@ -261,9 +276,7 @@ __device__ __forceinline__ void bwd_vec(const BwdRow& r, const float* v, int c, 
 template <Dt D, bool SCALED>
 __device__ __forceinline__ void bwd_compute_store(const BwdRow& r, const Raw8<D>& raw, bool deep,
                                                   float inv_t, int c, int lim, float* d) {
-    // z - M is exact for unscaled BF16 / FP16 values (short significands); otherwise its
-    // rounding error is carried into the exponential.
-    constexpr bool kTwoSum = SCALED || D == Dt::F32;
+    constexpr bool kTwoSum = bwd_two_sum<D, SCALED>();
     float v[kVec];
     unpack8<D>(raw, v);
 #pragma unroll
@@ -297,8 +310,8 @@ __global__ __launch_bounds__(bwd_tile_waves<D>() * kWave) void bwd_kernel(
         if (first + i >= total) break;
         row[i] = (first + i) / view_tiles;
         start[i] = static_cast<int>(first + i - row[i] * view_tiles) * kTile;
-        r[i] = bwd_row<SCALED>(row[i], col_begin, vocab_real, inv_t, targets, active, ignore_index,
-                               grad, stats);
+        r[i] = bwd_row<D, SCALED>(row[i], col_begin, vocab_real, inv_t, targets, active,
+                                  ignore_index, grad, stats);
     }
     Raw8<D> w[TPW][kLoads];
 #pragma unroll
@@ -356,12 +369,12 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
     const int64_t row_a = q0 / vpr;
     const int64_t sp = (row_a + 1) * vpr - q0;
     const int split = sp < kChunk ? static_cast<int>(sp) : kChunk;  // vectors in row_a
-    const BwdRow ra = bwd_row<SCALED>(row_a, col_begin, vocab_real, inv_t, targets, active,
+    const BwdRow ra = bwd_row<D, SCALED>(row_a, col_begin, vocab_real, inv_t, targets, active,
                                       ignore_index, grad, stats);
     BwdRow rb = ra;
     if (split < kChunk && row_a + 1 < n)
-        rb = bwd_row<SCALED>(row_a + 1, col_begin, vocab_real, inv_t, targets, active,
-                             ignore_index, grad, stats);
+        rb = bwd_row<D, SCALED>(row_a + 1, col_begin, vocab_real, inv_t, targets, active,
+                                ignore_index, grad, stats);
 
     Raw8<D> w[kLoads];
 #pragma unroll

@@ -191,3 +191,20 @@ def test_subnormal_gradients_fp16_and_fp32():
         say(f"{dtype} very spread logits")
         ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, 0.9999)
         check_ex(case, ulps=ulps, min_cr=min_cr)
+
+
+@pytest.mark.parametrize("dtype,inv_t", [("f32", 1.0), ("bf16", 1 / 0.7), ("f16", 0.5),
+                                         ("f32", 2.0)])
+def test_negative_max_and_wide_rows(dtype, inv_t):
+    """Rows whose scored max is negative, and rows where most scored logits lie below -M:
+    there z - M needs the general two-sum (FP32 logits, scaled logits)."""
+    case = case_in(dtype, 16, 20000, sigma=3.0, seed=23)
+    x = case.logits
+    gen = torch.Generator().manual_seed(29)
+    x[0:6, :20000] = (x[0:6, :20000].float() - 40.0).to(x.dtype)
+    x[6:12, :20000] = (torch.rand((6, 20000), generator=gen) * 22.0 - 20.0).to(x.dtype).to(DEV)
+    x[12, :20000] = (torch.rand(20000, generator=gen) * 0.5 - 0.25).to(x.dtype).to(DEV)
+    say(f"negative max / wide rows {dtype} inv_t={inv_t:.3f}")
+    ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, 0.9999)
+    _, fwd, bwd = check_ex(case, inv_t=inv_t, ulps=ulps, min_cr=min_cr)
+    say(f"{dtype} inv_t={inv_t:.3f}: {fwd} {bwd}")
