@@ -14,6 +14,9 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
   merge, rne_bf16, rne_f16, count_bad_targets: pinned.
   Rows whose valid target logit is -inf while other logits are finite, and rows that
   hold NaN or +inf logits: parity unpinned (no closed form was written for them).
+
+``grpo_oracle.py`` (plain numpy, float64) is the oracle of the GRPO loss on these
+log-probabilities; its pins are in ``tests/test_grpo_oracle_pins.py``.
 """
 
 from __future__ import annotations
