@@ -157,6 +157,104 @@ def time_variants(dst, case, stream, steps: int) -> dict:
     return out
 
 
+def time_grpo(dst, case, stream, steps: int) -> dict:
+    """The GRPO rows: (1) one GRPO training step on the headline logits viewed as 32
+    sequences x 1024 tokens -- logp_forward, grpo_loss (seq_mean, KL 0.04, 10% of tokens
+    masked), logp_backward fed with d loss / d logp; (2) grpo_loss alone on 1024 sequences x
+    4096 tokens, against its algorithmic bytes (logp, old_logp, ref_logp 4 B, mask 1 B read
+    once, dlogp 4 B written; 4 B of advantage and 16 B of sums per sequence)."""
+    import torch
+
+    from deterministic_selected_token_amd import grpo
+
+    dev = case.logits.device
+    gen = torch.Generator(device=dev).manual_seed(7)
+
+    def inputs(B, T):
+        noise = lambda: 0.05 * torch.randn((B, T), generator=gen, device=dev)
+        mask = (torch.rand((B, T), generator=gen, device=dev) >= 0.1).to(torch.uint8)
+        adv = grpo.grpo_advantages(torch.randn(B, generator=gen, device=dev), 8)
+        return noise, mask, adv
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in evs:
+            fn(e)
+        torch.cuda.synchronize()
+        a = sum(x.elapsed_time(y) for x, y, _ in evs) / steps
+        b = sum(y.elapsed_time(z) for _, y, z in evs) / steps
+        return a, b
+
+    out = {}
+    n, v = case.n, case.vocab_real
+    B, T = 32, n // 32
+    x, y = case.logits, case.targets
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse, stats = torch.empty_like(logp), torch.empty((n, 2), dtype=torch.float32, device=dev)
+    d = torch.empty((n, v), dtype=torch.bfloat16, device=dev)
+    dst.logp_forward(x, y, logp=logp, lse=lse, stats=stats, stream=stream)
+    noise, mask, adv = inputs(B, T)
+    old = (logp.view(B, T) + noise()).contiguous()
+    ref = (logp.view(B, T) + noise()).contiguous()
+    seq_stats = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    loss = torch.empty(6, dtype=torch.int64, device=dev)
+    dlogp = torch.empty((B, T), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        dst.logp_forward(x, y, logp=logp, lse=lse, stats=stats, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        grpo.grpo_loss(logp.view(B, T), old, adv, ref_logp=ref, mask=mask, mode="seq_mean",
+                       beta=0.04, seq_stats=seq_stats, loss=loss, dlogp=dlogp, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dst.logp_backward(x, y, dlogp.view(-1), stats, dlogits=d, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    for e in evs:
+        e[3].record(stream)
+        step(e)
+    torch.cuda.synchronize()
+    total = sum(e[3].elapsed_time(e[2]) for e in evs) / steps
+    loss_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    out["grpo_step_headline"] = {"sequences": B, "tokens_per_sequence": T,
+                                 "ms_per_step": round(total, 4), "grpo_loss_ms": round(loss_ms, 4),
+                                 "loss": grpo.loss_fields(loss)["loss"]}
+    del d
+    torch.cuda.empty_cache()
+
+    B, T = 1024, 4096
+    noise, mask, adv = inputs(B, T)
+    lp = -1.0 - torch.rand((B, T), generator=gen, device=dev)
+    old, ref = lp + noise(), lp + noise()
+    seq_stats = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    dlogp = torch.empty((B, T), dtype=torch.float32, device=dev)
+
+    def loss_only(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        grpo.grpo_loss(lp, old, adv, ref_logp=ref, mask=mask, mode="token_mean", beta=0.04,
+                       seq_stats=seq_stats, loss=loss, dlogp=dlogp, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+            ev[2].record(stream)
+
+    ms, _ = timed(loss_only)
+    nbytes = B * T * (4 * 3 + 1 + 4) + B * (4 + 16) + 48
+    out["grpo_loss_1024x4096"] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes,
+                                  "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                  "launches": 4}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,7 +266,8 @@ def main() -> int:
                     help="also time logp_partials (4 shards) + logp_merge")
     ap.add_argument("--variants", action="store_true",
                     help="also time FP16 and FP32 logits and BF16 at temperature 0.7 on the "
-                         "same shape (reported under config.variants)")
+                         "same shape, a GRPO step and the GRPO loss alone (reported under "
+                         "config.variants)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="run a 4 GiB device copy after the timed region (counter scaling)")
     args = ap.parse_args()
@@ -262,6 +361,7 @@ def main() -> int:
                                "merge_ms": round(e[1].elapsed_time(e[2]), 4)}
     if args.variants:
         extra["variants"] = time_variants(dst, case, stream, args.steps)
+        extra["variants"].update(time_grpo(dst, case, stream, args.steps))
     if args.profile_copy:
         src = torch.empty(1 << 31, dtype=torch.int16, device=dev)  # 4 GiB
         dst_buf = torch.empty_like(src)

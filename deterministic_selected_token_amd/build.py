@@ -13,8 +13,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblogp_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "logp_kernels.hip")]
-HEADERS = [os.path.join(CSRC, "logp_device.hpp"), os.path.join(INCLUDE, "logp.h")]
+SOURCES = [os.path.join(CSRC, "logp_kernels.hip"), os.path.join(CSRC, "grpo_kernels.hip")]
+HEADERS = [os.path.join(CSRC, "logp_device.hpp"), os.path.join(CSRC, "host_common.hpp"),
+           os.path.join(INCLUDE, "logp.h"), os.path.join(INCLUDE, "grpo_loss.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -222,6 +222,12 @@ __device__ __forceinline__ void store8(typename DtInfo<D>::Storage* out, int c, 
 
 // ------------------------------------------------------------------ lane tree
 
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+
+
 // Pairwise tree over lanes 0..63 in index order: partners at xor 1, 2, 4, 8, 16, 32.
 // After each step both partners hold the same value (max and + are commutative), so every
 // lane ends with identical bits.

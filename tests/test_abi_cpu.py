@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every function that
-include/logp.h declares, and rejects bad arguments on the host before any HIP call."""
+include/*.h declares, and rejects bad arguments on the host before any HIP call."""
 
 from __future__ import annotations
 
@@ -15,9 +15,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "logp.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADERS = [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h")]
 PKG = os.path.join(ROOT, "deterministic_selected_token_amd")
 
 import deterministic_selected_token_amd as dst  # noqa: E402
+from deterministic_selected_token_amd import grpo  # noqa: E402
 
 OK, NULL, SHAPE, SHARD, ARG = 0, 1, 2, 3, 8
 T = 4096
@@ -25,20 +28,24 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails hos
 
 
 def declared_functions() -> list[str]:
-    text = open(HEADER).read()
-    return re.findall(r"^LOGP_API\s+[\w\s\*]+?\b(logp_\w+)\s*\(", text, flags=re.M)
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        names += re.findall(r"^LOGP_API\s+[\w\s\*]+?\b((?:logp|grpo)_\w+)\s*\(", text,
+                            flags=re.M)
+    return names
 
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert sorted(names) == sorted(dst.EXPORTED)
+    assert sorted(names) == sorted(dst.EXPORTED + grpo.EXPORTED)
     lib = ctypes.CDLL(dst.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", dst.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT\s+(logp_\w+)$", out, flags=re.M))
-    assert exported == set(names)  # nothing else with the prefix leaks out
+    exported = set(re.findall(r"\bT\s+((?:logp|grpo)_\w+)$", out, flags=re.M))
+    assert exported == set(names)  # nothing else with the prefixes leaks out
 
 
 def test_header_constants_match_binding():
@@ -206,9 +213,9 @@ def test_product_path_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
-                assert "logp_oracle" not in text, f
-    text = open(HEADER).read()
-    assert "oracle" not in text.lower()
+                assert "logp_oracle" not in text and "grpo_oracle" not in text, f
+    for h in HEADERS:
+        assert "oracle" not in open(h).read().lower(), h
 
 
 def test_import_fails_loudly_without_the_library():
