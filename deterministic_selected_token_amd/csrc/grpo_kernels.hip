@@ -6,7 +6,8 @@
 // summation order over tokens, then sequences, then ranks, merged in fixed order instead of
 // by a collective sum.
 //
-//   seq kernel      one workgroup per sequence: its waves take the sequence's 256-token tiles
+//   seq kernel      one workgroup per sequence (one wave per tile, up to 16): its waves take
+//                   the sequence's 256-token tiles
 //                   round-robin, compute every token's terms and gradient in registers,
 //                   reduce each tile with the lane tree, park the tile sums in LDS; wave 0
 //                   merges them in the fixed order.  One pass over the per-token inputs.
@@ -15,11 +16,12 @@
 //   merge kernel    one wave per sequence over its tile partials: the same merge code.
 //   count / norm    active tokens per sequence, then the batch normalizer (only needed when a
 //                   mask makes them unknown on the host).
-//   reduce kernel   one wave over the batch's sequences: the same merge order again.
+//   reduce kernel   one workgroup over the batch's sequences: the same merge order again.
 //   advantages      one wave per reward group.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "grpo_loss.h"
@@ -33,7 +35,7 @@ namespace {
 
 constexpr int kTokTile = GRPO_TOKEN_TILE;       // tokens per tile
 constexpr int kTokPerLane = kTokTile / kWave;  // 4
-constexpr int kSeqWaves = 4;                    // waves per sequence workgroup
+constexpr int kSeqMaxWaves = 16;                // most waves per sequence workgroup
 constexpr int kMaxTokTiles = GRPO_MAX_SEQ_LEN / kTokTile;
 constexpr int kItemWaves = 4;                   // waves per workgroup of per-wave kernels
 constexpr int kCountThreads = 256;
@@ -133,17 +135,29 @@ __device__ __forceinline__ grpo_partial_t grpo_tile(const Tokens& tk, const Obje
 }
 
 // Fixed-order merge of items [0, count) read through src(i): lane l adds items l, l+64, ...
-// in order from +0, then the lane tree.  Every lane returns the same sums.
+// in order from +0, then the lane tree.  Every lane returns the same sums.  Items are
+// fetched kMergeBatch at a time ahead of the additions, which keep their order.
+constexpr int kMergeBatch = 8;
+
 template <class Src>
 __device__ __forceinline__ grpo_partial_t grpo_merge(const Src& src, int64_t count, int lane) {
     float pg = 0.0f, kl = 0.0f;
     int clipped = 0, tokens = 0;
-    for (int64_t i = lane; i < count; i += kWave) {
-        const grpo_partial_t p = src(i);
-        pg = pg + p.pg_sum;
-        kl = kl + p.kl_sum;
-        clipped += p.clipped;
-        tokens += p.tokens;
+    for (int64_t i0 = lane; i0 < count; i0 += int64_t(kWave) * kMergeBatch) {
+        grpo_partial_t p[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const int64_t i = i0 + int64_t(j) * kWave;
+            if (i < count) p[j] = src(i);
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            if (i0 + int64_t(j) * kWave >= count) break;
+            pg = pg + p[j].pg_sum;
+            kl = kl + p[j].kl_sum;
+            clipped += p[j].clipped;
+            tokens += p[j].tokens;
+        }
     }
     grpo_partial_t s;
     s.pg_sum = wave_sum(pg);
@@ -188,18 +202,19 @@ struct RowPartials {
 // One workgroup per sequence.  `counts` (stride 4 ints = one grpo_partial_t) holds n_i when
 // `counted`; otherwise every sequence has tk.width active tokens.  The normalizer D is
 // `norm_dev[0]` when given (computed on the device from the counts), else `norm_host`.
-__global__ __launch_bounds__(kSeqWaves* kWave) void grpo_seq_kernel(
+__global__ __launch_bounds__(kSeqMaxWaves* kWave) void grpo_seq_kernel(
     Tokens tk, Objective o, const int64_t* norm_dev, int64_t norm_host,
     grpo_partial_t* __restrict__ seq_stats, float* dlogp) {
     extern __shared__ grpo_partial_t slots[];  // one slot per tile of the sequence
     const int64_t row = blockIdx.x;
     const int lane = lane_id(), wave = wave_id();
+    const int waves = static_cast<int>(blockDim.x) / kWave;
     const float A = tk.adv[row];
     const int64_t n_i = norm_dev != nullptr ? seq_stats[row].tokens : tk.width;
     const int64_t D = norm_dev != nullptr ? norm_dev[0] : norm_host;
     const float scale = grpo_scale(o.mode, n_i, D);
     const int tiles = (tk.width + kTokTile - 1) / kTokTile;
-    for (int t = wave; t < tiles; t += kSeqWaves) {
+    for (int t = wave; t < tiles; t += waves) {
         const grpo_partial_t s = grpo_tile(tk, o, row, t * kTokTile, A, scale, dlogp, tk.ld, lane);
         if (lane == 0) slots[t] = s;
     }
@@ -237,7 +252,15 @@ __global__ __launch_bounds__(kItemWaves* kWave) void grpo_merge_kernel(
     if (lane_id() == 0) seq_stats[row] = s;
 }
 
-// Active tokens of view row blockIdx.x, written to counts[row * stride].
+// Nonzero bytes of a 32-bit word: bit 7 of each byte of y is set iff that byte of x is not 0.
+__device__ __forceinline__ int nonzero_bytes(uint32_t x) {
+    const uint32_t y = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+    return __popc(y);
+}
+
+// Active tokens of view row blockIdx.x, written to counts[row * stride].  VEC: the row starts
+// are 16-byte aligned and the mask is read 16 bytes at a time.
+template <bool VEC>
 __global__ __launch_bounds__(kCountThreads) void grpo_count_kernel(
     const uint8_t* __restrict__ mask, int64_t ld, int width, int32_t* counts, int64_t stride) {
     __shared__ int wave_counts[kCountThreads / kWave];
@@ -246,7 +269,18 @@ __global__ __launch_bounds__(kCountThreads) void grpo_count_kernel(
     if (mask == nullptr) {
         c = threadIdx.x == 0 ? width : 0;
     } else {
-        for (int t = threadIdx.x; t < width; t += kCountThreads) c += mask[row * ld + t] != 0;
+        const uint8_t* m = mask + row * ld;
+        int t0 = 0;
+        if (VEC) {
+            const int nv = width / 16;
+            for (int q = threadIdx.x; q < nv; q += kCountThreads) {
+                const uint4 v = reinterpret_cast<const uint4*>(m)[q];
+                c += nonzero_bytes(v.x) + nonzero_bytes(v.y) + nonzero_bytes(v.z) +
+                     nonzero_bytes(v.w);
+            }
+            t0 = nv * 16;
+        }
+        for (int t = t0 + threadIdx.x; t < width; t += kCountThreads) c += m[t] != 0;
     }
     c = wave_isum(c);
     if (lane_id() == 0) wave_counts[wave_id()] = c;
@@ -258,14 +292,20 @@ __global__ __launch_bounds__(kCountThreads) void grpo_count_kernel(
     }
 }
 
+const void* count_kernel(const uint8_t* mask, int64_t ld) {
+    const bool vec = mask != nullptr && aligned16(mask) && ld % 16 == 0;
+    return vec ? reinterpret_cast<const void*>(&grpo_count_kernel<true>)
+               : reinterpret_cast<const void*>(&grpo_count_kernel<false>);
+}
+
 // Batch counts and the normalizer from seq_stats[].tokens, into loss->tokens / sequences /
-// norm.  One wave.
-__global__ __launch_bounds__(kWave) void grpo_norm_kernel(
+// norm.  One workgroup; integer sums, so any order gives the same result.
+__global__ __launch_bounds__(kCountThreads) void grpo_norm_kernel(
     const grpo_partial_t* __restrict__ seq_stats, int64_t n_seqs, int32_t mode,
     int64_t norm_tokens, int64_t norm_seqs, grpo_loss_t* loss) {
-    const int lane = lane_id();
+    __shared__ long long part[2][kCountThreads / kWave];
     long long tokens = 0, nonempty = 0;
-    for (int64_t i = lane; i < n_seqs; i += kWave) {
+    for (int64_t i = threadIdx.x; i < n_seqs; i += kCountThreads) {
         const int32_t n = seq_stats[i].tokens;
         tokens += n;
         nonempty += n > 0 ? 1 : 0;
@@ -275,7 +315,17 @@ __global__ __launch_bounds__(kWave) void grpo_norm_kernel(
         tokens += __shfl_xor(tokens, o, kWave);
         nonempty += __shfl_xor(nonempty, o, kWave);
     }
-    if (lane == 0) {
+    if (lane_id() == 0) {
+        part[0][wave_id()] = tokens;
+        part[1][wave_id()] = nonempty;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        tokens = nonempty = 0;
+        for (int w = 0; w < kCountThreads / kWave; ++w) {
+            tokens += part[0][w];
+            nonempty += part[1][w];
+        }
         loss->tokens = tokens;
         loss->sequences = nonempty;
         loss->norm = grpo_norm(mode, norm_tokens, norm_seqs, tokens, nonempty);
@@ -297,14 +347,15 @@ struct SeqContribution {
     }
 };
 
-// The loss from per-sequence sums, in the fixed order.  One wave.
-__global__ __launch_bounds__(kWave) void grpo_reduce_kernel(
+// The loss from per-sequence sums: wave 0 merges the float sums in the fixed order while
+// every wave adds up the integer counts (order-free).
+__global__ __launch_bounds__(kCountThreads) void grpo_reduce_kernel(
     const grpo_partial_t* __restrict__ seq_stats, int64_t n_seqs, int32_t mode, float beta,
     int64_t norm_tokens, int64_t norm_seqs, grpo_loss_t* loss) {
-    const int lane = lane_id();
-    const grpo_partial_t s = grpo_merge(SeqContribution{seq_stats, mode}, n_seqs, lane);
+    __shared__ long long part[3][kCountThreads / kWave];
+    const int lane = lane_id(), wave = wave_id();
     long long tokens = 0, nonempty = 0, clipped = 0;
-    for (int64_t i = lane; i < n_seqs; i += kWave) {
+    for (int64_t i = threadIdx.x; i < n_seqs; i += kCountThreads) {
         const grpo_partial_t p = seq_stats[i];
         tokens += p.tokens;
         nonempty += p.tokens > 0 ? 1 : 0;
@@ -317,6 +368,20 @@ __global__ __launch_bounds__(kWave) void grpo_reduce_kernel(
         clipped += __shfl_xor(clipped, o, kWave);
     }
     if (lane == 0) {
+        part[0][wave] = tokens;
+        part[1][wave] = nonempty;
+        part[2][wave] = clipped;
+    }
+    grpo_partial_t s{};
+    if (wave == 0) s = grpo_merge(SeqContribution{seq_stats, mode}, n_seqs, lane);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        tokens = nonempty = clipped = 0;
+        for (int w = 0; w < kCountThreads / kWave; ++w) {
+            tokens += part[0][w];
+            nonempty += part[1][w];
+            clipped += part[2][w];
+        }
         const int64_t D = grpo_norm(mode, norm_tokens, norm_seqs, tokens, nonempty);
         const double d = static_cast<double>(D);
         const float pg = D > 0 ? static_cast<float>(static_cast<double>(s.pg_sum) / d) : 0.0f;
@@ -450,8 +515,8 @@ logp_status_t grpo_token_counts(const uint8_t* mask, int64_t n_seqs, int64_t seq
     if (!guard.ok()) return LOGP_ERR_DEVICE;
     int64_t stride = 1;
     void* args[] = {&m, &ld, &width, &counts, &stride};
-    return launch(reinterpret_cast<const void*>(&grpo_count_kernel),
-                  dim3(static_cast<uint32_t>(n_seqs)), dim3(kCountThreads), args, 0, stream);
+    return launch(count_kernel(m, ld), dim3(static_cast<uint32_t>(n_seqs)), dim3(kCountThreads),
+                  args, 0, stream);
 }
 
 logp_status_t grpo_loss(const float* logp, const float* old_logp, const float* ref_logp,
@@ -492,27 +557,29 @@ logp_status_t grpo_loss(const float* logp, const float* old_logp, const float* r
             int32_t* counts = &seq_stats[0].tokens;
             int64_t stride = sizeof(grpo_partial_t) / sizeof(int32_t);
             void* ca[] = {&m, &ld, &width, &counts, &stride};
-            st = launch(reinterpret_cast<const void*>(&grpo_count_kernel),
-                        dim3(static_cast<uint32_t>(n_seqs)), dim3(kCountThreads), ca, 0, stream);
+            st = launch(count_kernel(m, ld), dim3(static_cast<uint32_t>(n_seqs)),
+                        dim3(kCountThreads), ca, 0, stream);
             if (st != LOGP_OK) return st;
             void* na[] = {&seq_stats, &n_seqs, &mode, &nt, &ns, &loss};
-            st = launch(reinterpret_cast<const void*>(&grpo_norm_kernel), dim3(1), dim3(kWave),
-                        na, 0, stream);
+            st = launch(reinterpret_cast<const void*>(&grpo_norm_kernel), dim3(1),
+                        dim3(kCountThreads), na, 0, stream);
             if (st != LOGP_OK) return st;
             norm_dev = &loss->norm;
         } else {
             norm_host = grpo_norm(mode, nt, ns, n_seqs * seq_len, seq_len > 0 ? n_seqs : 0);
         }
         void* sa[] = {&tk, &o, &norm_dev, &norm_host, &seq_stats, &dlogp};
-        const size_t lds =
-            static_cast<size_t>(ceil_div(seq_len, kTokTile)) * sizeof(grpo_partial_t);
+        const int64_t tiles = ceil_div(seq_len, kTokTile);
+        const size_t lds = static_cast<size_t>(tiles) * sizeof(grpo_partial_t);
+        const int waves = static_cast<int>(std::min<int64_t>(kSeqMaxWaves, std::max<int64_t>(1,
+                                                                                     tiles)));
         st = launch(reinterpret_cast<const void*>(&grpo_seq_kernel),
-                    dim3(static_cast<uint32_t>(n_seqs)), dim3(kSeqWaves * kWave), sa, lds, stream);
+                    dim3(static_cast<uint32_t>(n_seqs)), dim3(waves * kWave), sa, lds, stream);
         if (st != LOGP_OK) return st;
     }
     void* ra[] = {&seq_stats, &n_seqs, &mode, &beta, &nt, &ns, &loss};
-    return launch(reinterpret_cast<const void*>(&grpo_reduce_kernel), dim3(1), dim3(kWave), ra, 0,
-                  stream);
+    return launch(reinterpret_cast<const void*>(&grpo_reduce_kernel), dim3(1),
+                  dim3(kCountThreads), ra, 0, stream);
 }
 
 logp_status_t grpo_loss_partials(const float* logp, const float* old_logp, const float* ref_logp,
@@ -606,8 +673,8 @@ logp_status_t grpo_loss_reduce(const grpo_partial_t* seq_stats, int64_t n_seqs,
     float beta = params->beta;
     int64_t nt = params->norm_tokens, ns = params->norm_seqs;
     void* args[] = {&seq_stats, &n_seqs, &mode, &beta, &nt, &ns, &loss};
-    return launch(reinterpret_cast<const void*>(&grpo_reduce_kernel), dim3(1), dim3(kWave), args,
-                  0, stream);
+    return launch(reinterpret_cast<const void*>(&grpo_reduce_kernel), dim3(1),
+                  dim3(kCountThreads), args, 0, stream);
 }
 
 }  // extern "C"
