@@ -115,7 +115,7 @@ def default_threads() -> int:
 
 # ------------------------------------------------------------------ marshalling
 
-DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
+DTYPES = {"bf16": 0, "f16": 1, "f32": 2, "f64": 3}  # f64: forward and partials only
 
 
 def _logits(logits):
@@ -130,6 +130,8 @@ def _logits(logits):
                 return t.numpy(), "f16"
             if t.dtype == torch.float32:
                 return t.numpy(), "f32"
+            if t.dtype == torch.float64:
+                return t.numpy(), "f64"
             raise TypeError(f"oracle: unsupported logits dtype {t.dtype}")
     except ImportError:  # pragma: no cover
         pass
@@ -140,7 +142,9 @@ def _logits(logits):
         return a, "f16"
     if a.dtype == np.float32:
         return a, "f32"
-    raise TypeError("oracle expects BF16 bits (uint16), float16 or float32 logits")
+    if a.dtype == np.float64:
+        return a, "f64"
+    raise TypeError("oracle expects BF16 bits (uint16), float16, float32 or float64 logits")
 
 
 def _bits(logits) -> np.ndarray:

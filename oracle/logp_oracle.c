@@ -70,10 +70,13 @@ static double f16_bits_to_double(uint16_t h) {
     return sign ? -v : v;
 }
 
-enum { DT_BF16 = 0, DT_F16 = 1, DT_F32 = 2 };
+enum { DT_BF16 = 0, DT_F16 = 1, DT_F32 = 2, DT_F64 = 3 };
 
-/* Logit number `index` of a buffer of the given dtype, scaled: fl32(x * inv_temperature). */
+/* Logit number `index` of a buffer of the given dtype, scaled: fl32(x * inv_temperature).
+ * FP64 logits (exact logits of a linear layer, computed in double) are used as they are,
+ * times inv_temperature in double. */
 static double logit_at(const void* logits, int dtype, int64_t index, float inv_temperature) {
+    if (dtype == DT_F64) return ((const double*)logits)[index] * (double)inv_temperature;
     float x;
     if (dtype == DT_BF16)
         x = (float)bf16_bits_to_double(((const uint16_t*)logits)[index]);
@@ -259,7 +262,7 @@ ORACLE_API int oracle_forward_ex(int dtype, float inv_temperature, const void* l
                                  int64_t n, int64_t vocab_real, const int64_t* targets,
                                  const uint8_t* active, int64_t ignore_index, double* logp,
                                  double* lse, double* row_max, double* row_sumexp, int nthreads) {
-    if (n < 0 || vocab_real < 1 || ld < vocab_real || dtype < 0 || dtype > 2) return 1;
+    if (n < 0 || vocab_real < 1 || ld < vocab_real || dtype < 0 || dtype > 3) return 1;
     if (n > 0 && (logits == NULL || targets == NULL)) return 1;
     fwd_ctx c = {logits, dtype, inv_temperature, ld, vocab_real, targets, active, ignore_index,
                  logp, lse, row_max, row_sumexp};
@@ -404,7 +407,7 @@ ORACLE_API int oracle_tile_partials_ex(int dtype, float inv_temperature, const v
                                        int nthreads) {
     if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real || ld < vocab_real || tile < 1)
         return 1;
-    if (dtype < 0 || dtype > 2) return 1;
+    if (dtype < 0 || dtype > 3) return 1;
     if (n > 0 && (logits == NULL || targets == NULL || !m || !s || !sel)) return 1;
     part_ctx c = {logits, dtype, inv_temperature, ld, vocab_real, vocab_padded, tile,
                   (vocab_padded + tile - 1) / tile, targets, active, ignore_index, m, s, sel};

@@ -1,0 +1,142 @@
+"""Pins of the FP64 linear_logp oracle (CPU only).
+
+Each pin checks it against something other than itself: one-hot hidden states, which turn
+h W^T into columns of W and so reduce linear_logp to the (separately pinned) logp oracle on
+BF16 logits; an exactness case that a float32 accumulation would get wrong; torch float64
+log_softmax of h W^T; uniform rows; padded vocabulary rows that must not count; and
+linearity in h.  Planted mistakes (altered copies of the oracle source) must each fail one.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "linear_oracle.py")
+
+
+def load(src: str = None):
+    src = open(SRC).read() if src is None else src
+    mod = types.ModuleType("oracle.linear_oracle_copy")
+    mod.__package__ = "oracle"
+    exec(compile(src, SRC, "exec"), mod.__dict__)
+    return mod
+
+
+def bf16(x) -> torch.Tensor:
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def rand_bf16(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
+
+
+def pin_one_hot_rows(o):
+    """h[t] = c_t e_{k_t}: logits[t, v] = c_t W[v, k_t] exactly, so linear_logp equals the
+    logp oracle on the BF16 logits c_t W[:, k_t] (c_t powers of two keep them BF16)."""
+    n, H, V = 6, 40, 300
+    W = rand_bf16((V, H), 1, 2.0)
+    ks = [0, 7, 39, 12, 12, 25]
+    cs = [1.0, 2.0, 0.5, -1.0, 4.0, 1.0]
+    h = torch.zeros((n, H), dtype=torch.bfloat16)
+    for t, (k, c) in enumerate(zip(ks, cs)):
+        h[t, k] = c
+    y = np.array([3, 0, 299, 150, 7, 42])
+    got = o.forward(h, W, y, V)
+    z = torch.stack([W[:, k].float() * c for k, c in zip(ks, cs)]).to(torch.bfloat16)
+    want = oracle.forward(z, y, V)
+    assert np.array_equal(got["logits"], z.double().numpy())
+    for key in ("logp", "lse", "max", "sumexp"):
+        assert np.array_equal(got[key], want[key]), key
+
+
+def pin_exact_accumulation(o):
+    """2^10 * 1 + 1 * 2^-20 + (-2^10) * 1 = 2^-20 exactly; a float32 running sum loses the
+    small term (2^10 + 2^-20 needs 31 significand bits)."""
+    h = bf16([[1024.0, 1.0, -1024.0]])
+    W = bf16([[1.0, 2.0 ** -20, 1.0], [0.0, 0.0, 0.0]])
+    z = o.logits(h, W)
+    assert z[0, 0] == 2.0 ** -20 and z[0, 1] == 0.0
+    assert np.all(o.logit_abs(h, W)[0] == [2048.0 + 2.0 ** -20, 0.0])
+
+
+def pin_torch_log_softmax(o):
+    n, H, V = 9, 64, 517
+    h = rand_bf16((n, H), 2)
+    W = rand_bf16((V, H), 3, 0.3)
+    y = np.array([0, 5, 516, 100, 200, 300, 400, 1, 2])
+    got = o.forward(h, W, y, V)
+    z = h.double() @ W.double().T
+    ls = torch.log_softmax(z, dim=1)
+    np.testing.assert_allclose(got["logp"], ls[np.arange(n), y].numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["lse"], torch.logsumexp(z, 1).numpy(), rtol=0, atol=1e-12)
+
+
+def pin_uniform_and_padding(o):
+    """Equal rows of W give -log V; rows at or beyond vocab_real never count, even huge ones."""
+    V, Vp, H = 1000, 1024, 16
+    W = torch.zeros((Vp, H), dtype=torch.bfloat16)
+    W[:V] = bf16(np.full((V, H), 0.25))
+    W[V:] = 100.0
+    h = rand_bf16((3, H), 4)
+    got = o.forward(h, W, np.array([0, 999, 500]), V)
+    assert np.allclose(got["logp"], -math.log(V), rtol=0, atol=1e-13)
+    p = o.tile_partials(h, W, np.array([0, 999, 500]), V, Vp, tile=256)
+    assert np.all(np.isfinite(p["max"][:, :3])) and p["max"].shape == (3, 4)
+    assert np.all(p["max"][:, 3] == got["max"])  # the last tile holds 232 real columns
+
+
+def pin_linearity_and_orientation(o):
+    """z(h1 + h2) = z(h1) + z(h2) (exact here: small integers), and z[t, v] pairs hidden row t
+    with vocabulary row v on a non-square shape."""
+    h1 = bf16(np.arange(12).reshape(3, 4) % 5 - 2)
+    h2 = bf16(np.arange(12).reshape(3, 4) % 3)
+    W = bf16(np.arange(20).reshape(5, 4) % 7 - 3)
+    z = o.logits(h1, W)
+    assert z.shape == (3, 5)
+    assert np.array_equal(o.logits(bf16(h1.float() + h2.float()), W), z + o.logits(h2, W))
+    assert z[2, 4] == sum(float(h1[2, k]) * float(W[4, k]) for k in range(4))
+
+
+PINS = [pin_one_hot_rows, pin_exact_accumulation, pin_torch_log_softmax,
+        pin_uniform_and_padding, pin_linearity_and_orientation]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_linear_oracle_pin(pin):
+    pin(load())
+
+
+MUTATIONS = [
+    ("float32 accumulation", "    return h @ w[:v].T\n",
+     "    return (h.astype(np.float32) @ w[:v].T.astype(np.float32)).astype(np.float64)\n"),
+    ("weight used untransposed", "    return h @ w[:v].T\n", "    return h @ w[:v, :v]\n"),
+    ("vocabulary order reversed", "    return h @ w[:v].T\n", "    return h @ w[:v][::-1].T\n"),
+    ("bf16 decoded with the wrong shift",
+     "(a.astype(np.uint32) << 16).view(np.float32)",
+     "(a.astype(np.uint32) << 15).view(np.float32)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new):
+    src = open(SRC).read()
+    assert old in src, name
+    bad = load(src.replace(old, new, 1))
+    failed = 0
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(bad)
+        except Exception:
+            failed += 1
+    assert failed >= 1, f"no pin catches: {name}"
