@@ -13,9 +13,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblogp_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "logp_kernels.hip"), os.path.join(CSRC, "grpo_kernels.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("logp_kernels.hip", "grpo_kernels.hip",
+                                            "linear_kernels.hip")]
 HEADERS = [os.path.join(CSRC, "logp_device.hpp"), os.path.join(CSRC, "host_common.hpp"),
-           os.path.join(INCLUDE, "logp.h"), os.path.join(INCLUDE, "grpo_loss.h")]
+           os.path.join(INCLUDE, "logp.h"), os.path.join(INCLUDE, "grpo_loss.h"),
+           os.path.join(INCLUDE, "linear_logp.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -1,0 +1,319 @@
+// gfx950 kernel and C entry point of the fused LM-head + selected-token log-probability
+// (include/linear_logp.h).
+//
+// One workgroup per (block of 128 rows, global vocab tile of 4096 columns).  It walks the
+// tile in 32 sub-blocks of 128 columns; for each it forms the 128 x 128 logits block on the
+// matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension, the
+// hidden states and weight rows staged through double-buffered LDS with the next stage's
+// global loads in flight), reduces the block to a per-row (max, sum-exp) in registers with
+// a fixed lane tree, and folds it into the row's running tile state in LDS.  After the last
+// sub-block the tile's (m, s, sel) partial is written in logp.h's layout, and logp_merge
+// completes the forward.  The logits never leave the chip.
+//
+// Sources: PR #495 (Summary) names the fused LM-head + logp op; issue #241 ("PR 3", "PR6")
+// and PR #314 (Tensor Parallel doc) fix the per-tile partials and their merge.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "host_common.hpp"
+#include "linear_logp.h"
+#include "logp_device.hpp"
+
+using namespace logp;
+using namespace logp_host;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kWM = 2, kWN = 2;               // waves along rows / columns
+constexpr int kTM = 2, kTN = 2;               // 32 x 32 MFMA tiles per wave along rows / cols
+constexpr int kThreads = kWM * kWN * kWave;   // 256
+constexpr int kBM = kWM * kTM * 32;           // rows per workgroup
+constexpr int kBN = kWN * kTN * 32;           // columns per sub-block
+constexpr int kBK = 32;                       // hidden elements per LDS stage
+constexpr int kRow = kBK + 8;                 // LDS row stride in elements (80 bytes)
+constexpr int kSubBlocks = kTile / kBN;       // sub-blocks per vocab tile
+constexpr int kChunksA = kBM * kBK / 8 / kThreads;  // 16-byte chunks per thread per stage
+constexpr int kChunksB = kBN * kBK / 8 / kThreads;
+constexpr int kChunksPerRow = kBK / 8;
+
+static_assert(kChunksA * kThreads * 8 == kBM * kBK, "A stage is whole chunks per thread");
+static_assert(kChunksB * kThreads * 8 == kBN * kBK, "B stage is whole chunks per thread");
+static_assert(kTile % kBN == 0, "a vocab tile is whole sub-blocks");
+
+struct Smem {
+    uint16_t a[2][kBM * kRow];  // hidden-state stage, [row][k]
+    uint16_t b[2][kBN * kRow];  // weight stage, [vocab row][k]
+    float red_max[kWN][kBM];    // per-wave-column row maxima of the current sub-block
+    float red_sum[kWN][kBM];    // per-wave-column row sums
+    float m[kBM], s[kBM], sel[kBM];  // running tile state per row
+    int y_rel[kBM];             // target column inside this tile, or -1
+};
+
+// Loads this thread's 16-byte chunks of one stage: hidden rows [row0, row0 + kBM) and weight
+// rows [col0, col0 + kBN) of the view, hidden elements [k0, k0 + kBK).  Out-of-range chunks
+// (rows >= n, weight rows >= lim, k >= H) are zero.
+__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ h, int64_t ld_h,
+                                           int64_t n, const uint16_t* __restrict__ w, int64_t ld_w,
+                                           int lim, int H, int64_t row0, int col0, int k0,
+                                           u32x4v (&ra)[kChunksA], u32x4v (&rb)[kChunksB]) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kChunksA; ++i) {
+        const int q = t + i * kThreads;
+        const int r = q / kChunksPerRow, k = k0 + (q % kChunksPerRow) * 8;
+        const int64_t row = row0 + r;
+        ra[i] = (row < n && k < H)
+                    ? *reinterpret_cast<const u32x4v*>(h + row * ld_h + k)
+                    : u32x4v{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kChunksB; ++i) {
+        const int q = t + i * kThreads;
+        const int r = q / kChunksPerRow, k = k0 + (q % kChunksPerRow) * 8;
+        const int col = col0 + r;
+        rb[i] = (col < lim && k < H)
+                    ? *reinterpret_cast<const u32x4v*>(w + int64_t(col) * ld_w + k)
+                    : u32x4v{0u, 0u, 0u, 0u};
+    }
+}
+
+__device__ __forceinline__ void store_stage(Smem& sm, int buf, const u32x4v (&ra)[kChunksA],
+                                            const u32x4v (&rb)[kChunksB]) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kChunksA; ++i) {
+        const int q = t + i * kThreads;
+        *reinterpret_cast<u32x4v*>(&sm.a[buf][(q / kChunksPerRow) * kRow +
+                                              (q % kChunksPerRow) * 8]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kChunksB; ++i) {
+        const int q = t + i * kThreads;
+        *reinterpret_cast<u32x4v*>(&sm.b[buf][(q / kChunksPerRow) * kRow +
+                                              (q % kChunksPerRow) * 8]) = rb[i];
+    }
+}
+
+// Row (inside the workgroup's block) of accumulator register r of MFMA row-tile tm, for lane
+// `lane` of wave-row wm: the 32 x 32 result layout puts column (lane & 31) in a lane and
+// rows (r & 3) + 8 (r >> 2) + 4 (lane >> 5) in its 16 registers.
+__device__ __forceinline__ int acc_row(int wm, int tm, int r, int lane) {
+    return wm * (kTM * 32) + tm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+}
+
+// Max / sum over the 32 lanes of a half-wave (the lanes that hold one row of a 32-column
+// tile): pairwise tree over lane index, partners xor 1, 2, 4, 8, 16.
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) v = v + __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void linear_partials_kernel(
+    const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
+    const uint16_t* __restrict__ w, int64_t ld_w, int lim, int row_blocks, int64_t col_begin,
+    int64_t vocab_real, const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
+    int64_t ignore_index, logp_partial_t* __restrict__ partials, int64_t ldp) {
+    __shared__ Smem sm;
+    const int rb_idx = static_cast<int>(blockIdx.x % static_cast<uint32_t>(row_blocks));
+    const int tile = static_cast<int>(blockIdx.x / static_cast<uint32_t>(row_blocks));
+    const int64_t row0 = int64_t(rb_idx) * kBM;
+    const int tile_col0 = tile * kTile;  // first view column of the tile
+    const int lane = lane_id(), wave = wave_id();
+    const int wm = wave / kWN, wn = wave % kWN;
+
+    if (threadIdx.x < kBM) {
+        const int t = threadIdx.x;
+        const int64_t row = row0 + t;
+        int yr = -1;
+        if (row < n) {
+            int64_t y;
+            if (row_valid(targets, active, ignore_index, vocab_real, row, y)) {
+                const int64_t c = y - col_begin - tile_col0;
+                if (c >= 0 && c < kTile) yr = static_cast<int>(c);
+            }
+        }
+        sm.y_rel[t] = yr;
+        sm.m[t] = kNegInf;
+        sm.s[t] = 0.0f;
+        sm.sel[t] = 0.0f;
+    }
+
+    const int nk = (H + kBK - 1) / kBK;
+    for (int sb = 0; sb < kSubBlocks; ++sb) {
+        const int col0 = tile_col0 + sb * kBN;  // first view column of the sub-block
+        f32x16 acc[kTM][kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        u32x4v ra[kChunksA], rbv[kChunksB];
+        load_stage(h, ld_h, n, w, ld_w, lim, H, row0, col0, 0, ra, rbv);
+        store_stage(sm, 0, ra, rbv);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < nk)
+                load_stage(h, ld_h, n, w, ld_w, lim, H, row0, col0, (kt + 1) * kBK, ra, rbv);
+#pragma unroll
+            for (int ks = 0; ks < kBK / 16; ++ks) {
+                const int k = ks * 16 + 8 * (lane >> 5);
+                bf16x8 fa[kTM], fb[kTN];
+#pragma unroll
+                for (int i = 0; i < kTM; ++i)
+                    fa[i] = *reinterpret_cast<const bf16x8*>(
+                        &sm.a[cur][(wm * kTM * 32 + i * 32 + (lane & 31)) * kRow + k]);
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    fb[j] = *reinterpret_cast<const bf16x8*>(
+                        &sm.b[cur][(wn * kTN * 32 + j * 32 + (lane & 31)) * kRow + k]);
+#pragma unroll
+                for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                    for (int j = 0; j < kTN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j],
+                                                                             acc[i][j], 0, 0, 0);
+            }
+            if (kt + 1 < nk) store_stage(sm, cur ^ 1, ra, rbv);
+            __syncthreads();
+        }
+
+        // ---- sub-block reduction: masked columns are -inf
+        bool col_ok[kTN];
+        int col_in_tile[kTN];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            col_in_tile[j] = sb * kBN + wn * (kTN * 32) + j * 32 + (lane & 31);
+            col_ok[j] = tile_col0 + col_in_tile[j] < lim;
+        }
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = kNegInf;
+#pragma unroll
+                for (int j = 0; j < kTN; ++j) v = fmaxf(v, col_ok[j] ? acc[i][j][r] : kNegInf);
+                v = half_max(v);
+                const int row = acc_row(wm, i, r, lane);
+                if ((lane & 31) == 0) sm.red_max[wn][row] = v;
+                const int yr = sm.y_rel[row];
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    if (col_ok[j] && yr == col_in_tile[j]) sm.sel[row] = acc[i][j][r];
+            }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = acc_row(wm, i, r, lane);
+                float mb = sm.red_max[0][row];
+#pragma unroll
+                for (int q = 1; q < kWN; ++q) mb = fmaxf(mb, sm.red_max[q][row]);
+                float ls = 0.0f;
+                if (mb != kNegInf) {
+#pragma unroll
+                    for (int j = 0; j < kTN; ++j)
+                        ls = ls + (col_ok[j] ? fwd_exp(acc[i][j][r] - mb) : 0.0f);
+                }
+                ls = half_sum(ls);
+                if ((lane & 31) == 0) sm.red_sum[wn][row] = ls;
+            }
+        __syncthreads();
+        if (threadIdx.x < kBM) {
+            const int t = threadIdx.x;
+            float mb = sm.red_max[0][t];
+            float sb_sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < kWN; ++q) {
+                mb = fmaxf(mb, sm.red_max[q][t]);
+                sb_sum = sb_sum + sm.red_sum[q][t];
+            }
+            const float m_old = sm.m[t];
+            const float m_new = fmaxf(m_old, mb);
+            const float a = m_old == kNegInf ? 0.0f : sm.s[t] * fwd_exp(m_old - m_new);
+            const float b = mb == kNegInf ? 0.0f : sb_sum * fwd_exp(mb - m_new);
+            sm.m[t] = m_new;
+            sm.s[t] = a + b;
+        }
+        // the next sub-block's first barrier orders these LDS updates before any reuse
+    }
+    __syncthreads();
+    if (threadIdx.x < kBM) {
+        const int t = threadIdx.x;
+        const int64_t row = row0 + t;
+        if (row < n) {
+            logp_partial_t p;
+            p.max = sm.m[t];
+            p.sumexp = sm.s[t];
+            p.sel = sm.sel[t];
+            partials[row * ldp + tile] = p;
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h, int64_t n,
+                                   int64_t hidden_size, const uint16_t* weight, int64_t ld_w,
+                                   int64_t vocab_real, int64_t vocab_padded, int64_t col_begin,
+                                   int64_t col_end, const int64_t* targets, const uint8_t* active,
+                                   int64_t ignore_index, logp_partial_t* partials, int64_t ldp,
+                                   hipStream_t stream) {
+    if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
+        vocab_padded > (int64_t(1) << 31) - 1 - kTile)
+        return LOGP_ERR_SHAPE;
+    if (col_begin < 0 || col_end < col_begin || col_end > vocab_padded ||
+        col_begin % kTile != 0 || (col_end % kTile != 0 && col_end != vocab_padded))
+        return LOGP_ERR_SHARD;
+    if (n == 0 || col_end == col_begin) return LOGP_OK;
+    if (hidden == nullptr || weight == nullptr || targets == nullptr || partials == nullptr)
+        return LOGP_ERR_NULL;
+    const int64_t H = hidden_size;
+    if (H < 1 || H > LINEAR_LOGP_MAX_HIDDEN || H % 8 != 0 || ld_h < H || ld_w < H ||
+        ld_h % 8 != 0 || ld_w % 8 != 0 || !aligned16(hidden) || !aligned16(weight))
+        return LOGP_ERR_SHAPE;
+    const int64_t width = col_end - col_begin;
+    const int64_t view_tiles = ceil_div(width, kTile);
+    if (ldp < view_tiles) return LOGP_ERR_SHAPE;
+    if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
+    // weight rows actually read: the view's real vocabulary rows
+    const int64_t lim = std::max<int64_t>(0, std::min(width, vocab_real - col_begin));
+    const Span in[] = {{hidden, span_bytes(n, ld_h, H, 2)},
+                       {weight, lim > 0 ? span_bytes(lim, ld_w, H, 2) : 0},
+                       {targets, uint64_t(n) * 8},
+                       {active, active ? uint64_t(n) : 0}};
+    const Span out[] = {{partials, span_bytes(n, ldp, view_tiles, sizeof(logp_partial_t))}};
+    int dev = -1;
+    logp_status_t st = check_buffers(in, 4, out, 1, stream, &dev);
+    if (st != LOGP_OK) return st;
+    DeviceGuard guard(dev);
+    if (!guard.ok()) return LOGP_ERR_DEVICE;
+    const int64_t row_blocks = ceil_div(n, kBM);
+    if (row_blocks * view_tiles > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
+    int Hi = static_cast<int>(H), lim_i = static_cast<int>(lim);
+    int rbk = static_cast<int>(row_blocks);
+    void* args[] = {&hidden, &ld_h, &n, &Hi, &weight, &ld_w, &lim_i, &rbk, &col_begin,
+                    &vocab_real, &targets, &active, &ignore_index, &partials, &ldp};
+    return launch(reinterpret_cast<const void*>(&linear_partials_kernel),
+                  dim3(static_cast<uint32_t>(row_blocks * view_tiles)), dim3(kThreads), args, 0,
+                  stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+"""Python binding of the fused LM-head + selected-token logp (C ABI in include/linear_logp.h).
+
+Argument marshalling only: tensors are checked, outputs allocated with torch when none are
+passed, and the C entry points called on torch's current stream.  The logits h W^T are
+formed and reduced inside the HIP kernel; the merge is the log-probability library's
+``logp_merge``.
+
+Tensor conventions:
+  * hidden: bfloat16 ``[n, H]`` with unit column stride (row stride a multiple of 8, start
+    16-byte aligned); weight: bfloat16 rows of the LM head ``[rows, H]`` (a vocab shard is a
+    row slice ``W[c0:c1]``); H a multiple of 8.
+  * partials: float32 ``[n, L, 3]`` of (m_l, s_l, sel_l), ``L = logp_num_tiles(vocab_padded)``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _stream, logp_merge,
+               logp_num_tiles)
+
+EXPORTED = ("linear_logp_partials",)
+MAX_HIDDEN = 65536
+
+_P, _I64 = ctypes.c_void_p, ctypes.c_int64
+_lib.linear_logp_partials.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64,
+                                      _P, _P, _I64, _P, _I64, _P]
+_lib.linear_logp_partials.restype = ctypes.c_int32
+
+
+def _bf16_rows(name: str, t: torch.Tensor, device=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bfloat16 tensor")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t
+
+
+def _row_stride(t: torch.Tensor) -> int:
+    return int(t.stride(0)) if t.shape[0] > 1 else int(max(t.shape[1], t.stride(0), 8))
+
+
+def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                         vocab_real: int, vocab_padded: int, col_begin: int, col_end: int,
+                         partials: torch.Tensor, active=None, ignore_index: int = -100,
+                         stream=None) -> torch.Tensor:
+    """Write the (m, s, sel) partials of vocab columns [col_begin, col_end) of h W^T into the
+    full ``partials`` buffer; ``weight`` is the row slice W[col_begin:col_end]."""
+    hidden = _bf16_rows("hidden", hidden)
+    dev = hidden.device
+    weight = _bf16_rows("weight", weight, dev)
+    n, H = hidden.shape
+    if weight.shape[1] != H:
+        raise ValueError("hidden and weight must have the same hidden size")
+    targets = _rows("targets", targets, torch.int64, n, dev)
+    active = _active(active, n, dev)
+    if partials.dim() != 3 or partials.shape[0] != n or partials.shape[2] != 3 \
+            or partials.dtype != torch.float32 or partials.device != dev \
+            or partials.stride(2) != 1 or partials.stride(1) != 3:
+        raise ValueError("partials must be float32 [n, L, 3] with packed triples")
+    if col_begin % TILE_COLS != 0 or col_begin // TILE_COLS >= partials.shape[1]:
+        raise ValueError("col_begin must be a tile boundary inside the partials buffer")
+    rows_needed = max(0, min(col_end, vocab_real) - col_begin)
+    if weight.shape[0] < rows_needed:
+        raise ValueError(f"weight holds {weight.shape[0]} rows, the range needs {rows_needed}")
+    first = partials[:, col_begin // TILE_COLS]
+    ldp = partials.stride(0) // 3 if partials.stride(0) % 3 == 0 else -1
+    st = _lib.linear_logp_partials(
+        _ptr(hidden), _row_stride(hidden), n, H, _ptr(weight), _row_stride(weight),
+        int(vocab_real), int(vocab_padded), int(col_begin), int(col_end), _ptr(targets),
+        _ptr(active), int(ignore_index), first.data_ptr(), ldp, _stream(dev, stream))
+    _check("linear_logp_partials", st)
+    return partials
+
+
+def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                        vocab_real: Optional[int] = None, vocab_padded: Optional[int] = None,
+                        active=None, ignore_index: int = -100,
+                        partials: Optional[torch.Tensor] = None,
+                        logp: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        stats: Optional[torch.Tensor] = None, stream=None):
+    """logp, LSE and (M, S) of the logits h W^T over the whole vocabulary:
+    linear_logp_partials over all tiles, then logp_merge -> (logp, lse, stats)."""
+    vocab_padded = weight.shape[0] if vocab_padded is None else int(vocab_padded)
+    vocab_real = vocab_padded if vocab_real is None else int(vocab_real)
+    n = hidden.shape[0]
+    L = logp_num_tiles(vocab_padded)
+    if partials is None:
+        partials = torch.empty((n, L, 3), dtype=torch.float32, device=hidden.device)
+    linear_logp_partials(hidden, weight, targets, vocab_real, vocab_padded, 0, vocab_padded,
+                         partials, active=active, ignore_index=ignore_index, stream=stream)
+    return logp_merge(partials, targets, vocab_real, num_tiles=L, active=active,
+                      ignore_index=ignore_index, logp=logp, lse=lse, stats=stats,
+                      stream=stream)

@@ -1,0 +1,69 @@
+/* Fused LM-head + selected-token log-probability (linear_logp), for MI355X (gfx950).
+ *
+ * Source: PR #495 "zero-workspace backward for generic CUDA fused logp" lists linear_logp,
+ * the fused LM-head plus logp op, beside the generic fused logp (Summary); issue #241 "[WS2]
+ * TP-aware deterministic logprob …" fixes what the logp path computes and how vocab-parallel
+ * partials merge (sections PR 3 and PR6).  The pages give linear_logp no more than its name;
+ * the reading here: the logits z = h W^T of BF16 hidden states h [n, H] and the BF16 LM-head
+ * weight W [V, H] (one row per vocabulary entry) are formed tile by tile on the matrix cores
+ * with FP32 accumulation and reduced at once to the per-tile partials of logp.h, so the
+ * [n, V] logits never exist in memory.  logp_merge over those partials then gives logp, LSE
+ * and (M, S) exactly as for materialised logits, and a vocab-parallel rank that holds the
+ * rows [col_begin, col_end) of W produces its slice of the same partials.
+ *
+ * Numerical contract (deterministic, independent of n, of a row's position in the batch and
+ * of the shard split):
+ *   z[t, v]  = sum over k of h[t, k] W[v, k]: products exact, added in FP32 by a fixed
+ *              sequence of v_mfma_f32_32x32x16_bf16 steps, k = 0, 16, 32, ... (hidden sizes
+ *              that are not a multiple of 32 are padded with zeros);
+ *   each 4096-column global tile is reduced in 32 sub-blocks of 128 columns; a sub-block
+ *   gives (m_b, s_b) with m_b its max and s_b = sum exp(z - m_b) added in a fixed lane
+ *   order; the tile's (m_l, s_l) folds the sub-blocks in order, b = 0 .. 31:
+ *   m <- max(m, m_b), s <- s exp(m_old - m) + s_b exp(m_b - m) (terms of -inf maxima are 0);
+ *   sel_l = z[t, y_t] in the owner tile of a valid row, 0 elsewhere.  exp is the logp
+ *   forward's (2^(t log2 e) on the hardware exp2).
+ *
+ * All pointers are device memory on one device, owned by the caller; arguments are checked
+ * on the host before any launch (codes of logp.h).  Nothing is allocated; nothing
+ * synchronizes. */
+#ifndef LINEAR_LOGP_H
+#define LINEAR_LOGP_H
+
+#include <stdint.h>
+
+#include "logp.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LINEAR_LOGP_MAX_HIDDEN 65536  /* largest hidden size H */
+
+/* Per-tile partials of the logits h W^T over the vocabulary columns [col_begin, col_end).
+ *   hidden        [n, ld_h] BF16 bits; row t at hidden + t*ld_h; H = hidden_size columns used.
+ *   weight        BF16 bits pointing at row col_begin of W: row v of the view at
+ *                 weight + (v - col_begin)*ld_w, H columns used.  Rows at or beyond vocab_real
+ *                 are never read (they count as -inf logits, like padding columns).
+ *   hidden_size   H, 1 <= H <= LINEAR_LOGP_MAX_HIDDEN, a multiple of 8.
+ *   ld_h, ld_w    row strides in elements, >= H and multiples of 8; hidden and weight must
+ *                 be 16-byte aligned (else LOGP_ERR_SHAPE).
+ *   vocab_real, vocab_padded, col_begin, col_end, targets, active, ignore_index, partials,
+ *   ldp           exactly as in logp_partials: col_begin a multiple of LOGP_TILE_COLS, col_end
+ *                 one too or vocab_padded; partials points at the slot of tile
+ *                 col_begin / LOGP_TILE_COLS of row 0 of an [n, ldp] array.
+ * logp_merge over all tiles completes the forward (logp, LSE, stats for logp_backward_ex on
+ * the same logits). */
+LOGP_API logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h, int64_t n,
+                                            int64_t hidden_size, const uint16_t* weight,
+                                            int64_t ld_w, int64_t vocab_real,
+                                            int64_t vocab_padded, int64_t col_begin,
+                                            int64_t col_end, const int64_t* targets,
+                                            const uint8_t* active, int64_t ignore_index,
+                                            logp_partial_t* partials, int64_t ldp,
+                                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINEAR_LOGP_H */

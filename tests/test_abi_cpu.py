@@ -20,7 +20,7 @@ HEADERS = [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE)) if f.en
 PKG = os.path.join(ROOT, "deterministic_selected_token_amd")
 
 import deterministic_selected_token_amd as dst  # noqa: E402
-from deterministic_selected_token_amd import grpo  # noqa: E402
+from deterministic_selected_token_amd import grpo, linear  # noqa: E402
 
 OK, NULL, SHAPE, SHARD, ARG = 0, 1, 2, 3, 8
 T = 4096
@@ -31,20 +31,20 @@ def declared_functions() -> list[str]:
     names = []
     for h in HEADERS:
         text = open(h).read()
-        names += re.findall(r"^LOGP_API\s+[\w\s\*]+?\b((?:logp|grpo)_\w+)\s*\(", text,
-                            flags=re.M)
+        names += re.findall(r"^LOGP_API\s+[\w\s\*]+?\b((?:logp|grpo|linear)_\w+)\s*\(",
+                            text, flags=re.M)
     return names
 
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert sorted(names) == sorted(dst.EXPORTED + grpo.EXPORTED)
+    assert sorted(names) == sorted(dst.EXPORTED + grpo.EXPORTED + linear.EXPORTED)
     lib = ctypes.CDLL(dst.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", dst.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT\s+((?:logp|grpo)_\w+)$", out, flags=re.M))
+    exported = set(re.findall(r"\bT\s+((?:logp|grpo|linear)_\w+)$", out, flags=re.M))
     assert exported == set(names)  # nothing else with the prefixes leaks out
 
 

@@ -1,0 +1,165 @@
+"""Fused LM-head + selected-token logp on the GPU against the FP64 oracle, and its bitwise
+contract (run to run, batch composition, vocab shards, padding).
+
+Tolerance, derived from the arithmetic: each logit is a float32 accumulation of H exact
+BF16 x BF16 products in H/16 matrix-core steps, so |z_gpu - z| <= (H/16 + 2) 2^-24 A_v with
+A_v = sum_k |h_k W_vk|.  logp = z_y - LSE then moves by at most twice the largest such bound
+of the row, plus the float32 rounding of the logp arithmetic (1e-6 relative).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import deterministic_selected_token_amd as dst
+from deterministic_selected_token_amd import linear
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+T = dst.TILE_COLS
+
+
+def say(msg: str):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def make(n, H, V, Vp=None, seed=0, scale=3.0, ignore_frac=0.1, pad_value=float("nan")):
+    """h ~ N(0, 1), W ~ N(0, scale^2 / H) (logits ~ N(0, scale^2)); rows of W at or beyond V
+    hold `pad_value` (never read)."""
+    Vp = V if Vp is None else Vp
+    g = torch.Generator().manual_seed(seed)
+    h = torch.randn((n, H), generator=g).to(torch.bfloat16)
+    W = torch.full((Vp, H), pad_value)
+    W[:V] = torch.randn((V, H), generator=g) * (scale / H ** 0.5)
+    W = W.to(torch.bfloat16)
+    y = torch.randint(0, V, (n,), generator=g)
+    y[torch.rand(n, generator=g) < ignore_frac] = -100
+    return h.to(DEV), W.to(DEV), y.to(DEV)
+
+
+def check(h, W, y, V, Vp=None, rows=None, active=None):
+    from oracle import linear_oracle as LO
+    Vp = V if Vp is None else Vp
+    logp, lse, stats = linear.linear_logp_forward(h, W, y, V, Vp, active=active)
+    torch.cuda.synchronize()
+    rows = np.arange(h.shape[0]) if rows is None else np.asarray(rows)
+    hc = h.cpu()[rows]
+    Wc = W.cpu()[:V]
+    yc = y.cpu().numpy()[rows]
+    act = None if active is None else active.cpu().numpy()[rows]
+    ref = LO.forward(hc, Wc, yc, V, active=act)
+    A = LO.logit_abs(hc, Wc, V)
+    H = h.shape[1]
+    bound = (H / 16 + 2) * 2.0 ** -24 * A.max(axis=1)
+    lp = logp.cpu().numpy()[rows].astype(np.float64)
+    ls = lse.cpu().numpy()[rows].astype(np.float64)
+    fin = np.isfinite(ref["logp"])
+    err = np.abs(lp - ref["logp"])
+    tol = 2 * bound + 1e-6 * (1 + np.abs(ref["logp"]))
+    assert np.all(err[fin] <= tol[fin]), (err[fin].max(), tol[fin].min())
+    assert np.all(lp[~fin] == ref["logp"][~fin])
+    lerr = np.abs(ls - ref["lse"])
+    assert np.all(lerr <= bound + 1e-6 * (1 + np.abs(ref["lse"])))
+    st = stats.cpu().numpy()[rows].astype(np.float64)
+    assert np.all(np.abs(st[:, 0] - ref["max"]) <= bound)
+    return {"logp_max_err": float(err[fin].max(initial=0)),
+            "lse_max_err": float(lerr.max()), "bound_min": float(bound.min())}, (logp, lse, stats)
+
+
+SHAPES = [(5, 64, 300), (130, 128, 5000), (64, 256, 4100), (33, 200, 8192),
+          (200, 512, 12345), (3, 8, 4096)]
+
+
+@pytest.mark.parametrize("n,H,V", SHAPES, ids=[f"n{n}_H{H}_V{V}" for n, H, V in SHAPES])
+def test_linear_parity(n, H, V):
+    h, W, y = make(n, H, V, seed=n + H + V)
+    say(f"linear parity n={n} H={H} V={V}")
+    res, _ = check(h, W, y, V)
+    say(f"n={n} H={H} V={V}: {res}")
+
+
+def test_linear_padding_rows_never_read_and_padding_invariance():
+    V, Vp, H = 10000, 16384, 256  # the fourth tile is all padding
+    h, W, y = make(50, H, V, Vp, seed=3, pad_value=float("nan"))
+    say("padded vocabulary with NaN rows")
+    res, (lp, ls, st) = check(h, W, y, V, Vp)
+    lp2, ls2, st2 = linear.linear_logp_forward(h, W[:V].contiguous(), y, V, V)
+    assert torch.equal(lp, lp2) and torch.equal(ls, ls2) and torch.equal(st, st2)
+
+
+def test_linear_qwen_width_sampled():
+    """Qwen3-8B LM-head shape (H = 4096, V = 151936) on 256 rows; 12 rows against the oracle."""
+    h, W, y = make(256, 4096, 151936, seed=5)
+    say("linear H=4096 V=151936, 256 rows")
+    res, _ = check(h, W, y, 151936, rows=np.arange(0, 256, 23))
+    say(f"qwen width: {res}")
+
+
+def test_linear_masks_and_targets():
+    h, W, y = make(70, 128, 9000, seed=7, ignore_frac=0.0)
+    y[0] = 0
+    y[1] = 8999
+    y[2] = 9000   # out of range: invalid
+    y[3] = -100
+    active = (torch.arange(70, device=DEV) % 5 != 0).to(torch.uint8)
+    say("masks and boundary targets")
+    res, (lp, _, _) = check(h, W, y, 9000, active=active)
+    lpc = lp.cpu()
+    assert lpc[2] == 0 and lpc[3] == 0 and torch.all(lpc[::5] == 0)
+
+
+def test_linear_run_to_run_and_batch_invariance():
+    n, H, V = 300, 256, 20000
+    h, W, y = make(n, H, V, seed=11)
+    say("linear run to run / batch composition")
+    ref = linear.linear_logp_forward(h, W, y, V)
+    again = linear.linear_logp_forward(h, W, y, V)
+    assert all(torch.equal(a, b) for a, b in zip(ref, again))
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(1)).to(DEV)
+    got = linear.linear_logp_forward(h[perm].contiguous(), W, y[perm].contiguous(), V)
+    assert all(torch.equal(a[perm], b) for a, b in zip(ref, got))
+    for chunk in (1, 7, 129):
+        for r0 in range(0, n, chunk):
+            s = slice(r0, min(n, r0 + chunk))
+            got = linear.linear_logp_forward(h[s], W, y[s], V)
+            assert all(torch.equal(a[s], b) for a, b in zip(ref, got)), chunk
+
+
+def test_linear_vocab_shards_are_bitwise():
+    """Rows of W split over 'ranks' at tile boundaries: shard partials merge to the same bits
+    as one call, including an all-padding last shard."""
+    n, H, V, Vp = 40, 128, 3 * T + 1000, 5 * T
+    h, W, y = make(n, H, V, Vp, seed=13, pad_value=0.0)
+    say("linear vocab shards")
+    ref = linear.linear_logp_forward(h, W, y, V, Vp)
+    L = dst.logp_num_tiles(Vp)
+    for layout in ([5], [2, 3], [1, 1, 2, 1], [4, 1]):
+        partials = torch.full((n, L, 3), float("nan"), device=DEV)
+        c0 = 0
+        for tiles in layout:
+            c1 = min(Vp, c0 + tiles * T)
+            linear.linear_logp_partials(h, W[c0:c1], y, V, Vp, c0, c1, partials)
+            c0 = c1
+        got = dst.logp_merge(partials, y, V)
+        assert all(torch.equal(a, b) for a, b in zip(ref, got)), layout
+
+
+def test_linear_partials_against_oracle_tiles():
+    from oracle import linear_oracle as LO
+    n, H, V = 20, 64, 2 * T + 300
+    h, W, y = make(n, H, V, seed=17)
+    say("linear partials vs oracle tiles")
+    L = dst.logp_num_tiles(V)
+    partials = torch.empty((n, L, 3), device=DEV)
+    linear.linear_logp_partials(h, W, y, V, V, 0, V, partials)
+    p = partials.cpu().numpy().astype(np.float64)
+    ref = LO.tile_partials(h.cpu(), W.cpu(), y.cpu().numpy(), V, V)
+    A = LO.logit_abs(h.cpu(), W.cpu(), V)
+    bound = (H / 16 + 2) * 2.0 ** -24 * A.max()
+    assert np.all(np.abs(p[..., 0] - ref["max"]) <= bound)
+    assert np.allclose(p[..., 1], ref["sumexp"], rtol=2e-5 + 4 * bound, atol=0)
+    owner = ref["sel"] != 0
+    assert np.all(np.abs(p[..., 2] - ref["sel"]) <= bound)
+    assert np.all(p[..., 2][~owner] == 0)

@@ -1,0 +1,56 @@
+"""Host-side validation of linear_logp_partials (no GPU: every case fails before any HIP
+call) and the constants the binding shares with include/linear_logp.h."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from deterministic_selected_token_amd import linear
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, SHARD = 0, 1, 2, 3
+A = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced
+U = ctypes.c_void_p(0x10002)  # misaligned
+lib = linear._lib
+
+
+def call(**over):
+    a = dict(h=A, ld_h=64, n=10, H=64, w=A, ld_w=64, vr=5000, vp=5000, c0=0, c1=5000, y=A,
+             act=None, ign=-100, p=A, ldp=2)
+    a.update(over)
+    return lib.linear_logp_partials(a["h"], a["ld_h"], a["n"], a["H"], a["w"], a["ld_w"],
+                                    a["vr"], a["vp"], a["c0"], a["c1"], a["y"], a["act"],
+                                    a["ign"], a["p"], a["ldp"], None)
+
+
+def test_header_constant():
+    text = open(os.path.join(ROOT, "include", "linear_logp.h")).read()
+    assert int(re.search(r"#define LINEAR_LOGP_MAX_HIDDEN (\d+)", text).group(1)) == \
+        linear.MAX_HIDDEN
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(n=-1), SHAPE), (dict(vr=0), SHAPE), (dict(vp=4000), SHAPE),
+    (dict(c0=100), SHARD), (dict(c1=4097), SHARD), (dict(c1=6000), SHARD),
+    (dict(n=0), OK), (dict(c0=4096, c1=4096), OK),
+    (dict(h=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL), (dict(p=None), NULL),
+    (dict(H=0), SHAPE), (dict(H=60, ld_h=64, ld_w=64), SHAPE), (dict(H=65544, ld_h=65544,
+                                                                     ld_w=65544), SHAPE),
+    (dict(ld_h=60), SHAPE), (dict(ld_w=68), SHAPE), (dict(ld_h=72, H=72, ld_w=71), SHAPE),
+    (dict(h=U), SHAPE), (dict(w=U), SHAPE), (dict(ldp=1), SHAPE),
+], ids=lambda v: str(v))
+def test_linear_partials_host_validation(over, want):
+    assert call(**over) == want
+
+
+def test_binding_rejects_cpu_and_wrong_dtype():
+    import torch
+    h = torch.zeros((2, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        linear.linear_logp_forward(h, h, torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        linear.linear_logp_forward(h.float(), h, torch.zeros(2, dtype=torch.int64))
