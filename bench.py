@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix-core peak
 PAGES_FWD_BWD_MS = 27.2  # fused kernel, B200, N=32768, V=151936, BF16 (context, not target)
 METRIC = "fwd+bwd ms and achieved HBM GB/s (% of peak), N=32768 V=151936 BF16"
 KERNEL_SOURCES = [os.path.join(ROOT, "deterministic_selected_token_amd", "csrc", f)
@@ -255,6 +256,49 @@ def time_grpo(dst, case, stream, steps: int) -> dict:
     return out
 
 
+def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
+                vocab: int = 151936) -> dict:
+    """linear_logp forward (linear_logp_partials + logp_merge) on n rows of a Qwen3-8B-shaped
+    LM head (hidden 4096, vocabulary 151936): 2 n V H flops on the matrix cores."""
+    import torch
+
+    from deterministic_selected_token_amd import linear
+
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    h = torch.randn((n, hidden), generator=gen, device=dev).to(torch.bfloat16)
+    W = (torch.randn((vocab, hidden), generator=gen, device=dev) * (3.0 / hidden ** 0.5)) \
+        .to(torch.bfloat16)
+    y = torch.randint(0, vocab, (n,), generator=gen, device=dev)
+    L = dst.logp_num_tiles(vocab)
+    partials = torch.empty((n, L, 3), dtype=torch.float32, device=dev)
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse, stats = torch.empty_like(logp), torch.empty((n, 2), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        linear.linear_logp_partials(h, W, y, vocab, vocab, 0, vocab, partials, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dst.logp_merge(partials, y, vocab, logp=logp, lse=lse, stats=stats, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    k_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    m_ms = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+    flops = 2.0 * n * vocab * hidden
+    return {"rows": n, "hidden": hidden, "vocab": vocab, "partials_ms": round(k_ms, 4),
+            "merge_ms": round(m_ms, 4), "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1),
+            "frac_of_bf16_peak": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,6 +406,7 @@ def main() -> int:
     if args.variants:
         extra["variants"] = time_variants(dst, case, stream, args.steps)
         extra["variants"].update(time_grpo(dst, case, stream, args.steps))
+        extra["variants"]["linear_logp_fwd"] = time_linear(dst, stream, max(3, args.steps // 4))
     if args.profile_copy:
         src = torch.empty(1 << 31, dtype=torch.int16, device=dev)  # 4 GiB
         dst_buf = torch.empty_like(src)

@@ -2,7 +2,7 @@
 // (include/linear_logp.h).
 //
 // One workgroup per (block of 128 rows, global vocab tile of 4096 columns).  It walks the
-// tile in 32 sub-blocks of 128 columns; for each it forms the 128 x 128 logits block on the
+// tile in 16 sub-blocks of 256 columns; for each it forms the 128 x 256 logits block on the
 // matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension, the
 // hidden states and weight rows staged through double-buffered LDS with the next stage's
 // global loads in flight), reduces the block to a per-row (max, sum-exp) in registers with
@@ -31,7 +31,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWM = 2, kWN = 2;               // waves along rows / columns
-constexpr int kTM = 2, kTN = 2;               // 32 x 32 MFMA tiles per wave along rows / cols
+constexpr int kTM = 2, kTN = 4;               // 32 x 32 MFMA tiles per wave along rows / cols
 constexpr int kThreads = kWM * kWN * kWave;   // 256
 constexpr int kBM = kWM * kTM * 32;           // rows per workgroup
 constexpr int kBN = kWN * kTN * 32;           // columns per sub-block
