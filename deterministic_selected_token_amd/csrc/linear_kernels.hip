@@ -2,7 +2,7 @@
 // (include/linear_logp.h).
 //
 // One workgroup per (block of 128 rows, global vocab tile of 4096 columns).  It walks the
-// tile in 16 sub-blocks of 256 columns; for each it forms the 128 x 256 logits block on the
+// tile in 32 sub-blocks of 128 columns; for each it forms the 128 x 128 logits block on the
 // matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension, the
 // hidden states and weight rows staged through double-buffered LDS with the next stage's
 // global loads in flight), reduces the block to a per-row (max, sum-exp) in registers with
@@ -31,12 +31,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWM = 2, kWN = 2;               // waves along rows / columns
-constexpr int kTM = 2, kTN = 4;               // 32 x 32 MFMA tiles per wave along rows / cols
+constexpr int kTM = 2, kTN = 2;               // 32 x 32 MFMA tiles per wave along rows / cols
 constexpr int kThreads = kWM * kWN * kWave;   // 256
 constexpr int kBM = kWM * kTM * 32;           // rows per workgroup
 constexpr int kBN = kWN * kTN * 32;           // columns per sub-block
-constexpr int kBK = 32;                       // hidden elements per LDS stage
-constexpr int kRow = kBK + 8;                 // LDS row stride in elements (80 bytes)
+constexpr int kBK = 64;                       // hidden elements per LDS stage
+constexpr int kRow = kBK + 8;                 // LDS row stride in elements (144 bytes)
 constexpr int kSubBlocks = kTile / kBN;       // sub-blocks per vocab tile
 constexpr int kChunksA = kBM * kBK / 8 / kThreads;  // 16-byte chunks per thread per stage
 constexpr int kChunksB = kBN * kBK / 8 / kThreads;
@@ -46,13 +46,21 @@ static_assert(kChunksA * kThreads * 8 == kBM * kBK, "A stage is whole chunks per
 static_assert(kChunksB * kThreads * 8 == kBN * kBK, "B stage is whole chunks per thread");
 static_assert(kTile % kBN == 0, "a vocab tile is whole sub-blocks");
 
-struct Smem {
-    uint16_t a[2][kBM * kRow];  // hidden-state stage, [row][k]
-    uint16_t b[2][kBN * kRow];  // weight stage, [vocab row][k]
+// The stage arrays are 16-byte aligned so their 16-byte chunks move as single ds_read_b128 /
+// ds_write_b128 instructions.
+struct alignas(16) Smem {
+    alignas(16) uint16_t a[2][kBM * kRow];  // hidden-state stage, [row][k]
+    alignas(16) uint16_t b[2][kBN * kRow];  // weight stage, [vocab row][k]
     float red_max[kWN][kBM];    // per-wave-column row maxima of the current sub-block
     float red_sum[kWN][kBM];    // per-wave-column row sums
     float m[kBM], s[kBM], sel[kBM];  // running tile state per row
     int y_rel[kBM];             // target column inside this tile, or -1
+};
+
+// One stage of this thread's chunks in registers (global loads in flight).
+struct Stage {
+    u32x4v a[kChunksA];
+    u32x4v b[kChunksB];
 };
 
 // Loads this thread's 16-byte chunks of one stage: hidden rows [row0, row0 + kBM) and weight
@@ -61,7 +69,9 @@ struct Smem {
 __device__ __forceinline__ void load_stage(const uint16_t* __restrict__ h, int64_t ld_h,
                                            int64_t n, const uint16_t* __restrict__ w, int64_t ld_w,
                                            int lim, int H, int64_t row0, int col0, int k0,
-                                           u32x4v (&ra)[kChunksA], u32x4v (&rb)[kChunksB]) {
+                                           Stage& st) {
+    u32x4v (&ra)[kChunksA] = st.a;
+    u32x4v (&rb)[kChunksB] = st.b;
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kChunksA; ++i) {
@@ -83,8 +93,9 @@ __device__ __forceinline__ void load_stage(const uint16_t* __restrict__ h, int64
     }
 }
 
-__device__ __forceinline__ void store_stage(Smem& sm, int buf, const u32x4v (&ra)[kChunksA],
-                                            const u32x4v (&rb)[kChunksB]) {
+__device__ __forceinline__ void store_stage(Smem& sm, int buf, const Stage& st) {
+    const u32x4v (&ra)[kChunksA] = st.a;
+    const u32x4v (&rb)[kChunksB] = st.b;
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kChunksA; ++i) {
@@ -97,6 +108,30 @@ __device__ __forceinline__ void store_stage(Smem& sm, int buf, const u32x4v (&ra
         const int q = t + i * kThreads;
         *reinterpret_cast<u32x4v*>(&sm.b[buf][(q / kChunksPerRow) * kRow +
                                               (q % kChunksPerRow) * 8]) = rb[i];
+    }
+}
+
+// The matrix-core steps of one LDS stage: kBK / 16 steps of k, each wave's kTM x kTN tiles.
+__device__ __forceinline__ void mma_stage(const Smem& sm, int buf, int wm, int wn, int lane,
+                                          f32x16 (&acc)[kTM][kTN]) {
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+        const int k = ks * 16 + 8 * (lane >> 5);
+        bf16x8 fa[kTM], fb[kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8*>(
+                &sm.a[buf][(wm * kTM * 32 + i * 32 + (lane & 31)) * kRow + k]);
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+            fb[j] = *reinterpret_cast<const bf16x8*>(
+                &sm.b[buf][(wn * kTN * 32 + j * 32 + (lane & 31)) * kRow + k]);
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+                acc[i][j] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
 }
 
@@ -120,7 +155,9 @@ __device__ __forceinline__ float half_sum(float v) {
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void linear_partials_kernel(
+// Two workgroups per CU (78 KB of LDS each, at most 256 registers per lane) so that two waves
+// per SIMD cover each other's global-load latency.
+__global__ __launch_bounds__(kThreads, 2) void linear_partials_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
     const uint16_t* __restrict__ w, int64_t ld_w, int lim, int row_blocks, int64_t col_begin,
     int64_t vocab_real, const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
@@ -161,34 +198,18 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        u32x4v ra[kChunksA], rbv[kChunksB];
-        load_stage(h, ld_h, n, w, ld_w, lim, H, row0, col0, 0, ra, rbv);
-        store_stage(sm, 0, ra, rbv);
+        // The global loads of stage kt + 1 are issued before the matrix-core work of stage
+        // kt and go to the other LDS buffer after it.
+        Stage rs;
+        load_stage(h, ld_h, n, w, ld_w, lim, H, row0, col0, 0, rs);
+        store_stage(sm, 0, rs);
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
             if (kt + 1 < nk)
-                load_stage(h, ld_h, n, w, ld_w, lim, H, row0, col0, (kt + 1) * kBK, ra, rbv);
-#pragma unroll
-            for (int ks = 0; ks < kBK / 16; ++ks) {
-                const int k = ks * 16 + 8 * (lane >> 5);
-                bf16x8 fa[kTM], fb[kTN];
-#pragma unroll
-                for (int i = 0; i < kTM; ++i)
-                    fa[i] = *reinterpret_cast<const bf16x8*>(
-                        &sm.a[cur][(wm * kTM * 32 + i * 32 + (lane & 31)) * kRow + k]);
-#pragma unroll
-                for (int j = 0; j < kTN; ++j)
-                    fb[j] = *reinterpret_cast<const bf16x8*>(
-                        &sm.b[cur][(wn * kTN * 32 + j * 32 + (lane & 31)) * kRow + k]);
-#pragma unroll
-                for (int i = 0; i < kTM; ++i)
-#pragma unroll
-                    for (int j = 0; j < kTN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j],
-                                                                             acc[i][j], 0, 0, 0);
-            }
-            if (kt + 1 < nk) store_stage(sm, cur ^ 1, ra, rbv);
+                load_stage(h, ld_h, n, w, ld_w, lim, H, row0, col0, (kt + 1) * kBK, rs);
+            mma_stage(sm, cur, wm, wn, lane, acc);
+            if (kt + 1 < nk) store_stage(sm, cur ^ 1, rs);
             __syncthreads();
         }
 
