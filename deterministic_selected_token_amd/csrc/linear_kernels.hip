@@ -1,8 +1,8 @@
 // gfx950 kernel and C entry point of the fused LM-head + selected-token log-probability
 // (include/linear_logp.h).
 //
-// One workgroup per (block of 128 rows, global vocab tile of 4096 columns).  It walks the
-// tile in 32 sub-blocks of 128 columns; for each it forms the 128 x 128 logits block on the
+// One workgroup (8 waves) per (block of 128 rows, global vocab tile of 4096 columns).  It walks
+// the tile in 16 sub-blocks of 256 columns; for each it forms the 128 x 256 logits block on the
 // matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension, the
 // hidden states and weight rows staged through double-buffered LDS with the next stage's
 // global loads in flight), reduces the block to a per-row (max, sum-exp) in registers with
@@ -30,9 +30,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kWM = 2, kWN = 2;               // waves along rows / columns
+constexpr int kWM = 2, kWN = 4;               // waves along rows / columns
 constexpr int kTM = 2, kTN = 2;               // 32 x 32 MFMA tiles per wave along rows / cols
-constexpr int kThreads = kWM * kWN * kWave;   // 256
+constexpr int kThreads = kWM * kWN * kWave;   // 512
 constexpr int kBM = kWM * kTM * 32;           // rows per workgroup
 constexpr int kBN = kWN * kTN * 32;           // columns per sub-block
 constexpr int kBK = 64;                       // hidden elements per LDS stage
@@ -155,9 +155,9 @@ __device__ __forceinline__ float half_sum(float v) {
     return v;
 }
 
-// Two workgroups per CU (78 KB of LDS each, at most 256 registers per lane) so that two waves
-// per SIMD cover each other's global-load latency.
-__global__ __launch_bounds__(kThreads, 2) void linear_partials_kernel(
+// 8 waves per workgroup (114 KB of LDS, one workgroup per CU): two waves per SIMD cover each
+// other's global-load latency.
+__global__ __launch_bounds__(kThreads) void linear_partials_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
     const uint16_t* __restrict__ w, int64_t ld_w, int lim, int row_blocks, int64_t col_begin,
     int64_t vocab_real, const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
