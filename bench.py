@@ -252,8 +252,21 @@ def time_grpo(dst, case, stream, steps: int) -> dict:
     nbytes = B * T * (4 * 3 + 1 + 4) + B * (4 + 16) + 48
     out["grpo_loss_1024x4096"] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes,
                                   "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                                  "launches": 4}
+                                  "launches": 4, "cpu_baseline": grpo_oracle_rate(
+                                      lp, old, ref, adv, mask, nbytes)}
     return out
+
+
+def grpo_oracle_rate(lp, old, ref, adv, mask, nbytes: int) -> dict:
+    """The float64 GRPO oracle on the same tokens (numpy, as it stands), timed on the host."""
+    from oracle import grpo_oracle
+
+    host = [t.cpu().numpy() for t in (lp, old, ref, adv, mask)]
+    t0 = time.perf_counter()
+    grpo_oracle.loss(*host, mode="token_mean", beta=0.04)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+            "sample": f"all {lp.numel()} tokens, float64 numpy, {dt:.2f} s wall", "cores": 1}
 
 
 def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
@@ -294,9 +307,22 @@ def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
     k_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
     m_ms = sum(b.elapsed_time(c) for _, b, c in evs) / steps
     flops = 2.0 * n * vocab * hidden
+    # the float64 oracle on a few of the same rows (numpy float64 matmul + the C log-softmax)
+    from oracle import linear_oracle
+
+    rows = 4
+    h_host, w_host, y_host = h[:rows].cpu(), W.cpu(), y[:rows].cpu().numpy()
+    t0 = time.perf_counter()
+    linear_oracle.forward(h_host, w_host, y_host, vocab)
+    dt = time.perf_counter() - t0
+    cpu = {"value": round(2.0 * rows * vocab * hidden / dt / 1e12, 4), "unit": "TFLOP/s",
+           "kind": "oracle", "cores": len(os.sched_getaffinity(0)),
+           "sample": f"{rows} of the {n} rows, float64 logits and log-softmax, {dt:.2f} s wall "
+                     "(including the float64 copy of W)"}
     return {"rows": n, "hidden": hidden, "vocab": vocab, "partials_ms": round(k_ms, 4),
             "merge_ms": round(m_ms, 4), "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1),
-            "frac_of_bf16_peak": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "cpu_baseline": cpu}
 
 
 def main() -> int:
