@@ -11,7 +11,7 @@ marshals numpy arrays into it.
 
 Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``):
   forward, backward, tile_partials (BF16, FP16 and FP32 logits; any inv_temperature),
-  merge, rne_bf16, rne_f16, count_bad_targets: pinned.
+  merge, rne_bf16, rne_f16, count_bad_targets, backward_elements: pinned.
   Rows whose valid target logit is -inf while other logits are finite, and rows that
   hold NaN or +inf logits: parity unpinned (no closed form was written for them).
 
@@ -241,6 +241,28 @@ def backward(logits, targets, grad, vocab_real: int, vocab_padded: Optional[int]
                                        _ptr(rounded), vocab_padded, nthreads or default_threads())
     _check(rc, "backward")
     return {"d64": d64, "rounded": rounded, "bf16": rounded if dt == "bf16" else None}
+
+
+def backward_elements(logits_row, cols, target: int, grad: float, lse: float,
+                      vocab_real: int, valid: bool = True) -> np.ndarray:
+    """dlogits of one row at the given columns only, float64: g (1[c == y] - exp(x_c - LSE))
+    for real columns of a valid row, 0 elsewhere -- the definition ``backward`` evaluates for
+    whole rows, for rows too wide to expand in float64.  ``lse`` is the row's ``forward`` LSE;
+    ``logits_row`` is one BF16 row (torch bfloat16 or raw uint16 bits)."""
+    bits, dt = _logits(logits_row.reshape(1, -1) if hasattr(logits_row, "reshape")
+                       else np.asarray(logits_row).reshape(1, -1))
+    if dt != "bf16":
+        raise TypeError("backward_elements expects a BF16 row")
+    c = np.asarray(cols, dtype=np.int64)
+    out = np.zeros(c.shape, dtype=np.float64)
+    if not valid or not np.isfinite(lse):
+        return out
+    real = c < vocab_real
+    x = bf16_bits_to_f64(bits[0, c[real]])
+    d = -float(np.float32(grad)) * np.exp(x - lse)
+    d[c[real] == target] += float(np.float32(grad))
+    out[real] = d
+    return out
 
 
 def num_tiles(vocab_padded: int, tile: int = TILE) -> int:

@@ -592,3 +592,21 @@ def test_planted_mistakes_are_caught(name):
         assert _pins(lib) != [], f"planted mistake {name!r} passed every pin"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+def test_backward_elements_match_whole_row_backward():
+    """The sampled-column form used for rows too wide to expand gives the same values as the
+    whole-row backward (both evaluate g (onehot - softmax) in float64)."""
+    g = torch.Generator().manual_seed(41)
+    x = (torch.randn((3, 5000), generator=g) * 3).to(torch.bfloat16)
+    y = np.array([17, 4999, -100])
+    grad = np.array([0.75, -1.5, 2.0], dtype=np.float32)
+    vr = 4990  # target 4999 lies in padding: invalid
+    f = oracle.forward(x, y, vr)
+    b = oracle.backward(x, y, grad, vr, 5000)
+    cols = np.array([0, 17, 100, 4989, 4990, 4999])
+    for r in range(3):
+        valid = 0 <= y[r] < vr
+        e = oracle.backward_elements(x[r], cols, int(y[r]), float(grad[r]), f["lse"][r], vr,
+                                     valid=valid)
+        np.testing.assert_allclose(e, b["d64"][r, cols], rtol=1e-13, atol=1e-300)
