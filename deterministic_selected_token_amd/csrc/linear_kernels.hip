@@ -5,8 +5,9 @@
 // the tile in 16 sub-blocks of 256 columns; for each it forms the 128 x 256 logits block on the
 // matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension, the
 // hidden states and weight rows staged through double-buffered LDS with the next stage's
-// global loads in flight), reduces the block to a per-row (max, sum-exp) in registers with
-// a fixed lane tree, and folds it into the row's running tile state in LDS.  After the last
+// global loads in flight), reduces the block to a per-row (max, sum-exp) through LDS (each row
+// by 8 threads over 32 columns each, then a 3-level lane tree), and folds it into the row's
+// running tile state in LDS.  After the last
 // sub-block the tile's (m, s, sel) partial is written in logp.h's layout, and logp_merge
 // completes the forward.  The logits never leave the chip.
 //
@@ -42,17 +43,23 @@ constexpr int kChunksA = kBM * kBK / 8 / kThreads;  // 16-byte chunks per thread
 constexpr int kChunksB = kBN * kBK / 8 / kThreads;
 constexpr int kChunksPerRow = kBK / 8;
 
+// Sub-block reduction through LDS: half a row block (kBM / kTM rows) at a time, kRedThreads
+// threads per row, each reducing kRedCols columns.
+constexpr int kHalfRows = kWM * 32;
+constexpr int kRedThreads = kThreads / kHalfRows;     // 8
+constexpr int kRedCols = kBN / kRedThreads;           // 32
+constexpr int kRedRow = kBN + 32;                     // floats per LDS row (bank spread)
+
 static_assert(kChunksA * kThreads * 8 == kBM * kBK, "A stage is whole chunks per thread");
 static_assert(kChunksB * kThreads * 8 == kBN * kBK, "B stage is whole chunks per thread");
 static_assert(kTile % kBN == 0, "a vocab tile is whole sub-blocks");
+static_assert(kRedCols % 4 == 0 && kHalfRows * kRedThreads == kThreads, "reduction layout");
 
 // The stage arrays are 16-byte aligned so their 16-byte chunks move as single ds_read_b128 /
 // ds_write_b128 instructions.
 struct alignas(16) Smem {
     alignas(16) uint16_t a[2][kBM * kRow];  // hidden-state stage, [row][k]
     alignas(16) uint16_t b[2][kBN * kRow];  // weight stage, [vocab row][k]
-    float red_max[kWN][kBM];    // per-wave-column row maxima of the current sub-block
-    float red_sum[kWN][kBM];    // per-wave-column row sums
     float m[kBM], s[kBM], sel[kBM];  // running tile state per row
     int y_rel[kBM];             // target column inside this tile, or -1
 };
@@ -62,6 +69,9 @@ struct Stage {
     u32x4v a[kChunksA];
     u32x4v b[kChunksB];
 };
+
+static_assert(sizeof(float) * kHalfRows * kRedRow <= sizeof(Smem::a) + sizeof(Smem::b),
+              "the reduction area fits in the stage buffers");
 
 // Loads this thread's 16-byte chunks of one stage: hidden rows [row0, row0 + kBM) and weight
 // rows [col0, col0 + kBN) of the view, hidden elements [k0, k0 + kBK).  Out-of-range chunks
@@ -135,26 +145,6 @@ __device__ __forceinline__ void mma_stage(const Smem& sm, int buf, int wm, int w
     }
 }
 
-// Row (inside the workgroup's block) of accumulator register r of MFMA row-tile tm, for lane
-// `lane` of wave-row wm: the 32 x 32 result layout puts column (lane & 31) in a lane and
-// rows (r & 3) + 8 (r >> 2) + 4 (lane >> 5) in its 16 registers.
-__device__ __forceinline__ int acc_row(int wm, int tm, int r, int lane) {
-    return wm * (kTM * 32) + tm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-}
-
-// Max / sum over the 32 lanes of a half-wave (the lanes that hold one row of a 32-column
-// tile): pairwise tree over lane index, partners xor 1, 2, 4, 8, 16.
-__device__ __forceinline__ float half_max(float v) {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
-__device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) v = v + __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // 8 waves per workgroup (114 KB of LDS, one workgroup per CU): two waves per SIMD cover each
 // other's global-load latency.
 __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
@@ -213,63 +203,64 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
             __syncthreads();
         }
 
-        // ---- sub-block reduction: masked columns are -inf
-        bool col_ok[kTN];
-        int col_in_tile[kTN];
+        // ---- sub-block reduction through LDS (the stage buffers are free now), one half of
+        // the row block at a time: each wave writes its accumulators (masked columns as -inf),
+        // then 8 threads per row reduce 32 columns each and combine by a 3-level lane tree.
+        float* red = reinterpret_cast<float*>(&sm.a[0][0]);
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-            col_in_tile[j] = sb * kBN + wn * (kTN * 32) + j * 32 + (lane & 31);
-            col_ok[j] = tile_col0 + col_in_tile[j] < lim;
-        }
+        for (int i = 0; i < kTM; ++i) {
 #pragma unroll
-        for (int i = 0; i < kTM; ++i)
+            for (int j = 0; j < kTN; ++j) {
+                const int col = wn * (kTN * 32) + j * 32 + (lane & 31);  // in the sub-block
+                const bool ok = tile_col0 + sb * kBN + col < lim;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float v = kNegInf;
-#pragma unroll
-                for (int j = 0; j < kTN; ++j) v = fmaxf(v, col_ok[j] ? acc[i][j][r] : kNegInf);
-                v = half_max(v);
-                const int row = acc_row(wm, i, r, lane);
-                if ((lane & 31) == 0) sm.red_max[wn][row] = v;
-                const int yr = sm.y_rel[row];
-#pragma unroll
-                for (int j = 0; j < kTN; ++j)
-                    if (col_ok[j] && yr == col_in_tile[j]) sm.sel[row] = acc[i][j][r];
+                for (int r = 0; r < 16; ++r) {
+                    const int hr = wm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+                    red[hr * kRedRow + col] = ok ? acc[i][j][r] : kNegInf;
+                }
             }
-        __syncthreads();
+            __syncthreads();
+            {
+                const int t = threadIdx.x;
+                const int hr = t / kRedThreads, part = t % kRedThreads;
+                const int row = (hr / 32) * (kTM * 32) + i * 32 + (hr % 32);  // in the block
+                float v[kRedCols];
 #pragma unroll
-        for (int i = 0; i < kTM; ++i)
+                for (int q = 0; q < kRedCols / 4; ++q) {
+                    const float4 x = *reinterpret_cast<const float4*>(
+                        &red[hr * kRedRow + 4 * part + kRedThreads * 4 * q]);
+                    v[4 * q] = x.x;
+                    v[4 * q + 1] = x.y;
+                    v[4 * q + 2] = x.z;
+                    v[4 * q + 3] = x.w;
+                }
+                const int yr = sm.y_rel[row] - sb * kBN;  // target column in the sub-block
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = acc_row(wm, i, r, lane);
-                float mb = sm.red_max[0][row];
+                for (int q = 0; q < kRedCols; ++q)
+                    if (yr == 4 * part + kRedThreads * 4 * (q / 4) + (q % 4)) sm.sel[row] = v[q];
+                float mb = v[0];
 #pragma unroll
-                for (int q = 1; q < kWN; ++q) mb = fmaxf(mb, sm.red_max[q][row]);
+                for (int q = 1; q < kRedCols; ++q) mb = fmaxf(mb, v[q]);
+#pragma unroll
+                for (int o = 1; o < kRedThreads; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o, kWave));
                 float ls = 0.0f;
                 if (mb != kNegInf) {
 #pragma unroll
-                    for (int j = 0; j < kTN; ++j)
-                        ls = ls + (col_ok[j] ? fwd_exp(acc[i][j][r] - mb) : 0.0f);
+                    for (int q = 0; q < kRedCols; ++q)
+                        ls = ls + (v[q] == kNegInf ? 0.0f : fwd_exp(v[q] - mb));
                 }
-                ls = half_sum(ls);
-                if ((lane & 31) == 0) sm.red_sum[wn][row] = ls;
-            }
-        __syncthreads();
-        if (threadIdx.x < kBM) {
-            const int t = threadIdx.x;
-            float mb = sm.red_max[0][t];
-            float sb_sum = 0.0f;
 #pragma unroll
-            for (int q = 0; q < kWN; ++q) {
-                mb = fmaxf(mb, sm.red_max[q][t]);
-                sb_sum = sb_sum + sm.red_sum[q][t];
+                for (int o = 1; o < kRedThreads; o <<= 1) ls = ls + __shfl_xor(ls, o, kWave);
+                if (part == 0) {
+                    const float m_old = sm.m[row];
+                    const float m_new = fmaxf(m_old, mb);
+                    const float a = m_old == kNegInf ? 0.0f : sm.s[row] * fwd_exp(m_old - m_new);
+                    const float b = mb == kNegInf ? 0.0f : ls * fwd_exp(mb - m_new);
+                    sm.m[row] = m_new;
+                    sm.s[row] = a + b;
+                }
             }
-            const float m_old = sm.m[t];
-            const float m_new = fmaxf(m_old, mb);
-            const float a = m_old == kNegInf ? 0.0f : sm.s[t] * fwd_exp(m_old - m_new);
-            const float b = mb == kNegInf ? 0.0f : sb_sum * fwd_exp(mb - m_new);
-            sm.m[t] = m_new;
-            sm.s[t] = a + b;
+            __syncthreads();
         }
         // the next sub-block's first barrier orders these LDS updates before any reuse
     }

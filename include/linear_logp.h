@@ -17,8 +17,10 @@
  *              sequence of v_mfma_f32_32x32x16_bf16 steps, k = 0, 16, 32, ... (hidden sizes
  *              that are not a multiple of 32 are padded with zeros);
  *   each 4096-column global tile is reduced in 16 sub-blocks of 256 columns; a sub-block
- *   gives (m_b, s_b) with m_b its max and s_b = sum exp(z - m_b) added in a fixed lane
- *   order; the tile's (m_l, s_l) folds the sub-blocks in order, b = 0 .. 15:
+ *   gives (m_b, s_b) with m_b its max and s_b = sum exp(z - m_b): 8 partial sums over the
+ *   sub-block's columns 4p + 32q + e (p = 0..7; q = 0..7 then e = 0..3, in that order, from +0)
+ *   combined by a pairwise tree (p xor 1, 2, 4); the tile's (m_l, s_l) folds the sub-blocks
+ *   in order, b = 0 .. 15:
  *   m <- max(m, m_b), s <- s exp(m_old - m) + s_b exp(m_b - m) (terms of -inf maxima are 0);
  *   sel_l = z[t, y_t] in the owner tile of a valid row, 0 elsewhere.  exp is the logp
  *   forward's (2^(t log2 e) on the hardware exp2).
