@@ -1,15 +1,15 @@
 // gfx950 kernel and C entry point of the fused LM-head + selected-token log-probability
 // (include/linear_logp.h).
 //
-// One workgroup (8 waves) per (block of 128 rows, global vocab tile of 4096 columns).  It walks
-// the tile in 16 sub-blocks of 256 columns; for each it forms the 128 x 256 logits block on the
-// matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension, the
-// hidden states and weight rows staged through double-buffered LDS with the next stage's
-// global loads in flight), reduces the block to a per-row (max, sum-exp) through LDS (each row
-// by 8 threads over 32 columns each, then a 3-level lane tree), and folds it into the row's
-// running tile state in LDS.  After the last
-// sub-block the tile's (m, s, sel) partial is written in logp.h's layout, and logp_merge
-// completes the forward.  The logits never leave the chip.
+// One workgroup (8 waves) per (block of 256 rows, global vocab tile of 4096 columns).  It walks
+// the tile in 16 sub-blocks of 256 columns; for each it forms the 256 x 256 logits block on the
+// matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension; each
+// wave holds a 64 x 128 block; the hidden states and weight rows are staged through
+// double-buffered LDS with the next stage's global loads in flight), reduces the block to a
+// per-row (max, sum-exp) through LDS (half the rows at a time, 4 threads per row over 64
+// columns each, then a 2-level lane tree), and folds it into the row's running tile state in
+// LDS.  After the last sub-block the tile's (m, s, sel) partial is written in logp.h's layout,
+// and logp_merge completes the forward.  The logits never leave the chip.
 //
 // Sources: PR #495 (Summary) names the fused LM-head + logp op; issue #241 ("PR 3", "PR6")
 // and PR #314 (Tensor Parallel doc) fix the per-tile partials and their merge.
@@ -31,8 +31,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kWM = 2, kWN = 4;               // waves along rows / columns
-constexpr int kTM = 2, kTN = 2;               // 32 x 32 MFMA tiles per wave along rows / cols
+constexpr int kWM = 4, kWN = 2;               // waves along rows / columns
+constexpr int kTM = 2, kTN = 4;               // 32 x 32 MFMA tiles per wave along rows / cols
 constexpr int kThreads = kWM * kWN * kWave;   // 512
 constexpr int kBM = kWM * kTM * 32;           // rows per workgroup
 constexpr int kBN = kWN * kTN * 32;           // columns per sub-block
@@ -73,33 +73,31 @@ struct Stage {
 static_assert(sizeof(float) * kHalfRows * kRedRow <= sizeof(Smem::a) + sizeof(Smem::b),
               "the reduction area fits in the stage buffers");
 
-// Loads this thread's 16-byte chunks of one stage: hidden rows [row0, row0 + kBM) and weight
-// rows [col0, col0 + kBN) of the view, hidden elements [k0, k0 + kBK).  Out-of-range chunks
-// (rows >= n, weight rows >= lim, k >= H) are zero.
-__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ h, int64_t ld_h,
-                                           int64_t n, const uint16_t* __restrict__ w, int64_t ld_w,
-                                           int lim, int H, int64_t row0, int col0, int k0,
+// Loads this thread's 16-byte chunks of one stage: rows [0, kBM) of the hidden-state block at
+// `hb` (n_here of them real) and rows [col0, col0 + kBN) of the weight tile at `wb` (lim_here
+// real), hidden elements [k0, k0 + kBK); out-of-range chunks are zero.  Offsets from the two
+// wave-uniform bases are 32-bit.
+__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ hb, uint32_t ld_h,
+                                           int n_here, const uint16_t* __restrict__ wb,
+                                           uint32_t ld_w, int lim_here, int H, int col0, int k0,
                                            Stage& st) {
-    u32x4v (&ra)[kChunksA] = st.a;
-    u32x4v (&rb)[kChunksB] = st.b;
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kChunksA; ++i) {
         const int q = t + i * kThreads;
         const int r = q / kChunksPerRow, k = k0 + (q % kChunksPerRow) * 8;
-        const int64_t row = row0 + r;
-        ra[i] = (row < n && k < H)
-                    ? *reinterpret_cast<const u32x4v*>(h + row * ld_h + k)
-                    : u32x4v{0u, 0u, 0u, 0u};
+        st.a[i] = (r < n_here && k < H)
+                      ? *reinterpret_cast<const u32x4v*>(hb + (uint32_t(r) * ld_h + uint32_t(k)))
+                      : u32x4v{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < kChunksB; ++i) {
         const int q = t + i * kThreads;
         const int r = q / kChunksPerRow, k = k0 + (q % kChunksPerRow) * 8;
         const int col = col0 + r;
-        rb[i] = (col < lim && k < H)
-                    ? *reinterpret_cast<const u32x4v*>(w + int64_t(col) * ld_w + k)
-                    : u32x4v{0u, 0u, 0u, 0u};
+        st.b[i] = (col < lim_here && k < H)
+                      ? *reinterpret_cast<const u32x4v*>(wb + (uint32_t(col) * ld_w + uint32_t(k)))
+                      : u32x4v{0u, 0u, 0u, 0u};
     }
 }
 
@@ -145,7 +143,7 @@ __device__ __forceinline__ void mma_stage(const Smem& sm, int buf, int wm, int w
     }
 }
 
-// 8 waves per workgroup (114 KB of LDS, one workgroup per CU): two waves per SIMD cover each
+// 8 waves per workgroup (148 KB of LDS, one workgroup per CU): two waves per SIMD cover each
 // other's global-load latency.
 __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
@@ -177,9 +175,16 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
         sm.sel[t] = 0.0f;
     }
 
+    // wave-uniform bases of the row block and of the tile's weight rows
+    const uint16_t* hb = h + row0 * ld_h;
+    const uint16_t* wb = w + int64_t(tile_col0) * ld_w;
+    const int n_here = static_cast<int>(std::min<int64_t>(kBM, n - row0));
+    const int lim_here = lim - tile_col0;  // real weight rows of the tile (may exceed kTile)
+    const uint32_t ldh = static_cast<uint32_t>(ld_h), ldw = static_cast<uint32_t>(ld_w);
+
     const int nk = (H + kBK - 1) / kBK;
     for (int sb = 0; sb < kSubBlocks; ++sb) {
-        const int col0 = tile_col0 + sb * kBN;  // first view column of the sub-block
+        const int col0 = sb * kBN;  // first column of the sub-block inside the tile
         f32x16 acc[kTM][kTN];
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
@@ -191,13 +196,13 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
         // The global loads of stage kt + 1 are issued before the matrix-core work of stage
         // kt and go to the other LDS buffer after it.
         Stage rs;
-        load_stage(h, ld_h, n, w, ld_w, lim, H, row0, col0, 0, rs);
+        load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, 0, rs);
         store_stage(sm, 0, rs);
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
             if (kt + 1 < nk)
-                load_stage(h, ld_h, n, w, ld_w, lim, H, row0, col0, (kt + 1) * kBK, rs);
+                load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, (kt + 1) * kBK, rs);
             mma_stage(sm, cur, wm, wn, lane, acc);
             if (kt + 1 < nk) store_stage(sm, cur ^ 1, rs);
             __syncthreads();
@@ -224,30 +229,34 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
                 const int t = threadIdx.x;
                 const int hr = t / kRedThreads, part = t % kRedThreads;
                 const int row = (hr / 32) * (kTM * 32) + i * 32 + (hr % 32);  // in the block
-                float v[kRedCols];
+                // two passes over the row's columns in LDS (max, then the sum), so no row
+                // values stay in registers beside the accumulators of the other half
+                const int yr = sm.y_rel[row] - sb * kBN;  // target column in the sub-block
+                const float* src = &red[hr * kRedRow + 4 * part];
+                float mb = kNegInf;
 #pragma unroll
                 for (int q = 0; q < kRedCols / 4; ++q) {
-                    const float4 x = *reinterpret_cast<const float4*>(
-                        &red[hr * kRedRow + 4 * part + kRedThreads * 4 * q]);
-                    v[4 * q] = x.x;
-                    v[4 * q + 1] = x.y;
-                    v[4 * q + 2] = x.z;
-                    v[4 * q + 3] = x.w;
+                    const float4 x = *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
+                    mb = fmaxf(mb, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+                    const int c0 = 4 * part + kRedThreads * 4 * q;
+                    if (yr >= c0 && yr < c0 + 4) {
+                        const int e = yr - c0;
+                        sm.sel[row] = e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+                    }
                 }
-                const int yr = sm.y_rel[row] - sb * kBN;  // target column in the sub-block
-#pragma unroll
-                for (int q = 0; q < kRedCols; ++q)
-                    if (yr == 4 * part + kRedThreads * 4 * (q / 4) + (q % 4)) sm.sel[row] = v[q];
-                float mb = v[0];
-#pragma unroll
-                for (int q = 1; q < kRedCols; ++q) mb = fmaxf(mb, v[q]);
 #pragma unroll
                 for (int o = 1; o < kRedThreads; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o, kWave));
                 float ls = 0.0f;
                 if (mb != kNegInf) {
 #pragma unroll
-                    for (int q = 0; q < kRedCols; ++q)
-                        ls = ls + (v[q] == kNegInf ? 0.0f : fwd_exp(v[q] - mb));
+                    for (int q = 0; q < kRedCols / 4; ++q) {
+                        const float4 x =
+                            *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
+                        ls = ls + (x.x == kNegInf ? 0.0f : fwd_exp(x.x - mb));
+                        ls = ls + (x.y == kNegInf ? 0.0f : fwd_exp(x.y - mb));
+                        ls = ls + (x.z == kNegInf ? 0.0f : fwd_exp(x.z - mb));
+                        ls = ls + (x.w == kNegInf ? 0.0f : fwd_exp(x.w - mb));
+                    }
                 }
 #pragma unroll
                 for (int o = 1; o < kRedThreads; o <<= 1) ls = ls + __shfl_xor(ls, o, kWave);
@@ -299,8 +308,12 @@ logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h, int64_t
         return LOGP_ERR_NULL;
     const int64_t H = hidden_size;
     if (H < 1 || H > LINEAR_LOGP_MAX_HIDDEN || H % 8 != 0 || ld_h < H || ld_w < H ||
-        ld_h % 8 != 0 || ld_w % 8 != 0 || !aligned16(hidden) || !aligned16(weight))
+        ld_h % 8 != 0 || ld_w % 8 != 0 || ld_h > LINEAR_LOGP_MAX_LD ||
+        ld_w > LINEAR_LOGP_MAX_LD || !aligned16(hidden) || !aligned16(weight))
         return LOGP_ERR_SHAPE;
+    // in-kernel offsets from a row block's or a tile's first row are 32-bit
+    static_assert(uint64_t(kTile) * LINEAR_LOGP_MAX_LD < (uint64_t(1) << 32), "tile offsets");
+    static_assert(uint64_t(kBM) * LINEAR_LOGP_MAX_LD < (uint64_t(1) << 32), "block offsets");
     const int64_t width = col_end - col_begin;
     const int64_t view_tiles = ceil_div(width, kTile);
     if (ldp < view_tiles) return LOGP_ERR_SHAPE;

@@ -6,9 +6,9 @@ formed and reduced inside the HIP kernel; the merge is the log-probability libra
 ``logp_merge``.
 
 Tensor conventions:
-  * hidden: bfloat16 ``[n, H]`` with unit column stride (row stride a multiple of 8, start
-    16-byte aligned); weight: bfloat16 rows of the LM head ``[rows, H]`` (a vocab shard is a
-    row slice ``W[c0:c1]``); H a multiple of 8.
+  * hidden: bfloat16 ``[n, H]`` with unit column stride (row stride a multiple of 8 and at
+    most 262144, start 16-byte aligned); weight: bfloat16 rows of the LM head ``[rows, H]``
+    (a vocab shard is a row slice ``W[c0:c1]``); H a multiple of 8.
   * partials: float32 ``[n, L, 3]`` of (m_l, s_l, sel_l), ``L = logp_num_tiles(vocab_padded)``.
 """
 
@@ -24,6 +24,7 @@ from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _stream, logp_merg
 
 EXPORTED = ("linear_logp_partials",)
 MAX_HIDDEN = 65536
+MAX_LD = 262144
 
 _P, _I64 = ctypes.c_void_p, ctypes.c_int64
 _lib.linear_logp_partials.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64,

@@ -17,9 +17,9 @@
  *              sequence of v_mfma_f32_32x32x16_bf16 steps, k = 0, 16, 32, ... (hidden sizes
  *              that are not a multiple of 32 are padded with zeros);
  *   each 4096-column global tile is reduced in 16 sub-blocks of 256 columns; a sub-block
- *   gives (m_b, s_b) with m_b its max and s_b = sum exp(z - m_b): 8 partial sums over the
- *   sub-block's columns 4p + 32q + e (p = 0..7; q = 0..7 then e = 0..3, in that order, from +0)
- *   combined by a pairwise tree (p xor 1, 2, 4); the tile's (m_l, s_l) folds the sub-blocks
+ *   gives (m_b, s_b) with m_b its max and s_b = sum exp(z - m_b): 4 partial sums over the
+ *   sub-block's columns 4p + 16q + e (p = 0..3; q = 0..15 then e = 0..3, in that order, from
+ *   +0) combined by a pairwise tree (p xor 1, 2); the tile's (m_l, s_l) folds the sub-blocks
  *   in order, b = 0 .. 15:
  *   m <- max(m, m_b), s <- s exp(m_old - m) + s_b exp(m_b - m) (terms of -inf maxima are 0);
  *   sel_l = z[t, y_t] in the owner tile of a valid row, 0 elsewhere.  exp is the logp
@@ -40,6 +40,7 @@ extern "C" {
 #endif
 
 #define LINEAR_LOGP_MAX_HIDDEN 65536  /* largest hidden size H */
+#define LINEAR_LOGP_MAX_LD 262144      /* largest row stride of hidden and weight (elements) */
 
 /* Per-tile partials of the logits h W^T over the vocabulary columns [col_begin, col_end).
  *   hidden        [n, ld_h] BF16 bits; row t at hidden + t*ld_h; H = hidden_size columns used.
@@ -47,8 +48,9 @@ extern "C" {
  *                 weight + (v - col_begin)*ld_w, H columns used.  Rows at or beyond vocab_real
  *                 are never read (they count as -inf logits, like padding columns).
  *   hidden_size   H, 1 <= H <= LINEAR_LOGP_MAX_HIDDEN, a multiple of 8.
- *   ld_h, ld_w    row strides in elements, >= H and multiples of 8; hidden and weight must
- *                 be 16-byte aligned (else LOGP_ERR_SHAPE).
+ *   ld_h, ld_w    row strides in elements, >= H, multiples of 8 and at most
+ *                 LINEAR_LOGP_MAX_LD; hidden and weight must be 16-byte aligned (else
+ *                 LOGP_ERR_SHAPE).
  *   vocab_real, vocab_padded, col_begin, col_end, targets, active, ignore_index, partials,
  *   ldp           exactly as in logp_partials: col_begin a multiple of LOGP_TILE_COLS, col_end
  *                 one too or vocab_padded; partials points at the slot of tile

@@ -31,6 +31,7 @@ def test_header_constant():
     text = open(os.path.join(ROOT, "include", "linear_logp.h")).read()
     assert int(re.search(r"#define LINEAR_LOGP_MAX_HIDDEN (\d+)", text).group(1)) == \
         linear.MAX_HIDDEN
+    assert int(re.search(r"#define LINEAR_LOGP_MAX_LD (\d+)", text).group(1)) == linear.MAX_LD
 
 
 @pytest.mark.parametrize("over,want", [
@@ -42,6 +43,7 @@ def test_header_constant():
                                                                      ld_w=65544), SHAPE),
     (dict(ld_h=60), SHAPE), (dict(ld_w=68), SHAPE), (dict(ld_h=72, H=72, ld_w=71), SHAPE),
     (dict(h=U), SHAPE), (dict(w=U), SHAPE), (dict(ldp=1), SHAPE),
+    (dict(ld_h=262152), SHAPE), (dict(ld_w=262152), SHAPE),
 ], ids=lambda v: str(v))
 def test_linear_partials_host_validation(over, want):
     assert call(**over) == want
