@@ -17,6 +17,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "host_common.hpp"
 #include "linear_logp.h"
@@ -145,11 +146,15 @@ __device__ __forceinline__ void mma_stage(const Smem& sm, int buf, int wm, int w
 
 // 8 waves per workgroup (148 KB of LDS, one workgroup per CU): two waves per SIMD cover each
 // other's global-load latency.
+// SCALED = false is the unit temperature: the multiply by inv_t (exact at 1) is left out, as
+// it lengthens the epilogue, which no matrix-core work overlaps.
+template <bool SCALED>
 __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
     const uint16_t* __restrict__ w, int64_t ld_w, int lim, int row_blocks, int64_t col_begin,
-    int64_t vocab_real, const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
-    int64_t ignore_index, logp_partial_t* __restrict__ partials, int64_t ldp) {
+    int64_t vocab_real, float inv_t, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ active, int64_t ignore_index,
+    logp_partial_t* __restrict__ partials, int64_t ldp) {
     __shared__ Smem sm;
     const int rb_idx = static_cast<int>(blockIdx.x % static_cast<uint32_t>(row_blocks));
     const int tile = static_cast<int>(blockIdx.x / static_cast<uint32_t>(row_blocks));
@@ -209,7 +214,8 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
         }
 
         // ---- sub-block reduction through LDS (the stage buffers are free now), one half of
-        // the row block at a time: each wave writes its accumulators (masked columns as -inf),
+        // the row block at a time: each wave writes its scored accumulators
+        // fl32(acc * inv_t) (masked columns as -inf; inv_t = 1 leaves acc unchanged),
         // then 8 threads per row reduce 32 columns each and combine by a 3-level lane tree.
         float* red = reinterpret_cast<float*>(&sm.a[0][0]);
 #pragma unroll
@@ -221,7 +227,8 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int hr = wm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-                    red[hr * kRedRow + col] = ok ? acc[i][j][r] : kNegInf;
+                    const float z = SCALED ? acc[i][j][r] * inv_t : acc[i][j][r];
+                    red[hr * kRedRow + col] = ok ? z : kNegInf;
                 }
             }
             __syncthreads();
@@ -291,12 +298,14 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
 
 extern "C" {
 
-logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h, int64_t n,
-                                   int64_t hidden_size, const uint16_t* weight, int64_t ld_w,
-                                   int64_t vocab_real, int64_t vocab_padded, int64_t col_begin,
-                                   int64_t col_end, const int64_t* targets, const uint8_t* active,
-                                   int64_t ignore_index, logp_partial_t* partials, int64_t ldp,
-                                   hipStream_t stream) {
+logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hidden,
+                                      int64_t ld_h, int64_t n, int64_t hidden_size,
+                                      const uint16_t* weight, int64_t ld_w, int64_t vocab_real,
+                                      int64_t vocab_padded, int64_t col_begin, int64_t col_end,
+                                      const int64_t* targets, const uint8_t* active,
+                                      int64_t ignore_index, logp_partial_t* partials,
+                                      int64_t ldp, hipStream_t stream) {
+    if (!(inv_temperature > 0.0f) || !std::isfinite(inv_temperature)) return LOGP_ERR_ARG;
     if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
         vocab_padded > (int64_t(1) << 31) - 1 - kTile)
         return LOGP_ERR_SHAPE;
@@ -334,11 +343,25 @@ logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h, int64_t
     if (row_blocks * view_tiles > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
     int Hi = static_cast<int>(H), lim_i = static_cast<int>(lim);
     int rbk = static_cast<int>(row_blocks);
-    void* args[] = {&hidden, &ld_h, &n, &Hi, &weight, &ld_w, &lim_i, &rbk, &col_begin,
-                    &vocab_real, &targets, &active, &ignore_index, &partials, &ldp};
-    return launch(reinterpret_cast<const void*>(&linear_partials_kernel),
-                  dim3(static_cast<uint32_t>(row_blocks * view_tiles)), dim3(kThreads), args, 0,
-                  stream);
+    void* args[] = {&hidden,    &ld_h,       &n,     &Hi,     &weight,       &ld_w,
+                    &lim_i,     &rbk,        &col_begin,     &vocab_real,   &inv_temperature,
+                    &targets,   &active,     &ignore_index,  &partials,     &ldp};
+    const void* kernel = inv_temperature == 1.0f
+                             ? reinterpret_cast<const void*>(&linear_partials_kernel<false>)
+                             : reinterpret_cast<const void*>(&linear_partials_kernel<true>);
+    return launch(kernel, dim3(static_cast<uint32_t>(row_blocks * view_tiles)), dim3(kThreads),
+                  args, 0, stream);
+}
+
+logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h, int64_t n,
+                                   int64_t hidden_size, const uint16_t* weight, int64_t ld_w,
+                                   int64_t vocab_real, int64_t vocab_padded, int64_t col_begin,
+                                   int64_t col_end, const int64_t* targets, const uint8_t* active,
+                                   int64_t ignore_index, logp_partial_t* partials, int64_t ldp,
+                                   hipStream_t stream) {
+    return linear_logp_partials_ex(1.0f, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
+                                   vocab_padded, col_begin, col_end, targets, active,
+                                   ignore_index, partials, ldp, stream);
 }
 
 }  // extern "C"

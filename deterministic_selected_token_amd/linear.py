@@ -22,7 +22,7 @@ import torch
 from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _stream, logp_merge,
                logp_num_tiles)
 
-EXPORTED = ("linear_logp_partials",)
+EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex")
 MAX_HIDDEN = 65536
 MAX_LD = 262144
 
@@ -30,6 +30,8 @@ _P, _I64 = ctypes.c_void_p, ctypes.c_int64
 _lib.linear_logp_partials.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64,
                                       _P, _P, _I64, _P, _I64, _P]
 _lib.linear_logp_partials.restype = ctypes.c_int32
+_lib.linear_logp_partials_ex.argtypes = [ctypes.c_float] + _lib.linear_logp_partials.argtypes
+_lib.linear_logp_partials_ex.restype = ctypes.c_int32
 
 
 def _bf16_rows(name: str, t: torch.Tensor, device=None) -> torch.Tensor:
@@ -49,9 +51,10 @@ def _row_stride(t: torch.Tensor) -> int:
 def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
                          vocab_real: int, vocab_padded: int, col_begin: int, col_end: int,
                          partials: torch.Tensor, active=None, ignore_index: int = -100,
-                         stream=None) -> torch.Tensor:
-    """Write the (m, s, sel) partials of vocab columns [col_begin, col_end) of h W^T into the
-    full ``partials`` buffer; ``weight`` is the row slice W[col_begin:col_end]."""
+                         stream=None, inv_temperature: float = 1.0) -> torch.Tensor:
+    """Write the (m, s, sel) partials of vocab columns [col_begin, col_end) of the scored
+    logits fl32(h W^T * inv_temperature) into the full ``partials`` buffer; ``weight`` is the
+    row slice W[col_begin:col_end].  inv_temperature = 1 calls the plain entry point."""
     hidden = _bf16_rows("hidden", hidden)
     dev = hidden.device
     weight = _bf16_rows("weight", weight, dev)
@@ -71,11 +74,14 @@ def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: to
         raise ValueError(f"weight holds {weight.shape[0]} rows, the range needs {rows_needed}")
     first = partials[:, col_begin // TILE_COLS]
     ldp = partials.stride(0) // 3 if partials.stride(0) % 3 == 0 else -1
-    st = _lib.linear_logp_partials(
-        _ptr(hidden), _row_stride(hidden), n, H, _ptr(weight), _row_stride(weight),
-        int(vocab_real), int(vocab_padded), int(col_begin), int(col_end), _ptr(targets),
-        _ptr(active), int(ignore_index), first.data_ptr(), ldp, _stream(dev, stream))
-    _check("linear_logp_partials", st)
+    args = (_ptr(hidden), _row_stride(hidden), n, H, _ptr(weight), _row_stride(weight),
+            int(vocab_real), int(vocab_padded), int(col_begin), int(col_end), _ptr(targets),
+            _ptr(active), int(ignore_index), first.data_ptr(), ldp, _stream(dev, stream))
+    if inv_temperature == 1.0:
+        _check("linear_logp_partials", _lib.linear_logp_partials(*args))
+    else:
+        _check("linear_logp_partials_ex",
+               _lib.linear_logp_partials_ex(float(inv_temperature), *args))
     return partials
 
 
@@ -84,9 +90,11 @@ def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: tor
                         active=None, ignore_index: int = -100,
                         partials: Optional[torch.Tensor] = None,
                         logp: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                        stats: Optional[torch.Tensor] = None, stream=None):
-    """logp, LSE and (M, S) of the logits h W^T over the whole vocabulary:
-    linear_logp_partials over all tiles, then logp_merge -> (logp, lse, stats)."""
+                        stats: Optional[torch.Tensor] = None, stream=None,
+                        inv_temperature: float = 1.0):
+    """logp, LSE and (M, S) of the scored logits fl32(h W^T * inv_temperature) over the
+    whole vocabulary: linear_logp_partials over all tiles, then logp_merge -> (logp, lse,
+    stats)."""
     vocab_padded = weight.shape[0] if vocab_padded is None else int(vocab_padded)
     vocab_real = vocab_padded if vocab_real is None else int(vocab_real)
     n = hidden.shape[0]
@@ -94,7 +102,8 @@ def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: tor
     if partials is None:
         partials = torch.empty((n, L, 3), dtype=torch.float32, device=hidden.device)
     linear_logp_partials(hidden, weight, targets, vocab_real, vocab_padded, 0, vocab_padded,
-                         partials, active=active, ignore_index=ignore_index, stream=stream)
+                         partials, active=active, ignore_index=ignore_index, stream=stream,
+                         inv_temperature=inv_temperature)
     return logp_merge(partials, targets, vocab_real, num_tiles=L, active=active,
                       ignore_index=ignore_index, logp=logp, lse=lse, stats=stats,
                       stream=stream)

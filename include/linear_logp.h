@@ -66,6 +66,23 @@ LOGP_API logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h
                                             logp_partial_t* partials, int64_t ldp,
                                             hipStream_t stream);
 
+/* linear_logp_partials with temperature-scaled scoring (PR #314 "[WS2][Logp] Deterministic
+ * config option", Numerical contract: rollout and trainer score the same logits at
+ * temperatures such as 1.0 and 0.7).  Each logit of the FP32 accumulation above is scored
+ * once, z = fl32(acc * inv_temperature), before any reduction; m_l, s_l and sel_l are those of
+ * the scored logits.  inv_temperature = 1/tau must be finite and > 0 (else LOGP_ERR_ARG).
+ * With inv_temperature = 1 the partials are bitwise those of linear_logp_partials, which calls
+ * this.  logp_merge then gives logp, LSE and (M, S) of the scored logits; logp_backward_ex
+ * with the same inv_temperature on materialised logits h W^T takes those stats. */
+LOGP_API logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hidden,
+                                               int64_t ld_h, int64_t n, int64_t hidden_size,
+                                               const uint16_t* weight, int64_t ld_w,
+                                               int64_t vocab_real, int64_t vocab_padded,
+                                               int64_t col_begin, int64_t col_end,
+                                               const int64_t* targets, const uint8_t* active,
+                                               int64_t ignore_index, logp_partial_t* partials,
+                                               int64_t ldp, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,19 +54,25 @@ def logit_abs(hidden, weight, vocab_real: Optional[int] = None) -> np.ndarray:
 
 
 def forward(hidden, weight, targets, vocab_real: int, active=None, ignore_index: int = -100,
-            lib=None) -> dict:
-    """logp, LSE, M, S (float64) of the logits h W^T, as ``oracle.forward`` defines them."""
+            lib=None, inv_temperature: float = 1.0) -> dict:
+    """logp, LSE, M, S (float64) of the logits h W^T, as ``oracle.forward`` defines them;
+    with inv_temperature the scored logits are z * inv_temperature (one float64 product with
+    the float32 value of inv_temperature, PR #314's temperature-scaled scoring)."""
     z = np.ascontiguousarray(logits(hidden, weight, vocab_real))
-    out = _forward(z, targets, vocab_real, active=active, ignore_index=ignore_index, lib=lib)
+    out = _forward(z, targets, vocab_real, active=active, ignore_index=ignore_index, lib=lib,
+                   inv_temperature=inv_temperature)
     out["logits"] = z
     return out
 
 
 def tile_partials(hidden, weight, targets, vocab_real: int, vocab_padded: int, tile: int = 4096,
-                  active=None, ignore_index: int = -100, lib=None) -> dict:
-    """Per global tile (m_l, s_l, sel_l) of the logits h W^T (columns >= vocab_real masked)."""
+                  active=None, ignore_index: int = -100, lib=None,
+                  inv_temperature: float = 1.0) -> dict:
+    """Per global tile (m_l, s_l, sel_l) of the logits h W^T scored by inv_temperature
+    (columns >= vocab_real masked)."""
     z = logits(hidden, weight, vocab_real)
     zp = np.full((z.shape[0], vocab_padded), -np.inf)
     zp[:, :vocab_real] = z
     return _tile_partials(np.ascontiguousarray(zp), targets, vocab_real, vocab_padded,
-                          tile=tile, active=active, ignore_index=ignore_index, lib=lib)
+                          tile=tile, active=active, ignore_index=ignore_index, lib=lib,
+                          inv_temperature=inv_temperature)

@@ -4,7 +4,9 @@ contract (run to run, batch composition, vocab shards, padding).
 Tolerance, derived from the arithmetic: each logit is a float32 accumulation of H exact
 BF16 x BF16 products in H/16 matrix-core steps, so |z_gpu - z| <= (H/16 + 2) 2^-24 A_v with
 A_v = sum_k |h_k W_vk|.  logp = z_y - LSE then moves by at most twice the largest such bound
-of the row, plus the float32 rounding of the logp arithmetic (1e-6 relative).
+of the row, plus the float32 rounding of the logp arithmetic (1e-6 relative).  Scored at
+inv_temperature, each logit is that sum times inv_t rounded once more: the bound becomes
+inv_t ((H/16 + 2) 2^-24 A_v + 2^-24 |z_v|).
 """
 
 from __future__ import annotations
@@ -39,20 +41,23 @@ def make(n, H, V, Vp=None, seed=0, scale=3.0, ignore_frac=0.1, pad_value=float("
     return h.to(DEV), W.to(DEV), y.to(DEV)
 
 
-def check(h, W, y, V, Vp=None, rows=None, active=None):
+def check(h, W, y, V, Vp=None, rows=None, active=None, inv_t=1.0):
     from oracle import linear_oracle as LO
     Vp = V if Vp is None else Vp
-    logp, lse, stats = linear.linear_logp_forward(h, W, y, V, Vp, active=active)
+    logp, lse, stats = linear.linear_logp_forward(h, W, y, V, Vp, active=active,
+                                                  inv_temperature=inv_t)
     torch.cuda.synchronize()
     rows = np.arange(h.shape[0]) if rows is None else np.asarray(rows)
     hc = h.cpu()[rows]
     Wc = W.cpu()[:V]
     yc = y.cpu().numpy()[rows]
     act = None if active is None else active.cpu().numpy()[rows]
-    ref = LO.forward(hc, Wc, yc, V, active=act)
+    ref = LO.forward(hc, Wc, yc, V, active=act, inv_temperature=inv_t)
     A = LO.logit_abs(hc, Wc, V)
     H = h.shape[1]
-    bound = (H / 16 + 2) * 2.0 ** -24 * A.max(axis=1)
+    it = float(np.float32(inv_t))
+    bound = it * ((H / 16 + 2) * 2.0 ** -24 * A.max(axis=1)
+                  + 2.0 ** -24 * np.abs(ref["logits"]).max(axis=1))
     lp = logp.cpu().numpy()[rows].astype(np.float64)
     ls = lse.cpu().numpy()[rows].astype(np.float64)
     fin = np.isfinite(ref["logp"])
@@ -163,3 +168,67 @@ def test_linear_partials_against_oracle_tiles():
     owner = ref["sel"] != 0
     assert np.all(np.abs(p[..., 2] - ref["sel"]) <= bound)
     assert np.all(p[..., 2][~owner] == 0)
+
+
+TEMPS = [1 / 0.7, 2.0, 0.25]
+
+
+@pytest.mark.parametrize("inv_t", TEMPS, ids=[f"inv_t{t:.4g}" for t in TEMPS])
+@pytest.mark.parametrize("n,H,V", [(130, 128, 5000), (200, 512, 12345)],
+                         ids=["n130_H128_V5000", "n200_H512_V12345"])
+def test_linear_temperature_parity(n, H, V, inv_t):
+    h, W, y = make(n, H, V, seed=n + V)
+    say(f"linear temperature n={n} H={H} V={V} inv_t={inv_t:.6g}")
+    res, _ = check(h, W, y, V, inv_t=inv_t)
+    say(f"inv_t={inv_t:.6g}: {res}")
+
+
+def _partials_ex(inv_t, h, W, y, V, Vp, partials):
+    """The C entry point linear_logp_partials_ex itself, also at inv_t = 1 (which the binding
+    routes to the plain entry point)."""
+    first = partials[:, 0]
+    st = linear._lib.linear_logp_partials_ex(
+        float(inv_t), h.data_ptr(), h.stride(0), h.shape[0], h.shape[1], W.data_ptr(),
+        W.stride(0), V, Vp, 0, Vp, y.data_ptr(), None, -100, first.data_ptr(),
+        partials.stride(0) // 3, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, st
+    return partials
+
+
+def test_linear_temperature_identities_are_bitwise():
+    """inv_t = 1 through the _ex entry point gives the plain partials; inv_t = 1/2 gives the
+    partials of the halved weight (halving is exact in BF16 and commutes with every FP32
+    rounding of the accumulation)."""
+    n, H, V = 300, 256, 3 * T + 77
+    h, W, y = make(n, H, V, seed=19)
+    say("linear temperature identities")
+    L = dst.logp_num_tiles(V)
+    plain = linear.linear_logp_partials(h, W, y, V, V, 0, V, torch.empty((n, L, 3), device=DEV))
+    one = _partials_ex(1.0, h, W, y, V, V, torch.empty((n, L, 3), device=DEV))
+    half = _partials_ex(0.5, h, W, y, V, V, torch.empty((n, L, 3), device=DEV))
+    Wh = (W.float() * 0.5).to(torch.bfloat16)
+    assert torch.equal((Wh.float() * 2).to(torch.bfloat16), W)
+    halved = linear.linear_logp_partials(h, Wh, y, V, V, 0, V, torch.empty((n, L, 3), device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(plain, one)
+    assert torch.equal(half, halved)
+    assert not torch.equal(half, plain)
+
+
+def test_linear_temperature_vocab_shards_are_bitwise():
+    n, H, V, Vp = 40, 128, 3 * T + 1000, 5 * T
+    h, W, y = make(n, H, V, Vp, seed=23, pad_value=0.0)
+    inv_t = 1 / 0.7
+    say("linear temperature vocab shards")
+    ref = linear.linear_logp_forward(h, W, y, V, Vp, inv_temperature=inv_t)
+    L = dst.logp_num_tiles(Vp)
+    for layout in ([2, 3], [1, 1, 2, 1]):
+        partials = torch.full((n, L, 3), float("nan"), device=DEV)
+        c0 = 0
+        for tiles in layout:
+            c1 = min(Vp, c0 + tiles * T)
+            linear.linear_logp_partials(h, W[c0:c1], y, V, Vp, c0, c1, partials,
+                                        inv_temperature=inv_t)
+            c0 = c1
+        got = dst.logp_merge(partials, y, V)
+        assert all(torch.equal(a, b) for a, b in zip(ref, got)), layout

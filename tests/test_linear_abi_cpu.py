@@ -1,4 +1,4 @@
-"""Host-side validation of linear_logp_partials (no GPU: every case fails before any HIP
+"""Host-side validation of linear_logp_partials(_ex) (no GPU: every case fails before any HIP
 call) and the constants the binding shares with include/linear_logp.h."""
 
 from __future__ import annotations
@@ -12,7 +12,7 @@ import pytest
 from deterministic_selected_token_amd import linear
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, SHARD = 0, 1, 2, 3
+OK, NULL, SHAPE, SHARD, ARG = 0, 1, 2, 3, 8
 A = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced
 U = ctypes.c_void_p(0x10002)  # misaligned
 lib = linear._lib
@@ -25,6 +25,28 @@ def call(**over):
     return lib.linear_logp_partials(a["h"], a["ld_h"], a["n"], a["H"], a["w"], a["ld_w"],
                                     a["vr"], a["vp"], a["c0"], a["c1"], a["y"], a["act"],
                                     a["ign"], a["p"], a["ldp"], None)
+
+
+def call_ex(inv_t, **over):
+    a = dict(h=A, ld_h=64, n=10, H=64, w=A, ld_w=64, vr=5000, vp=5000, c0=0, c1=5000, y=A,
+             act=None, ign=-100, p=A, ldp=2)
+    a.update(over)
+    return lib.linear_logp_partials_ex(inv_t, a["h"], a["ld_h"], a["n"], a["H"], a["w"],
+                                       a["ld_w"], a["vr"], a["vp"], a["c0"], a["c1"], a["y"],
+                                       a["act"], a["ign"], a["p"], a["ldp"], None)
+
+
+@pytest.mark.parametrize("inv_t", [0.0, -0.0, -1.0, float("inf"), float("-inf"), float("nan")])
+def test_linear_partials_ex_rejects_bad_temperature(inv_t):
+    assert call_ex(inv_t) == ARG
+    assert call_ex(inv_t, n=0) == ARG  # checked before anything else
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(n=-1), SHAPE), (dict(c0=100), SHARD), (dict(n=0), OK), (dict(h=None), NULL),
+    (dict(w=U), SHAPE), (dict(ldp=1), SHAPE)], ids=lambda v: str(v))
+def test_linear_partials_ex_validates_like_the_plain_entry(over, want):
+    assert call_ex(1.0 / 0.7, **over) == want == call(**over)
 
 
 def test_header_constant():

@@ -107,8 +107,33 @@ def pin_linearity_and_orientation(o):
     assert z[2, 4] == sum(float(h1[2, k]) * float(W[4, k]) for k in range(4))
 
 
+def pin_temperature(o):
+    """Scoring at inv_temperature = 1/2 equals halving W (exact in BF16 and in float64), on the
+    forward and the tile partials; at 1/0.7 it is torch's float64 log_softmax of z times the
+    float32 value of 1/0.7."""
+    n, H, V = 7, 48, 700
+    h = rand_bf16((n, H), 5)
+    W = rand_bf16((V, H), 6, 0.5)
+    y = np.array([0, 1, 699, 350, 2, 698, 10])
+    half = (W.float() * 0.5).to(torch.bfloat16)
+    got = o.forward(h, W, y, V, inv_temperature=0.5)
+    want = o.forward(h, half, y, V)
+    for key in ("logp", "lse", "max", "sumexp"):
+        assert np.array_equal(got[key], want[key]), key
+    pg = o.tile_partials(h, W, y, V, 768, tile=256, inv_temperature=0.5)
+    pw = o.tile_partials(h, half, y, V, 768, tile=256)
+    for key in ("max", "sumexp", "sel"):
+        assert np.array_equal(pg[key], pw[key]), key
+    inv_t = float(np.float32(1 / 0.7))
+    got = o.forward(h, W, y, V, inv_temperature=1 / 0.7)
+    z = (h.double() @ W.double().T) * inv_t
+    ls = torch.log_softmax(z, dim=1)
+    np.testing.assert_allclose(got["logp"], ls[np.arange(n), y].numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["max"], z.max(1).values.numpy(), rtol=0, atol=0)
+
+
 PINS = [pin_one_hot_rows, pin_exact_accumulation, pin_torch_log_softmax,
-        pin_uniform_and_padding, pin_linearity_and_orientation]
+        pin_uniform_and_padding, pin_linearity_and_orientation, pin_temperature]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -121,6 +146,10 @@ MUTATIONS = [
      "    return (h.astype(np.float32) @ w[:v].T.astype(np.float32)).astype(np.float64)\n"),
     ("weight used untransposed", "    return h @ w[:v].T\n", "    return h @ w[:v, :v]\n"),
     ("vocabulary order reversed", "    return h @ w[:v].T\n", "    return h @ w[:v][::-1].T\n"),
+    ("temperature dropped from the forward",
+     "lib=lib,\n                   inv_temperature=inv_temperature)", "lib=lib)"),
+    ("temperature dropped from the tile partials",
+     "lib=lib,\n                          inv_temperature=inv_temperature)", "lib=lib)"),
     ("bf16 decoded with the wrong shift",
      "(a.astype(np.uint32) << 16).view(np.float32)",
      "(a.astype(np.uint32) << 15).view(np.float32)"),
