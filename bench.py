@@ -270,9 +270,11 @@ def grpo_oracle_rate(lp, old, ref, adv, mask, nbytes: int) -> dict:
 
 
 def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
-                vocab: int = 151936) -> dict:
+                vocab: int = 151936, inv_temperature: float = 1.0,
+                cpu_baseline: bool = True) -> dict:
     """linear_logp forward (linear_logp_partials + logp_merge) on n rows of a Qwen3-8B-shaped
-    LM head (hidden 4096, vocabulary 151936): 2 n V H flops on the matrix cores."""
+    LM head (hidden 4096, vocabulary 151936), logits scored at inv_temperature: 2 n V H flops
+    on the matrix cores."""
     import torch
 
     from deterministic_selected_token_amd import linear
@@ -291,7 +293,8 @@ def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        linear.linear_logp_partials(h, W, y, vocab, vocab, 0, vocab, partials, stream=stream)
+        linear.linear_logp_partials(h, W, y, vocab, vocab, 0, vocab, partials, stream=stream,
+                                    inv_temperature=inv_temperature)
         if ev is not None:
             ev[1].record(stream)
         dst.logp_merge(partials, y, vocab, logp=logp, lse=lse, stats=stats, stream=stream)
@@ -307,22 +310,26 @@ def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
     k_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
     m_ms = sum(b.elapsed_time(c) for _, b, c in evs) / steps
     flops = 2.0 * n * vocab * hidden
+    out = {"rows": n, "hidden": hidden, "vocab": vocab, "inv_temperature": inv_temperature,
+           "partials_ms": round(k_ms, 4), "merge_ms": round(m_ms, 4),
+           "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1),
+           "frac_of_bf16_peak": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if not cpu_baseline:
+        return out
     # the float64 oracle on a few of the same rows (numpy float64 matmul + the C log-softmax)
     from oracle import linear_oracle
 
     rows = 4
     h_host, w_host, y_host = h[:rows].cpu(), W.cpu(), y[:rows].cpu().numpy()
     t0 = time.perf_counter()
-    linear_oracle.forward(h_host, w_host, y_host, vocab)
+    linear_oracle.forward(h_host, w_host, y_host, vocab, inv_temperature=inv_temperature)
     dt = time.perf_counter() - t0
-    cpu = {"value": round(2.0 * rows * vocab * hidden / dt / 1e12, 4), "unit": "TFLOP/s",
-           "kind": "oracle", "cores": len(os.sched_getaffinity(0)),
-           "sample": f"{rows} of the {n} rows, float64 logits and log-softmax, {dt:.2f} s wall "
-                     "(including the float64 copy of W)"}
-    return {"rows": n, "hidden": hidden, "vocab": vocab, "partials_ms": round(k_ms, 4),
-            "merge_ms": round(m_ms, 4), "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1),
-            "frac_of_bf16_peak": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "cpu_baseline": cpu}
+    out["cpu_baseline"] = {
+        "value": round(2.0 * rows * vocab * hidden / dt / 1e12, 4), "unit": "TFLOP/s",
+        "kind": "oracle", "cores": len(os.sched_getaffinity(0)),
+        "sample": f"{rows} of the {n} rows, float64 logits and log-softmax, {dt:.2f} s wall "
+                  "(including the float64 copy of W)"}
+    return out
 
 
 def main() -> int:
@@ -433,6 +440,8 @@ def main() -> int:
         extra["variants"] = time_variants(dst, case, stream, args.steps)
         extra["variants"].update(time_grpo(dst, case, stream, args.steps))
         extra["variants"]["linear_logp_fwd"] = time_linear(dst, stream, max(3, args.steps // 4))
+        extra["variants"]["linear_logp_fwd_temperature_0.7"] = time_linear(
+            dst, stream, max(3, args.steps // 4), inv_temperature=1 / 0.7, cpu_baseline=False)
     if args.profile_copy:
         src = torch.empty(1 << 31, dtype=torch.int16, device=dev)  # 4 GiB
         dst_buf = torch.empty_like(src)

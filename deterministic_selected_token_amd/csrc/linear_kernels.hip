@@ -47,8 +47,8 @@ constexpr int kChunksPerRow = kBK / 8;
 // Sub-block reduction through LDS: half a row block (kBM / kTM rows) at a time, kRedThreads
 // threads per row, each reducing kRedCols columns.
 constexpr int kHalfRows = kWM * 32;
-constexpr int kRedThreads = kThreads / kHalfRows;     // 8
-constexpr int kRedCols = kBN / kRedThreads;           // 32
+constexpr int kRedThreads = kThreads / kHalfRows;     // 4
+constexpr int kRedCols = kBN / kRedThreads;           // 64
 constexpr int kRedRow = kBN + 32;                     // floats per LDS row (bank spread)
 
 static_assert(kChunksA * kThreads * 8 == kBM * kBK, "A stage is whole chunks per thread");
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
         // ---- sub-block reduction through LDS (the stage buffers are free now), one half of
         // the row block at a time: each wave writes its scored accumulators
         // fl32(acc * inv_t) (masked columns as -inf; inv_t = 1 leaves acc unchanged),
-        // then 8 threads per row reduce 32 columns each and combine by a 3-level lane tree.
+        // then 4 threads per row reduce 64 columns each and combine by a 2-level lane tree.
         float* red = reinterpret_cast<float*>(&sm.a[0][0]);
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
@@ -245,12 +245,10 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
                 for (int q = 0; q < kRedCols / 4; ++q) {
                     const float4 x = *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
                     mb = fmaxf(mb, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
-                    const int c0 = 4 * part + kRedThreads * 4 * q;
-                    if (yr >= c0 && yr < c0 + 4) {
-                        const int e = yr - c0;
-                        sm.sel[row] = e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
-                    }
                 }
+                // the selected logit: the thread whose columns hold the target picks it up
+                if (yr >= 0 && yr < kBN && ((yr >> 2) & (kRedThreads - 1)) == part)
+                    sm.sel[row] = red[hr * kRedRow + yr];
 #pragma unroll
                 for (int o = 1; o < kRedThreads; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o, kWave));
                 float ls = 0.0f;
