@@ -486,7 +486,7 @@ logp_status_t grpo_advantages(const float* rewards, int64_t n, int64_t group_siz
     logp_status_t st = check_buffers(in, 1, out, 1, stream, &dev, in[0]);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
-    if (!guard.ok()) return LOGP_ERR_DEVICE;
+    if (!guard.ok()) return LOGP_ERR_HIP;
     int64_t groups = n / group_size;
     const int64_t blocks = ceil_div(groups, kItemWaves);
     if (blocks > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
@@ -512,7 +512,7 @@ logp_status_t grpo_token_counts(const uint8_t* mask, int64_t n_seqs, int64_t seq
     st = check_buffers(in, 1, out, 1, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
-    if (!guard.ok()) return LOGP_ERR_DEVICE;
+    if (!guard.ok()) return LOGP_ERR_HIP;
     int64_t stride = 1;
     void* args[] = {&m, &ld, &width, &counts, &stride};
     return launch(count_kernel(m, ld), dim3(static_cast<uint32_t>(n_seqs)), dim3(kCountThreads),
@@ -540,7 +540,7 @@ logp_status_t grpo_loss(const float* logp, const float* old_logp, const float* r
     st = check_buffers(in, 5, out, 3, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
-    if (!guard.ok()) return LOGP_ERR_DEVICE;
+    if (!guard.ok()) return LOGP_ERR_HIP;
 
     Tokens tk{logp, old_logp, ref_logp, adv, mask, ld, static_cast<int>(seq_len)};
     Objective o = objective(params, ref_logp != nullptr);
@@ -623,7 +623,7 @@ logp_status_t grpo_loss_partials(const float* logp, const float* old_logp, const
     st = check_buffers(in, 6, out, 2, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
-    if (!guard.ok()) return LOGP_ERR_DEVICE;
+    if (!guard.ok()) return LOGP_ERR_HIP;
     const uint32_t grid = item_blocks(n_seqs, view_tiles);
     if (grid == 0) return LOGP_ERR_SHAPE;
     Tokens tk{logp, old_logp, ref_logp, adv, mask, ld, static_cast<int>(width)};
@@ -648,7 +648,7 @@ logp_status_t grpo_loss_merge(const grpo_partial_t* partials, int64_t ldp, int64
     logp_status_t st = check_buffers(in, 1, out, 1, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
-    if (!guard.ok()) return LOGP_ERR_DEVICE;
+    if (!guard.ok()) return LOGP_ERR_HIP;
     const uint32_t grid = static_cast<uint32_t>(ceil_div(n_seqs, kItemWaves));
     void* args[] = {&partials, &ldp, &n_seqs, &num_tiles, &seq_stats};
     return launch(reinterpret_cast<const void*>(&grpo_merge_kernel), dim3(grid),
@@ -668,7 +668,7 @@ logp_status_t grpo_loss_reduce(const grpo_partial_t* seq_stats, int64_t n_seqs,
     st = check_buffers(in, 1, out, 1, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
-    if (!guard.ok()) return LOGP_ERR_DEVICE;
+    if (!guard.ok()) return LOGP_ERR_HIP;
     int32_t mode = params->mode;
     float beta = params->beta;
     int64_t nt = params->norm_tokens, ns = params->norm_seqs;

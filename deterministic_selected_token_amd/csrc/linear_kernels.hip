@@ -336,7 +336,7 @@ logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hid
     logp_status_t st = check_buffers(in, 4, out, 1, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
-    if (!guard.ok()) return LOGP_ERR_DEVICE;
+    if (!guard.ok()) return LOGP_ERR_HIP;
     const int64_t row_blocks = ceil_div(n, kBM);
     if (row_blocks * view_tiles > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
     int Hi = static_cast<int>(H), lim_i = static_cast<int>(lim);

@@ -207,7 +207,8 @@ __device__ __forceinline__ void store8(typename DtInfo<D>::Storage* out, int c, 
     if (VEC && c + kVec <= width) {
         u32x4* p = reinterpret_cast<u32x4*>(out + c);
         __builtin_nontemporal_store(u32x4{q[0], q[1], q[2], q[3]}, p);
-        if constexpr (D == Dt::F32) __builtin_nontemporal_store(u32x4{q[4], q[5], q[6], q[7]}, p + 1);
+        if constexpr (D == Dt::F32)
+            __builtin_nontemporal_store(u32x4{q[4], q[5], q[6], q[7]}, p + 1);
         return;
     }
 #pragma unroll

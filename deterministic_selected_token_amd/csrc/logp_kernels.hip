@@ -325,7 +325,8 @@ __global__ __launch_bounds__(bwd_tile_waves<D>() * kWave) void bwd_kernel(
 #pragma unroll
             for (int e = 0; e < kVec; ++e) z[e] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < kLoads; ++k) store8<D, VEC_OUT>(out, base + k * kLoadStride, width, z);
+            for (int k = 0; k < kLoads; ++k)
+                store8<D, VEC_OUT>(out, base + k * kLoadStride, width, z);
             continue;
         }
         bool hit = false;
@@ -713,8 +714,9 @@ logp_status_t logp_merge(const logp_partial_t* partials, int64_t ldp, int64_t n,
                          int64_t num_tiles, int64_t vocab_real, const int64_t* targets,
                          const uint8_t* active, int64_t ignore_index, float* logp, float* lse,
                          logp_stats_t* stats, hipStream_t stream) {
-    if (n < 0 || vocab_real < 1 || vocab_real > kMaxCols || num_tiles < ceil_div(vocab_real, kTile) ||
-        num_tiles > ceil_div(kMaxCols, kTile) || ldp < num_tiles)
+    if (n < 0 || vocab_real < 1 || vocab_real > kMaxCols ||
+        num_tiles < ceil_div(vocab_real, kTile) || num_tiles > ceil_div(kMaxCols, kTile) ||
+        ldp < num_tiles)
         return LOGP_ERR_SHAPE;
     if (n == 0) return LOGP_OK;
     if (partials == nullptr || targets == nullptr || logp == nullptr) return LOGP_ERR_NULL;
