@@ -144,6 +144,31 @@ __device__ __forceinline__ void mma_stage(const Smem& sm, int buf, int wm, int w
     }
 }
 
+// acc += the 256 x 256 block of A B^T for rows [0, n_here) of `hb` and rows
+// [col0, col0 + kBN) of `wb` (rows at or past lim_here and hidden elements at or past H read
+// as zero), in nk stages of kBK hidden elements: the one fixed accumulation order of every
+// logit, shared by the forward and the backward's recomputation.  The global loads of stage
+// kt + 1 are issued before the matrix-core work of stage kt and go to the other LDS buffer
+// after it.  Ends with a barrier (the stage buffers are free afterwards).
+__device__ __forceinline__ void block_product(Smem& sm, const uint16_t* __restrict__ hb,
+                                              uint32_t ldh, int n_here,
+                                              const uint16_t* __restrict__ wb, uint32_t ldw,
+                                              int lim_here, int H, int col0, int nk, int wm,
+                                              int wn, int lane, f32x16 (&acc)[kTM][kTN]) {
+    Stage rs;
+    load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, 0, rs);
+    store_stage(sm, 0, rs);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk)
+            load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, (kt + 1) * kBK, rs);
+        mma_stage(sm, cur, wm, wn, lane, acc);
+        if (kt + 1 < nk) store_stage(sm, cur ^ 1, rs);
+        __syncthreads();
+    }
+}
+
 // 8 waves per workgroup (148 KB of LDS, one workgroup per CU): two waves per SIMD cover each
 // other's global-load latency.
 // SCALED = false is the unit temperature: the multiply by inv_t (exact at 1) is left out, as
@@ -198,20 +223,7 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        // The global loads of stage kt + 1 are issued before the matrix-core work of stage
-        // kt and go to the other LDS buffer after it.
-        Stage rs;
-        load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, 0, rs);
-        store_stage(sm, 0, rs);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk)
-                load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, (kt + 1) * kBK, rs);
-            mma_stage(sm, cur, wm, wn, lane, acc);
-            if (kt + 1 < nk) store_stage(sm, cur ^ 1, rs);
-            __syncthreads();
-        }
+        block_product(sm, hb, ldh, n_here, wb, ldw, lim_here, H, col0, nk, wm, wn, lane, acc);
 
         // ---- sub-block reduction through LDS (the stage buffers are free now), one half of
         // the row block at a time: each wave writes its scored accumulators
@@ -292,6 +304,193 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
     }
 }
 
+
+// ------------------------------------------------------------------------------ backward
+//
+// dz = g inv_t (onehot - softmax(z)) of the scored logits, recomputed block by block with the
+// forward's block_product (so z is bit for bit the forward's), written to a workspace in BF16
+// twice ([row][column] and [column][row]); then dh = dz W and dW = dz^T h as "TN" products
+// (both operands with the reduction index contiguous) on the same matrix-core path, W and h
+// transposed into the workspace first.  Every operand in the workspace is zero-padded to whole
+// 256 x 256 blocks, so the products need no load bounds.
+
+// Row constants of dz in LDS: sm.m = M, sm.s = -g'/S, sm.sel = that times 2^-64, g' = g inv_t
+// in `gsc`, and sm.y_rel = the target's column inside this sub-block, -1 when elsewhere, -2
+// for a row without gradient (padding, masked, ignored, out-of-range target, M = -inf).
+template <bool SCALED>
+__global__ __launch_bounds__(kThreads) void linear_dz_kernel(
+    const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
+    const uint16_t* __restrict__ w, int64_t ld_w, int lim, int row_blocks, int64_t chunk_col0,
+    int64_t vocab_real, float inv_t, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ active, int64_t ignore_index, const float* __restrict__ grad,
+    const logp_stats_t* __restrict__ stats, uint16_t* __restrict__ dz, int64_t ldz,
+    uint16_t* __restrict__ dzt, int64_t ldzt) {
+    __shared__ Smem sm;
+    __shared__ float gsc[kBM];
+    const int rb_idx = static_cast<int>(blockIdx.x % static_cast<uint32_t>(row_blocks));
+    const int sb = static_cast<int>(blockIdx.x / static_cast<uint32_t>(row_blocks));
+    const int64_t row0 = int64_t(rb_idx) * kBM;
+    const int col0 = sb * kBN;  // first column of the sub-block inside the chunk
+    const int lane = lane_id(), wave = wave_id();
+    const int wm = wave / kWN, wn = wave % kWN;
+
+    if (threadIdx.x < kBM) {
+        const int t = threadIdx.x;
+        const int64_t row = row0 + t;
+        int yr = -2;
+        float M = 0.0f, nc = 0.0f, gs = 0.0f;
+        if (row < n) {
+            int64_t y;
+            const logp_stats_t st = stats[row];
+            if (row_valid(targets, active, ignore_index, vocab_real, row, y) &&
+                st.max != kNegInf) {
+                gs = SCALED ? grad[row] * inv_t : grad[row];  // d z / d x = inv_t
+                M = st.max;
+                nc = -(gs / st.sumexp);
+                const int64_t c = y - chunk_col0 - col0;
+                yr = (c >= 0 && c < kBN) ? static_cast<int>(c) : -1;
+            }
+        }
+        sm.y_rel[t] = yr;
+        sm.m[t] = M;
+        sm.s[t] = nc;
+        sm.sel[t] = nc * 0x1p-64f;
+        gsc[t] = gs;
+    }
+
+    f32x16 acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int n_here = static_cast<int>(std::min<int64_t>(kBM, n - row0));
+    block_product(sm, h + row0 * ld_h, static_cast<uint32_t>(ld_h), n_here, w,
+                  static_cast<uint32_t>(ld_w), lim, H, col0, (H + kBK - 1) / kBK, wm, wn, lane,
+                  acc);
+
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int lc = col0 + wn * (kTN * 32) + j * 32 + (lane & 31);  // in the chunk
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int lr0 = wm * (kTM * 32) + i * 32 + 8 * q + 4 * (lane >> 5);
+                uint16_t out[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int lr = lr0 + e;
+                    const int yr = sm.y_rel[lr];
+                    float d = 0.0f;
+                    if (yr != -2 && lc < lim) {
+                        const float acc_v = acc[i][j][4 * q + e];
+                        const float z = SCALED ? acc_v * inv_t : acc_v;
+                        d = bwd_term_deep<true>(z, sm.m[lr], sm.s[lr], sm.sel[lr]);
+                        if (lc - col0 == yr) d = gsc[lr] + d;  // g' (1 - p)
+                    }
+                    out[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(d));
+                    dz[(row0 + lr) * ldz + lc] = out[e];
+                }
+                // the 4 rows are consecutive: one 8-byte store into the transposed copy
+                *reinterpret_cast<uint2*>(&dzt[int64_t(lc) * ldzt + row0 + lr0]) =
+                    make_uint2(uint32_t(out[0]) | (uint32_t(out[1]) << 16),
+                               uint32_t(out[2]) | (uint32_t(out[3]) << 16));
+            }
+        }
+    }
+}
+
+// c (=|+=) a b^T for one 256 x 256 block: a [m_pad, K] and b [n_pad, K] BF16 with K a
+// multiple of kBK and both zero-padded to whole blocks; FP32 results stored for
+// rows < m_real and columns < n_real.
+template <bool ACCUM>
+__global__ __launch_bounds__(kThreads) void gemm_tn_kernel(
+    const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ b, int64_t ldb,
+    int K, int m_real, int n_real, int m_blocks, float* __restrict__ c, int64_t ldc) {
+    __shared__ Smem sm;
+    const int mb = static_cast<int>(blockIdx.x % static_cast<uint32_t>(m_blocks));
+    const int nb = static_cast<int>(blockIdx.x / static_cast<uint32_t>(m_blocks));
+    const int64_t row0 = int64_t(mb) * kBM, col0 = int64_t(nb) * kBN;
+    const int lane = lane_id(), wave = wave_id();
+    const int wm = wave / kWN, wn = wave % kWN;
+    f32x16 acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    block_product(sm, a + row0 * lda, static_cast<uint32_t>(lda), kBM, b + col0 * ldb,
+                  static_cast<uint32_t>(ldb), kBN, K, 0, K / kBK, wm, wn, lane, acc);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int64_t col = col0 + wn * (kTN * 32) + j * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row =
+                    row0 + wm * (kTM * 32) + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+                if (row < m_real && col < n_real) {
+                    float* p = c + row * ldc + col;
+                    *p = ACCUM ? *p + acc[i][j][r] : acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
+constexpr int kTr = 64;  // transpose tile
+
+// dst[col][row] = src[row][col] for row < rows, col < cols (cols a multiple of 8, rows of src
+// 16-byte aligned); zero elsewhere in the [cols_pad, rows_pad] destination (both multiples of
+// kTr, covered by the grid).
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
+                                                       int64_t ld_src, int rows, int cols,
+                                                       uint16_t* __restrict__ dst,
+                                                       int64_t ld_dst) {
+    __shared__ uint32_t tile[kTr][kTr / 2 + 1];  // [row][column pair], padded against conflicts
+    const int64_t r0 = int64_t(blockIdx.y) * kTr, c0 = int64_t(blockIdx.x) * kTr;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = t + 256 * i;
+        const int r = q / 8, c8 = (q % 8) * 8;
+        u32x4v v = {0u, 0u, 0u, 0u};
+        if (r0 + r < rows && c0 + c8 < cols)
+            v = *reinterpret_cast<const u32x4v*>(src + (r0 + r) * ld_src + c0 + c8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[r][c8 / 2 + e] = v[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = t + 256 * i;
+        const int c = q / 8, r8 = (q % 8) * 8;
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = tile[r8 + 2 * e][c / 2] >> (16 * (c & 1));
+            const uint32_t hi = tile[r8 + 2 * e + 1][c / 2] >> (16 * (c & 1));
+            o[e] = (lo & 0xFFFFu) | (hi << 16);
+        }
+        *reinterpret_cast<u32x4v*>(dst + (c0 + c) * ld_dst + r0 + r8) =
+            u32x4v{o[0], o[1], o[2], o[3]};
+    }
+}
+
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* __restrict__ p, int64_t ld,
+                                                       int64_t rows, int cols) {
+    const int64_t total = rows * cols;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * 256)
+        p[(i / cols) * ld + i % cols] = 0.0f;
+}
+
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
 }  // namespace
 
 extern "C" {
@@ -360,6 +559,159 @@ logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h, int64_t
     return linear_logp_partials_ex(1.0f, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
                                    vocab_padded, col_begin, col_end, targets, active,
                                    ignore_index, partials, ldp, stream);
+}
+
+int64_t linear_logp_backward_workspace(int64_t n, int64_t hidden_size, int64_t chunk_cols) {
+    if (n < 0 || hidden_size < 1 || chunk_cols < 1 || n > LINEAR_LOGP_BWD_MAX_ROWS ||
+        hidden_size > LINEAR_LOGP_MAX_HIDDEN || chunk_cols > LINEAR_LOGP_BWD_MAX_CHUNK)
+        return -1;
+    const int64_t n_pad = round_up(std::max<int64_t>(n, 1), kBM);
+    const int64_t h_pad = round_up(hidden_size, kBN);
+    const int64_t c_pad = round_up(chunk_cols, kBN);
+    return 2 * (h_pad * n_pad + h_pad * c_pad + 2 * n_pad * c_pad);
+}
+
+logp_status_t linear_logp_backward_ex(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
+    int64_t ld_dh, float* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream) {
+    if (!(inv_temperature > 0.0f) || !std::isfinite(inv_temperature)) return LOGP_ERR_ARG;
+    if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
+        vocab_padded > (int64_t(1) << 31) - 1 - kTile || n > LINEAR_LOGP_BWD_MAX_ROWS)
+        return LOGP_ERR_SHAPE;
+    if (col_begin < 0 || col_end < col_begin || col_end > vocab_padded ||
+        col_begin % kTile != 0 || (col_end % kTile != 0 && col_end != vocab_padded))
+        return LOGP_ERR_SHARD;
+    if (chunk_cols < kTile || chunk_cols % kTile != 0 || chunk_cols > LINEAR_LOGP_BWD_MAX_CHUNK)
+        return LOGP_ERR_SHAPE;
+    if (n == 0) return LOGP_OK;
+    const int64_t H = hidden_size;
+    if (H < 1 || H > LINEAR_LOGP_MAX_HIDDEN || H % 8 != 0 || ld_h < H || ld_w < H ||
+        ld_h % 8 != 0 || ld_w % 8 != 0 || ld_h > LINEAR_LOGP_MAX_LD ||
+        ld_w > LINEAR_LOGP_MAX_LD || ld_dh < H || ld_dw < H)
+        return LOGP_ERR_SHAPE;
+    const int64_t width = col_end - col_begin;
+    if (hidden == nullptr || targets == nullptr || grad_logp == nullptr || stats == nullptr ||
+        dhidden == nullptr || (width > 0 && (weight == nullptr || dweight == nullptr)) ||
+        workspace == nullptr)
+        return LOGP_ERR_NULL;
+    if (!aligned16(hidden) || (weight != nullptr && !aligned16(weight)) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return LOGP_ERR_SHAPE;
+    const int64_t need = linear_logp_backward_workspace(n, H, chunk_cols);
+    if (need < 0 || workspace_bytes < need) return LOGP_ERR_SHAPE;
+    if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
+    // weight rows actually read: the view's real vocabulary rows
+    const int64_t lim = std::max<int64_t>(0, std::min(width, vocab_real - col_begin));
+    const Span in[] = {{hidden, span_bytes(n, ld_h, H, 2)},
+                       {weight, lim > 0 ? span_bytes(lim, ld_w, H, 2) : 0},
+                       {targets, uint64_t(n) * 8},
+                       {active, active ? uint64_t(n) : 0},
+                       {grad_logp, uint64_t(n) * 4},
+                       {stats, uint64_t(n) * sizeof(logp_stats_t)}};
+    const Span out[] = {{dhidden, span_bytes(n, ld_dh, H, 4)},
+                        {dweight, width > 0 ? span_bytes(width, ld_dw, H, 4) : 0},
+                        {workspace, uint64_t(need)}};
+    int dev = -1;
+    logp_status_t st = check_buffers(in, 6, out, 3, stream, &dev);
+    if (st != LOGP_OK) return st;
+    DeviceGuard guard(dev);
+    if (!guard.ok()) return LOGP_ERR_HIP;
+
+    if (width == 0) {  // no vocabulary columns: this shard contributes dh = 0
+        int cols = static_cast<int>(H);
+        void* args[] = {&dhidden, &ld_dh, &n, &cols};
+        return launch(reinterpret_cast<const void*>(&zero_rows_kernel), dim3(1024), dim3(256),
+                      args, 0, stream);
+    }
+
+    const int64_t n_pad = round_up(n, kBM), h_pad = round_up(H, kBN);
+    const int64_t c_pad_max = round_up(chunk_cols, kBN);
+    uint16_t* ws = static_cast<uint16_t*>(workspace);
+    uint16_t* hT = ws;                      // [h_pad, n_pad]
+    uint16_t* wT = hT + h_pad * n_pad;      // [h_pad, c_pad]
+    uint16_t* dz = wT + h_pad * c_pad_max;  // [n_pad, c_pad]
+    uint16_t* dzT = dz + n_pad * c_pad_max; // [c_pad, n_pad]
+
+    int Hi = static_cast<int>(H), ni = static_cast<int>(n);
+    {  // h^T, zero-padded
+        void* args[] = {&hidden, &ld_h, &ni, &Hi, &hT, const_cast<int64_t*>(&n_pad)};
+        st = launch(reinterpret_cast<const void*>(&transpose_kernel),
+                    dim3(static_cast<uint32_t>(h_pad / kTr), static_cast<uint32_t>(n_pad / kTr)),
+                    dim3(256), args, 0, stream);
+        if (st != LOGP_OK) return st;
+    }
+    const bool scaled = inv_temperature != 1.0f;
+    const void* dz_kernel = scaled ? reinterpret_cast<const void*>(&linear_dz_kernel<true>)
+                                   : reinterpret_cast<const void*>(&linear_dz_kernel<false>);
+    int row_blocks = static_cast<int>(n_pad / kBM);
+    for (int64_t off = 0; off < width; off += chunk_cols) {
+        const int64_t cw = std::min(chunk_cols, width - off);     // chunk columns
+        const int64_t c_pad = round_up(cw, kBN);
+        const int64_t chunk_col0 = col_begin + off;              // global column of the chunk
+        int lim_c = static_cast<int>(std::max<int64_t>(0, std::min(cw, vocab_real - chunk_col0)));
+        const uint16_t* wc = weight + off * ld_w;
+        {  // W^T of the chunk's real rows, zero-padded to [h_pad, c_pad]
+            void* args[] = {&wc, &ld_w, &lim_c, &Hi, &wT, const_cast<int64_t*>(&c_pad)};
+            st = launch(reinterpret_cast<const void*>(&transpose_kernel),
+                        dim3(static_cast<uint32_t>(h_pad / kTr),
+                             static_cast<uint32_t>(c_pad / kTr)),
+                        dim3(256), args, 0, stream);
+            if (st != LOGP_OK) return st;
+        }
+        {  // dz and dz^T
+            int64_t ldz = c_pad, ldzt = n_pad;
+            int64_t cc0 = chunk_col0;
+            float inv_t = inv_temperature;
+            void* args[] = {&hidden, &ld_h, &n,     &Hi,     &wc,          &ld_w,
+                            &lim_c,  &row_blocks,   &cc0,    &vocab_real,  &inv_t,
+                            &targets, &active,      &ignore_index, &grad_logp, &stats,
+                            &dz,     &ldz,          &dzT,    &ldzt};
+            st = launch(dz_kernel, dim3(static_cast<uint32_t>(row_blocks * (c_pad / kBN))),
+                        dim3(kThreads), args, 0, stream);
+            if (st != LOGP_OK) return st;
+        }
+        {  // dh (=|+=) dz W: a = dz [n_pad, c_pad], b = W^T [h_pad, c_pad]
+            int64_t lda = c_pad, ldb = c_pad, ldc = ld_dh;
+            int K = static_cast<int>(c_pad), mr = ni, nr = Hi, mb = row_blocks;
+            void* args[] = {&dz, &lda, &wT, &ldb, &K, &mr, &nr, &mb, &dhidden, &ldc};
+            const void* k = off == 0 ? reinterpret_cast<const void*>(&gemm_tn_kernel<false>)
+                                     : reinterpret_cast<const void*>(&gemm_tn_kernel<true>);
+            st = launch(k, dim3(static_cast<uint32_t>(mb * (h_pad / kBN))), dim3(kThreads),
+                        args, 0, stream);
+            if (st != LOGP_OK) return st;
+        }
+        {  // dW of the chunk's rows = dz^T h: a = dz^T [c_pad, n_pad], b = h^T [h_pad, n_pad]
+            int64_t lda = n_pad, ldb = n_pad, ldc = ld_dw;
+            int K = static_cast<int>(n_pad), mr = static_cast<int>(cw), nr = Hi;
+            int mb = static_cast<int>(c_pad / kBM);
+            float* dwc = dweight + off * ld_dw;
+            void* args[] = {&dzT, &lda, &hT, &ldb, &K, &mr, &nr, &mb, &dwc, &ldc};
+            st = launch(reinterpret_cast<const void*>(&gemm_tn_kernel<false>),
+                        dim3(static_cast<uint32_t>(mb * (h_pad / kBN))), dim3(kThreads), args,
+                        0, stream);
+            if (st != LOGP_OK) return st;
+        }
+    }
+    return LOGP_OK;
+}
+
+logp_status_t linear_logp_backward(const uint16_t* hidden, int64_t ld_h, int64_t n,
+                                   int64_t hidden_size, const uint16_t* weight, int64_t ld_w,
+                                   int64_t vocab_real, int64_t vocab_padded, int64_t col_begin,
+                                   int64_t col_end, const int64_t* targets,
+                                   const uint8_t* active, int64_t ignore_index,
+                                   const float* grad_logp, const logp_stats_t* stats,
+                                   float* dhidden, int64_t ld_dh, float* dweight, int64_t ld_dw,
+                                   void* workspace, int64_t workspace_bytes, int64_t chunk_cols,
+                                   hipStream_t stream) {
+    return linear_logp_backward_ex(1.0f, hidden, ld_h, n, hidden_size, weight, ld_w,
+                                   vocab_real, vocab_padded, col_begin, col_end, targets, active,
+                                   ignore_index, grad_logp, stats, dhidden, ld_dh, dweight,
+                                   ld_dw, workspace, workspace_bytes, chunk_cols, stream);
 }
 
 }  // extern "C"

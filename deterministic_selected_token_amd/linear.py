@@ -22,9 +22,13 @@ import torch
 from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _stream, logp_merge,
                logp_num_tiles)
 
-EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex")
+EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex", "linear_logp_backward",
+            "linear_logp_backward_ex", "linear_logp_backward_workspace")
 MAX_HIDDEN = 65536
 MAX_LD = 262144
+BWD_MAX_ROWS = 8388608
+BWD_MAX_CHUNK = 1048576
+DEFAULT_CHUNK_COLS = 4 * TILE_COLS
 
 _P, _I64 = ctypes.c_void_p, ctypes.c_int64
 _lib.linear_logp_partials.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64,
@@ -32,6 +36,14 @@ _lib.linear_logp_partials.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64
 _lib.linear_logp_partials.restype = ctypes.c_int32
 _lib.linear_logp_partials_ex.argtypes = [ctypes.c_float] + _lib.linear_logp_partials.argtypes
 _lib.linear_logp_partials_ex.restype = ctypes.c_int32
+_lib.linear_logp_backward.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64,
+                                      _P, _P, _I64, _P, _P, _P, _I64, _P, _I64, _P, _I64, _I64,
+                                      _P]
+_lib.linear_logp_backward.restype = ctypes.c_int32
+_lib.linear_logp_backward_ex.argtypes = [ctypes.c_float] + _lib.linear_logp_backward.argtypes
+_lib.linear_logp_backward_ex.restype = ctypes.c_int32
+_lib.linear_logp_backward_workspace.argtypes = [_I64, _I64, _I64]
+_lib.linear_logp_backward_workspace.restype = _I64
 
 
 def _bf16_rows(name: str, t: torch.Tensor, device=None) -> torch.Tensor:
@@ -107,3 +119,72 @@ def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: tor
     return logp_merge(partials, targets, vocab_real, num_tiles=L, active=active,
                       ignore_index=ignore_index, logp=logp, lse=lse, stats=stats,
                       stream=stream)
+
+
+def linear_logp_backward_workspace(n: int, hidden_size: int,
+                                   chunk_cols: int = DEFAULT_CHUNK_COLS) -> int:
+    """Workspace bytes that linear_logp_backward needs (-1 when out of range)."""
+    return int(_lib.linear_logp_backward_workspace(int(n), int(hidden_size), int(chunk_cols)))
+
+
+def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                         grad_logp: torch.Tensor, stats: torch.Tensor,
+                         vocab_real: Optional[int] = None, vocab_padded: Optional[int] = None,
+                         col_begin: int = 0, col_end: Optional[int] = None, active=None,
+                         ignore_index: int = -100, inv_temperature: float = 1.0,
+                         chunk_cols: int = DEFAULT_CHUNK_COLS,
+                         dhidden: Optional[torch.Tensor] = None,
+                         dweight: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """(dhidden [n, H] float32, dweight [col_end - col_begin, H] float32): the gradients of
+    sum_t grad_logp[t] logp[t] with respect to hidden and to the weight rows
+    W[col_begin:col_end] (``weight`` is that row slice), for the logits of linear_logp_forward
+    with the same inv_temperature; ``stats`` is the forward's (M, S).  The workspace (a
+    uint8 GPU tensor of at least linear_logp_backward_workspace(n, H, chunk_cols) bytes) is
+    allocated with torch when none is passed."""
+    hidden = _bf16_rows("hidden", hidden)
+    dev = hidden.device
+    weight = _bf16_rows("weight", weight, dev)
+    n, H = hidden.shape
+    if weight.shape[1] != H:
+        raise ValueError("hidden and weight must have the same hidden size")
+    vocab_padded = col_begin + weight.shape[0] if vocab_padded is None else int(vocab_padded)
+    vocab_real = vocab_padded if vocab_real is None else int(vocab_real)
+    col_end = vocab_padded if col_end is None else int(col_end)
+    width = col_end - col_begin
+    targets = _rows("targets", targets, torch.int64, n, dev)
+    grad_logp = _rows("grad_logp", grad_logp, torch.float32, n, dev)
+    active = _active(active, n, dev)
+    if stats.shape != (n, 2) or stats.dtype != torch.float32 or stats.device != dev \
+            or (n > 0 and stats.stride() != (2, 1)):
+        raise ValueError("stats must be a contiguous float32 [n, 2] tensor")
+    rows_needed = max(0, min(col_end, vocab_real) - col_begin)
+    if weight.shape[0] < rows_needed:
+        raise ValueError(f"weight holds {weight.shape[0]} rows, the range needs {rows_needed}")
+    if dhidden is None:
+        dhidden = torch.empty((n, H), dtype=torch.float32, device=dev)
+    if dweight is None:
+        dweight = torch.empty((width, H), dtype=torch.float32, device=dev)
+    for name, t, rows in (("dhidden", dhidden, n), ("dweight", dweight, width)):
+        if t.dtype != torch.float32 or t.device != dev or t.dim() != 2 or \
+                t.shape[0] != rows or t.shape[1] != H or (H > 1 and t.stride(1) != 1):
+            raise ValueError(f"{name} must be float32 [{rows}, {H}] with unit column stride")
+    need = linear_logp_backward_workspace(n, H, chunk_cols)
+    if need < 0:
+        raise ValueError("n, hidden size or chunk_cols out of range")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    args = (_ptr(hidden), _row_stride(hidden), n, H, _ptr(weight) if weight.numel() else None,
+            _row_stride(weight), vocab_real, vocab_padded, int(col_begin), col_end,
+            _ptr(targets), _ptr(active), int(ignore_index), _ptr(grad_logp), _ptr(stats),
+            _ptr(dhidden), _row_stride(dhidden) if n else H,
+            _ptr(dweight) if dweight.numel() else None, _row_stride(dweight) if width else H,
+            _ptr(workspace), workspace.numel(), int(chunk_cols), _stream(dev, stream))
+    if inv_temperature == 1.0:
+        _check("linear_logp_backward", _lib.linear_logp_backward(*args))
+    else:
+        _check("linear_logp_backward_ex",
+               _lib.linear_logp_backward_ex(float(inv_temperature), *args))
+    return dhidden, dweight

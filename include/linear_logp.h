@@ -41,6 +41,8 @@ extern "C" {
 
 #define LINEAR_LOGP_MAX_HIDDEN 65536  /* largest hidden size H */
 #define LINEAR_LOGP_MAX_LD 262144      /* largest row stride of hidden and weight (elements) */
+#define LINEAR_LOGP_BWD_MAX_ROWS 8388608    /* largest n of the backward (2^23) */
+#define LINEAR_LOGP_BWD_MAX_CHUNK 1048576   /* largest chunk_cols of the backward (2^20) */
 
 /* Per-tile partials of the logits h W^T over the vocabulary columns [col_begin, col_end).
  *   hidden        [n, ld_h] BF16 bits; row t at hidden + t*ld_h; H = hidden_size columns used.
@@ -82,6 +84,54 @@ LOGP_API logp_status_t linear_logp_partials_ex(float inv_temperature, const uint
                                                const int64_t* targets, const uint8_t* active,
                                                int64_t ignore_index, logp_partial_t* partials,
                                                int64_t ldp, hipStream_t stream);
+
+/* Backward of linear_logp: the gradients of sum over valid rows t of g_t logp_t (logp of the
+ * scored logits z = fl32(acc(h W^T) * inv_temperature) of linear_logp_partials_ex) with respect
+ * to h and to the shard's rows of W.  The derivative through logp is the logp path's backward
+ * (PR #495 "zero-workspace backward for generic CUDA fused logp", Summary: dlogits =
+ * g (onehot - softmax), rounded straight to BF16), times inv_temperature through the scoring
+ * multiply (PR #314's temperature):
+ *   dz[t, v] = RNE_bf16( g' (1[v == y_t] - exp(z[t, v] - M_t) / S_t) ),  g' = fl32(g_t inv_t),
+ *     with z recomputed bit for bit as the forward formed it, (M, S) the forward's stats
+ *     (logp_merge), and dz = 0 for rows that are not valid, for M_t = -inf and for padding
+ *     columns (v >= vocab_real);
+ *   dhidden[t, :] = sum over this shard's columns v of dz[t, v] W[v, :]   (FP32, overwritten);
+ *   dweight[v - col_begin, :] = sum over rows t of dz[t, v] h[t, :]      (FP32, overwritten;
+ *     rows of padding columns are 0).
+ * Both sums run on the matrix cores with FP32 accumulation in a fixed order: dhidden adds the
+ * chunks of chunk_cols columns in column order, each a fixed-order product over its columns, so
+ * a row's dhidden does not depend on the other rows of the batch; dweight sums the rows in
+ * index order.  Vocab-parallel ranks each produce their shard's dhidden; the caller adds them
+ * in a fixed rank order.  Run to run the results are bitwise identical.
+ *   hidden, weight, targets, active, ignore_index, vocab_real, vocab_padded, col_begin,
+ *   col_end, inv_temperature   as in linear_logp_partials_ex (weight points at row col_begin).
+ *   grad_logp     [n] FP32 upstream gradient of logp.   stats  [n] (M, S) of the forward.
+ *   dhidden       [n, ld_dh] FP32, ld_dh >= H.   dweight  [col_end - col_begin, ld_dw] FP32.
+ *   workspace     device memory of at least linear_logp_backward_workspace(n, H, chunk_cols)
+ *                 bytes, 256-byte aligned, owned by the caller, contents irrelevant on entry.
+ *   chunk_cols    vocabulary columns per pass (a multiple of LOGP_TILE_COLS, at most
+ *                 LINEAR_LOGP_BWD_MAX_CHUNK); larger chunks take more workspace, not more
+ *                 time per column.
+ * n <= LINEAR_LOGP_BWD_MAX_ROWS.  col_end == col_begin writes dhidden = 0.  Errors as for
+ * linear_logp_partials_ex; outputs and the workspace must not overlap any input or each
+ * other (LOGP_ERR_OVERLAP); a short or misaligned workspace is LOGP_ERR_SHAPE. */
+LOGP_API int64_t linear_logp_backward_workspace(int64_t n, int64_t hidden_size,
+                                                int64_t chunk_cols);  /* -1 when out of range */
+LOGP_API logp_status_t linear_logp_backward_ex(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
+    int64_t ld_dh, float* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream);
+/* linear_logp_backward_ex at inv_temperature = 1. */
+LOGP_API logp_status_t linear_logp_backward(
+    const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
+    int64_t ld_dh, float* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import deterministic_selected_token_amd as dst
+import oracle
 from deterministic_selected_token_amd import linear
 
 pytestmark = pytest.mark.gpu
@@ -232,3 +233,145 @@ def test_linear_temperature_vocab_shards_are_bitwise():
             c0 = c1
         got = dst.logp_merge(partials, y, V)
         assert all(torch.equal(a, b) for a, b in zip(ref, got)), layout
+
+
+# ------------------------------------------------------------------------------ backward
+#
+# Tolerance, derived from the arithmetic: dz is rounded once to BF16 (relative 2^-9) from an
+# FP32 value whose softmax factor p carries the logit's accumulation error and the FP32 stats'
+# (relative well under 2^-14 at these sizes), so |dz_gpu - dz| <= 2^-8 (|dz| + |g'| p); dh and
+# dW then add K/16 + 2 roundings of 2^-24 relative over K summed products.  The bounds use the
+# oracle's |dz| + |g'| p in place of |dz| because the target entry's 1 - p can cancel.
+# A sharper check separates the products from that rounding: against dh and dW formed from
+# the oracle's own BF16 rounding of its dz, the only differences are the rare entries whose
+# rounding flips (about 1e-4 of them, one BF16 unit each) and the FP32 accumulation, so the
+# aggregate error stays below 2^-12 of the scale.
+
+def bwd_run(h, W, y, V, Vp=None, active=None, inv_t=1.0, chunk=linear.DEFAULT_CHUNK_COLS,
+            seed=5):
+    Vp = V if Vp is None else Vp
+    n = h.shape[0]
+    g = (torch.randn(n, generator=torch.Generator().manual_seed(seed)) * 0.5).to(DEV)
+    _, _, stats = linear.linear_logp_forward(h, W, y, V, Vp, active=active, inv_temperature=inv_t)
+    ws = torch.empty(linear.linear_logp_backward_workspace(n, h.shape[1], chunk),
+                     dtype=torch.uint8, device=DEV)
+    dh, dW = linear.linear_logp_backward(h, W, y, g, stats, V, Vp, active=active,
+                                         inv_temperature=inv_t, chunk_cols=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    return g, stats, dh, dW, ws
+
+
+def bwd_reference(h, W, y, g, V, active=None, inv_t=1.0):
+    from oracle import linear_oracle as LO
+    act = None if active is None else active.cpu().numpy()
+    ref = LO.backward(h.cpu(), W.cpu()[:V], y.cpu().numpy(), g.cpu().numpy(), V, active=act,
+                      inv_temperature=inv_t)
+    it = float(np.float32(inv_t))
+    gp = np.abs(g.cpu().numpy().astype(np.float64) * it)
+    # |g'| p for every entry: p = -dz / g' off target, 1 - dz / g' at the target
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(gp[:, None] > 0, -ref["dz"] / (g.cpu().numpy()[:, None] * it), 0.0)
+    yv = y.cpu().numpy()
+    rows = np.nonzero(ref["valid"])[0]
+    p[rows, yv[rows]] += 1.0
+    ref["scale"] = np.abs(ref["dz"]) + gp[:, None] * np.abs(p)
+    dz_r = oracle.bf16_bits_to_f64(oracle.rne_bf16(ref["dz"]))
+    hc, Wc = h.cpu().double().numpy(), W.cpu()[:V].double().numpy()
+    ref["dh_r"], ref["dW_r"] = dz_r @ Wc, dz_r.T @ hc
+    return ref
+
+
+def check_bwd(h, W, y, g, dh, dW, V, ref, width=None):
+    hc, Wc = h.cpu().double().numpy(), W.cpu()[:V].double().numpy()
+    n = h.shape[0]
+    s_dh = ref["scale"] @ np.abs(Wc)
+    s_dW = ref["scale"].T @ np.abs(hc)
+    e_dh = np.abs(dh.cpu().numpy().astype(np.float64) - ref["dh"])
+    tol_dh = (2.0 ** -8 + (V / 16 + 2) * 2.0 ** -24) * s_dh + 1e-30
+    assert np.all(e_dh <= tol_dh), (e_dh.max(), np.argwhere(e_dh > tol_dh)[:3])
+    dWg = dW.cpu().numpy().astype(np.float64)
+    e_dW = np.abs(dWg[:V] - ref["dW"])
+    tol_dW = (2.0 ** -8 + (n / 16 + 2) * 2.0 ** -24) * s_dW + 1e-30
+    assert np.all(e_dW <= tol_dW), (e_dW.max(), np.argwhere(e_dW > tol_dW)[:3])
+    assert np.all(dWg[V:] == 0)  # padding rows of the shard
+    # the products themselves, against the same products of the oracle's BF16 dz
+    rel_dh = np.linalg.norm(dh.cpu().numpy() - ref["dh_r"]) / max(np.linalg.norm(s_dh), 1e-300)
+    rel_dW = np.linalg.norm(dWg[:V] - ref["dW_r"]) / max(np.linalg.norm(s_dW), 1e-300)
+    assert rel_dh <= 2.0 ** -12 and rel_dW <= 2.0 ** -12, (rel_dh, rel_dW)
+    return {"dh_max_err": float(e_dh.max()), "dW_max_err": float(e_dW.max()),
+            "rel_dh_vs_rounded": float(rel_dh), "rel_dW_vs_rounded": float(rel_dW)}
+
+
+BWD = [(70, 128, 9000, 1.0), (130, 200, 5000, 1 / 0.7), (33, 64, 4100, 2.0),
+       (257, 256, 8300, 1.0), (64, 4096, 12000, 1.0)]
+
+
+@pytest.mark.parametrize("n,H,V,inv_t", BWD, ids=[f"n{a}_H{b}_V{c}_t{d:.3g}" for a, b, c, d in BWD])
+def test_linear_backward_parity(n, H, V, inv_t):
+    h, W, y = make(n, H, V, seed=n + H, scale=2.0)
+    active = (torch.arange(n, device=DEV) % 7 != 3).to(torch.uint8)
+    say(f"linear backward parity n={n} H={H} V={V} inv_t={inv_t:.4g}")
+    g, _, dh, dW, _ = bwd_run(h, W, y, V, active=active, inv_t=inv_t, chunk=4096)
+    ref = bwd_reference(h, W, y, g, V, active=active, inv_t=inv_t)
+    res = check_bwd(h, W, y, g, dh, dW, V, ref)
+    assert torch.all(dh[active.cpu().numpy() == 0] == 0)
+    say(f"n={n} H={H} V={V}: {res}")
+
+
+def test_linear_backward_dz_in_the_workspace():
+    """dz itself, read from the workspace ([hT | WT | dz | dzT], a single chunk): correctly
+    rounded BF16 of the float64 value almost everywhere, within the bound everywhere, and
+    dzT is its exact transpose."""
+    n, H, V = 100, 256, 3000
+    h, W, y = make(n, H, V, seed=21, scale=3.0)
+    inv_t = 1 / 0.7
+    say("linear backward dz in the workspace")
+    g, _, dh, dW, ws = bwd_run(h, W, y, V, inv_t=inv_t, chunk=4096)
+    ref = bwd_reference(h, W, y, g, V, inv_t=inv_t)
+    n_pad, h_pad, c_pad, c_max = 256, 256, 3072, 4096
+    base = h_pad * n_pad + h_pad * c_max
+    words = ws.view(torch.int16)
+    dz = words[base: base + n_pad * c_pad].view(n_pad, c_pad)
+    dzt = words[base + n_pad * c_max: base + n_pad * c_max + c_pad * n_pad].view(c_pad, n_pad)
+    assert torch.equal(dz.t().contiguous(), dzt)
+    dzh = dz.cpu()
+    got = oracle.bf16_bits_to_f64(dzh[:n, :V].numpy().view(np.uint16))
+    assert torch.all(dzh[n:] == 0) and torch.all(dzh[:, V:] == 0)
+    want = ref["dz"]
+    rounded = oracle.bf16_bits_to_f64(oracle.rne_bf16(want))
+    err = np.abs(got - want)
+    assert np.all(err <= 2.0 ** -8 * ref["scale"] + 1e-38), err.max()
+    frac = float(np.mean(got == rounded))
+    assert frac >= 0.999, frac
+    say(f"dz correctly rounded {frac:.6f}")
+
+
+def test_linear_backward_bitwise_contract():
+    """Run to run; dh rows independent of the batch around them; dW independent of the chunk
+    size; a vocab shard's dW rows equal the full call's; an empty shard gives dh = 0."""
+    n, H, V = 300, 128, 3 * T + 500
+    h, W, y = make(n, H, V, seed=31)
+    say("linear backward bitwise contract")
+    g, stats, dh, dW, _ = bwd_run(h, W, y, V, chunk=4096)
+    _, _, dh2, dW2, _ = bwd_run(h, W, y, V, chunk=4096)
+    assert torch.equal(dh, dh2) and torch.equal(dW, dW2)
+    for lo, hi in ((0, 1), (17, 151), (151, n)):
+        s = slice(lo, hi)
+        sdh, _ = linear.linear_logp_backward(h[s], W, y[s], g[s], stats[s].contiguous(), V, V,
+                                             chunk_cols=4096)
+        assert torch.equal(sdh, dh[s]), (lo, hi)
+    _, dW8 = linear.linear_logp_backward(h, W, y, g, stats, V, V, chunk_cols=2 * T)
+    assert torch.equal(dW8, dW)
+    c0, c1 = T, 3 * T
+    sdh, sdW = linear.linear_logp_backward(h, W[c0:c1], y, g, stats, V, V, col_begin=c0,
+                                           col_end=c1, chunk_cols=4096)
+    assert torch.equal(sdW, dW[c0:c1])
+    parts = [linear.linear_logp_backward(h, W[a:b], y, g, stats, V, V, col_begin=a, col_end=b,
+                                         chunk_cols=4096)[0]
+             for a, b in ((0, T), (T, 3 * T), (3 * T, V))]
+    total = (parts[0].double() + parts[1].double() + parts[2].double())
+    assert torch.allclose(total, dh.double(), rtol=1e-5, atol=1e-6 * float(dh.abs().max()))
+    z, zw = linear.linear_logp_backward(h, W[:0], y, g, stats, V, V, col_begin=0, col_end=0,
+                                        chunk_cols=4096)
+    torch.cuda.synchronize()
+    assert zw.shape == (0, H) and torch.all(z == 0)

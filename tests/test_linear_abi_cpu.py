@@ -49,11 +49,61 @@ def test_linear_partials_ex_validates_like_the_plain_entry(over, want):
     assert call_ex(1.0 / 0.7, **over) == want == call(**over)
 
 
+def call_bwd(inv_t=None, **over):
+    a = dict(h=A, ld_h=64, n=10, H=64, w=A, ld_w=64, vr=5000, vp=5000, c0=0, c1=5000, y=A,
+             act=None, ign=-100, g=A, st=A, dh=A, ld_dh=64, dw=A, ld_dw=64, ws=A,
+             wsb=1 << 40, chunk=4096)
+    a.update(over)
+    args = (a["h"], a["ld_h"], a["n"], a["H"], a["w"], a["ld_w"], a["vr"], a["vp"], a["c0"],
+            a["c1"], a["y"], a["act"], a["ign"], a["g"], a["st"], a["dh"], a["ld_dh"], a["dw"],
+            a["ld_dw"], a["ws"], a["wsb"], a["chunk"], None)
+    if inv_t is None:
+        return lib.linear_logp_backward(*args)
+    return lib.linear_logp_backward_ex(inv_t, *args)
+
+
+W16 = ctypes.c_void_p(0x10010)  # 16-byte but not 256-byte aligned
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(n=-1), SHAPE), (dict(vr=0), SHAPE), (dict(c0=100), SHARD), (dict(c1=4097), SHARD),
+    (dict(chunk=0), SHAPE), (dict(chunk=4000), SHAPE), (dict(chunk=2 ** 21), SHAPE),
+    (dict(n=0), OK), (dict(n=2 ** 23 + 1), SHAPE),
+    (dict(h=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL), (dict(g=None), NULL),
+    (dict(st=None), NULL), (dict(dh=None), NULL), (dict(dw=None), NULL), (dict(ws=None), NULL),
+    (dict(H=60, ld_h=64, ld_w=64), SHAPE), (dict(ld_dh=32), SHAPE), (dict(ld_dw=32), SHAPE),
+    (dict(h=U), SHAPE), (dict(w=U), SHAPE), (dict(ws=W16), SHAPE), (dict(wsb=1000), SHAPE),
+], ids=lambda v: str(v))
+def test_linear_backward_host_validation(over, want):
+    assert call_bwd(**over) == want
+
+
+@pytest.mark.parametrize("inv_t", [0.0, -1.0, float("inf"), float("nan")])
+def test_linear_backward_rejects_bad_temperature(inv_t):
+    assert call_bwd(inv_t) == ARG
+    assert call_bwd(1.0 / 0.7, n=-1) == SHAPE
+
+
+def test_linear_backward_workspace_size():
+    ws = linear.linear_logp_backward_workspace
+    # 2 bytes x (H_pad n_pad + H_pad chunk + 2 n_pad chunk), pads to 256
+    assert ws(8192, 4096, 4096) == 2 * (4096 * 8192 + 4096 * 4096 + 2 * 8192 * 4096)
+    assert ws(1, 8, 4096) == 2 * (256 * 256 + 256 * 4096 + 2 * 256 * 4096)
+    assert ws(0, 8, 4096) == ws(1, 8, 4096)
+    assert ws(-1, 8, 4096) == -1 and ws(10, 0, 4096) == -1 and ws(10, 8, 0) == -1
+    assert ws(linear.BWD_MAX_ROWS + 1, 8, 4096) == -1
+    assert ws(10, 8, linear.BWD_MAX_CHUNK + 1) == -1
+
+
 def test_header_constant():
     text = open(os.path.join(ROOT, "include", "linear_logp.h")).read()
     assert int(re.search(r"#define LINEAR_LOGP_MAX_HIDDEN (\d+)", text).group(1)) == \
         linear.MAX_HIDDEN
     assert int(re.search(r"#define LINEAR_LOGP_MAX_LD (\d+)", text).group(1)) == linear.MAX_LD
+    assert int(re.search(r"#define LINEAR_LOGP_BWD_MAX_ROWS (\d+)", text).group(1)) == \
+        linear.BWD_MAX_ROWS
+    assert int(re.search(r"#define LINEAR_LOGP_BWD_MAX_CHUNK (\d+)", text).group(1)) == \
+        linear.BWD_MAX_CHUNK
 
 
 @pytest.mark.parametrize("over,want", [
