@@ -332,6 +332,65 @@ def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
     return out
 
 
+def time_linear_backward(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
+                         vocab: int = 151936, chunk_cols: int = 16384) -> dict:
+    """linear_logp backward on the same LM-head shape: dz recomputed (2 n V H flops), then
+    dh = dz W and dW = dz^T h (2 n V H flops each), 6 n V H flops per call."""
+    import torch
+
+    from deterministic_selected_token_amd import linear
+
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev).manual_seed(12)
+    h = torch.randn((n, hidden), generator=gen, device=dev).to(torch.bfloat16)
+    W = (torch.randn((vocab, hidden), generator=gen, device=dev) * (3.0 / hidden ** 0.5)) \
+        .to(torch.bfloat16)
+    y = torch.randint(0, vocab, (n,), generator=gen, device=dev)
+    g = torch.randn((n,), generator=gen, device=dev) * 0.01
+    _, _, stats = linear.linear_logp_forward(h, W, y, vocab, vocab, stream=stream)
+    dh = torch.empty((n, hidden), dtype=torch.float32, device=dev)
+    dW = torch.empty((vocab, hidden), dtype=torch.float32, device=dev)
+    ws = torch.empty(linear.linear_logp_backward_workspace(n, hidden, chunk_cols),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        linear.linear_logp_backward(h, W, y, g, stats, vocab, vocab, chunk_cols=chunk_cols,
+                                    dhidden=dh, dweight=dW, workspace=ws, stream=stream)
+
+    step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    flops = 6.0 * n * vocab * hidden
+    del h, W, dW, ws
+    # the float64 oracle on a bounded sample: 4 rows against the first 16384 vocabulary rows
+    import numpy as np
+
+    from oracle import linear_oracle
+
+    rows, cols = 4, 16384
+    gen_c = torch.Generator().manual_seed(12)
+    hs = torch.randn((rows, hidden), generator=gen_c).to(torch.bfloat16)
+    Ws = (torch.randn((cols, hidden), generator=gen_c) * (3.0 / hidden ** 0.5)).to(torch.bfloat16)
+    t0 = time.perf_counter()
+    linear_oracle.backward(hs, Ws, np.arange(rows), np.ones(rows, dtype=np.float32), cols)
+    dt = time.perf_counter() - t0
+    cpu = {"value": round(6.0 * rows * cols * hidden / dt / 1e12, 4), "unit": "TFLOP/s",
+           "kind": "oracle", "cores": len(os.sched_getaffinity(0)),
+           "sample": f"{rows} rows x {cols} vocabulary rows, float64 dz, dh and dW, "
+                     f"{dt:.2f} s wall"}
+    return {"rows": n, "hidden": hidden, "vocab": vocab, "chunk_cols": chunk_cols,
+            "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "workspace_bytes": linear.linear_logp_backward_workspace(n, hidden, chunk_cols),
+            "cpu_baseline": cpu}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -442,6 +501,8 @@ def main() -> int:
         extra["variants"]["linear_logp_fwd"] = time_linear(dst, stream, max(3, args.steps // 4))
         extra["variants"]["linear_logp_fwd_temperature_0.7"] = time_linear(
             dst, stream, max(3, args.steps // 4), inv_temperature=1 / 0.7, cpu_baseline=False)
+        extra["variants"]["linear_logp_bwd"] = time_linear_backward(
+            dst, stream, max(2, args.steps // 8))
     if args.profile_copy:
         src = torch.empty(1 << 31, dtype=torch.int16, device=dev)  # 4 GiB
         dst_buf = torch.empty_like(src)
