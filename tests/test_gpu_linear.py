@@ -375,3 +375,21 @@ def test_linear_backward_bitwise_contract():
                                         chunk_cols=4096)
     torch.cuda.synchronize()
     assert zw.shape == (0, H) and torch.all(z == 0)
+
+
+def test_linear_backward_padded_vocabulary():
+    """Weight rows at or past vocab_real are never read (NaN there) and get zero dW; the real
+    part matches the unpadded call bitwise (an all-padding chunk adds +0 to dh)."""
+    n, H, V, Vp = 90, 128, 10000, 4 * T
+    h, W, y = make(n, H, V, Vp, seed=41, pad_value=float("nan"))
+    say("linear backward padded vocabulary")
+    g, stats, dh, dW, _ = bwd_run(h, W, y, V, Vp, chunk=4096)
+    assert torch.all(dW[V:] == 0) and not torch.isnan(dW).any() and not torch.isnan(dh).any()
+    _, _, stats_u = linear.linear_logp_forward(h, W[:V].contiguous(), y, V, V)
+    assert torch.equal(stats, stats_u)
+    dh_u, dW_u = linear.linear_logp_backward(h, W[:V].contiguous(), y, g, stats_u, V, V,
+                                             chunk_cols=4096)
+    torch.cuda.synchronize()
+    assert torch.equal(dh, dh_u) and torch.equal(dW[:V], dW_u)
+    ref = bwd_reference(h, W, y, g, V)
+    say(f"padded: {check_bwd(h, W, y, g, dh, dW, V, ref)}")
