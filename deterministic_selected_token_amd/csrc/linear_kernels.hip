@@ -510,7 +510,12 @@ logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hid
         col_begin % kTile != 0 || (col_end % kTile != 0 && col_end != vocab_padded))
         return LOGP_ERR_SHARD;
     if (n == 0 || col_end == col_begin) return LOGP_OK;
-    if (hidden == nullptr || weight == nullptr || targets == nullptr || partials == nullptr)
+    // weight rows actually read: the view's real vocabulary rows (none for an all-padding view,
+    // whose weight pointer may then be NULL)
+    const int64_t lim =
+        std::max<int64_t>(0, std::min(col_end - col_begin, vocab_real - col_begin));
+    if (hidden == nullptr || (lim > 0 && weight == nullptr) || targets == nullptr ||
+        partials == nullptr)
         return LOGP_ERR_NULL;
     const int64_t H = hidden_size;
     if (H < 1 || H > LINEAR_LOGP_MAX_HIDDEN || H % 8 != 0 || ld_h < H || ld_w < H ||
@@ -524,8 +529,6 @@ logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hid
     const int64_t view_tiles = ceil_div(width, kTile);
     if (ldp < view_tiles) return LOGP_ERR_SHAPE;
     if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
-    // weight rows actually read: the view's real vocabulary rows
-    const int64_t lim = std::max<int64_t>(0, std::min(width, vocab_real - col_begin));
     const Span in[] = {{hidden, span_bytes(n, ld_h, H, 2)},
                        {weight, lim > 0 ? span_bytes(lim, ld_w, H, 2) : 0},
                        {targets, uint64_t(n) * 8},
@@ -594,9 +597,12 @@ logp_status_t linear_logp_backward_ex(
         ld_w > LINEAR_LOGP_MAX_LD || ld_dh < H || ld_dw < H)
         return LOGP_ERR_SHAPE;
     const int64_t width = col_end - col_begin;
+    // weight rows actually read: the view's real vocabulary rows (none for an all-padding view,
+    // whose weight pointer may then be NULL)
+    const int64_t lim = std::max<int64_t>(0, std::min(width, vocab_real - col_begin));
     if (hidden == nullptr || targets == nullptr || grad_logp == nullptr || stats == nullptr ||
-        dhidden == nullptr || (width > 0 && (weight == nullptr || dweight == nullptr)) ||
-        workspace == nullptr)
+        dhidden == nullptr || (lim > 0 && weight == nullptr) ||
+        (width > 0 && dweight == nullptr) || workspace == nullptr)
         return LOGP_ERR_NULL;
     if (!aligned16(hidden) || (weight != nullptr && !aligned16(weight)) ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -604,8 +610,6 @@ logp_status_t linear_logp_backward_ex(
     const int64_t need = linear_logp_backward_workspace(n, H, chunk_cols);
     if (need < 0 || workspace_bytes < need) return LOGP_ERR_SHAPE;
     if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
-    // weight rows actually read: the view's real vocabulary rows
-    const int64_t lim = std::max<int64_t>(0, std::min(width, vocab_real - col_begin));
     const Span in[] = {{hidden, span_bytes(n, ld_h, H, 2)},
                        {weight, lim > 0 ? span_bytes(lim, ld_w, H, 2) : 0},
                        {targets, uint64_t(n) * 8},

@@ -48,7 +48,8 @@ extern "C" {
  *   hidden        [n, ld_h] BF16 bits; row t at hidden + t*ld_h; H = hidden_size columns used.
  *   weight        BF16 bits pointing at row col_begin of W: row v of the view at
  *                 weight + (v - col_begin)*ld_w, H columns used.  Rows at or beyond vocab_real
- *                 are never read (they count as -inf logits, like padding columns).
+ *                 are never read (they count as -inf logits, like padding columns); for a
+ *                 view with no real row (all padding) weight may be NULL.
  *   hidden_size   H, 1 <= H <= LINEAR_LOGP_MAX_HIDDEN, a multiple of 8.
  *   ld_h, ld_w    row strides in elements, >= H, multiples of 8 and at most
  *                 LINEAR_LOGP_MAX_LD; hidden and weight must be 16-byte aligned (else

@@ -393,3 +393,13 @@ def test_linear_backward_padded_vocabulary():
     assert torch.equal(dh, dh_u) and torch.equal(dW[:V], dW_u)
     ref = bwd_reference(h, W, y, g, V)
     say(f"padded: {check_bwd(h, W, y, g, dh, dW, V, ref)}")
+    # an all-padding shard needs no weight rows at all
+    c0, c1 = 3 * T, 4 * T
+    pdh, pdW = linear.linear_logp_backward(h, W[:0], y, g, stats, V, Vp, col_begin=c0,
+                                           col_end=c1, chunk_cols=4096)
+    L = dst.logp_num_tiles(Vp)
+    part = torch.full((n, L, 3), float("nan"), device=DEV)
+    linear.linear_logp_partials(h, W[:0], y, V, Vp, c0, c1, part)
+    torch.cuda.synchronize()
+    assert torch.all(pdh == 0) and torch.all(pdW == 0) and pdW.shape == (T, H)
+    assert torch.all(part[:, 3, 0] == float("-inf")) and torch.all(part[:, 3, 1:] == 0)

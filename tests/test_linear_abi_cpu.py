@@ -95,6 +95,20 @@ def test_linear_backward_workspace_size():
     assert ws(10, 8, linear.BWD_MAX_CHUNK + 1) == -1
 
 
+DEVICE = 4
+
+
+def test_weight_may_be_null_for_an_all_padding_view():
+    """No real row in [col_begin, col_end): the weight pointer is not needed, so NULL passes
+    the NULL check (and fails later only at the device check, this machine having no GPU)."""
+    pad = dict(w=None, vr=4000, vp=8192, c0=4096, c1=8192)
+    assert call(**pad) == DEVICE
+    assert call(**dict(pad, c0=0)) == NULL  # real rows in range: weight required
+    assert call_bwd(**pad) == DEVICE
+    assert call_bwd(**dict(pad, c0=0)) == NULL
+    assert call_bwd(**dict(pad, dw=None)) == NULL  # dweight is always required
+
+
 def test_header_constant():
     text = open(os.path.join(ROOT, "include", "linear_logp.h")).read()
     assert int(re.search(r"#define LINEAR_LOGP_MAX_HIDDEN (\d+)", text).group(1)) == \
