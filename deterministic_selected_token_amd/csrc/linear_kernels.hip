@@ -163,7 +163,11 @@ __device__ __forceinline__ void block_product(Smem& sm, const uint16_t* __restri
         const int cur = kt & 1;
         if (kt + 1 < nk)
             load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, (kt + 1) * kBK, rs);
+        // the wave with matrix-core work ready issues first (the other wave on the SIMD is
+        // then in its load / LDS phase): about 3% on the whole kernel
+        __builtin_amdgcn_s_setprio(1);
         mma_stage(sm, cur, wm, wn, lane, acc);
+        __builtin_amdgcn_s_setprio(0);
         if (kt + 1 < nk) store_stage(sm, cur ^ 1, rs);
         __syncthreads();
     }
