@@ -374,6 +374,9 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
         rb = bwd_row<D, SCALED>(row_a + 1, col_begin, vocab_real, inv_t, targets, active,
                                 ignore_index, grad, stats);
 
+    // loads issue at raised wave priority, so a wave that has its row constants gets its 8 KiB
+    // in flight ahead of waves that are computing (six A/B pairs: 0.3-1% on this kernel)
+    __builtin_amdgcn_s_setprio(1);
     Raw8<D> w[kLoads];
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
@@ -384,6 +387,7 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
         if (q0 + idx < total && (in_b ? rb.valid : ra.valid))
             load8<D, true>(logits + row * ld, col, lim, w[k]);
     }
+    __builtin_amdgcn_s_setprio(0);
     bool hit = false;
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
