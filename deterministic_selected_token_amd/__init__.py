@@ -27,7 +27,9 @@ TILE_COLS = 4096
 FWD_MAX_TILES = 4096
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblogp_mi355x.so")
+# DST_AMD_LIB selects another build of the same library (the tests' sanitizer build of the
+# host code uses it); by default the in-tree build next to this file.
+LIB_PATH = os.environ.get("DST_AMD_LIB") or os.path.join(_HERE, "liblogp_mi355x.so")
 
 STATUS = {
     0: "LOGP_OK", 1: "LOGP_ERR_NULL", 2: "LOGP_ERR_SHAPE", 3: "LOGP_ERR_SHARD",

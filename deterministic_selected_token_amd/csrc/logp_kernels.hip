@@ -490,7 +490,8 @@ const void* bwd_ptr(bool vin, bool vout, bool scaled, bool flat) {
 }
 
 // Element size of a dtype, or 0 when the value is not a logp_dtype_t.
-int64_t elem_bytes(logp_dtype_t dtype) {
+// dtype travels as an int32 (a logp_dtype_t value): any value a caller passes is defined here.
+int64_t elem_bytes(int32_t dtype) {
     switch (dtype) {
         case LOGP_DTYPE_BF16: return 2;
         case LOGP_DTYPE_F16: return 2;
@@ -516,7 +517,8 @@ int64_t logp_num_tiles(int64_t vocab_padded) {
     return vocab_padded < 1 ? 0 : ceil_div(vocab_padded, kTile);
 }
 
-const char* logp_status_string(logp_status_t status) {
+const char* logp_status_string(int32_t status) {
+    // an int, not the enum: any value a caller passes is defined here
     switch (status) {
         case LOGP_OK: return "ok";
         case LOGP_ERR_NULL: return "a required pointer is NULL";
@@ -536,7 +538,7 @@ const char* logp_status_string(logp_status_t status) {
     return "unknown status";
 }
 
-logp_status_t logp_forward_ex(logp_dtype_t dtype, float inv_temperature, const void* logits,
+logp_status_t logp_forward_ex(int32_t dtype, float inv_temperature, const void* logits,
                               int64_t ld, int64_t n, int64_t vocab_real, int64_t vocab_padded,
                               const int64_t* targets, const uint8_t* active, int64_t ignore_index,
                               float* logp, float* lse, logp_stats_t* stats, hipStream_t stream) {
@@ -582,7 +584,7 @@ logp_status_t logp_forward(const uint16_t* logits, int64_t ld, int64_t n, int64_
                            targets, active, ignore_index, logp, lse, stats, stream);
 }
 
-logp_status_t logp_backward_ex(logp_dtype_t dtype, float inv_temperature, const void* logits,
+logp_status_t logp_backward_ex(int32_t dtype, float inv_temperature, const void* logits,
                                int64_t ld, int64_t n, int64_t vocab_real, int64_t vocab_padded,
                                int64_t col_begin, int64_t col_end, const int64_t* targets,
                                const uint8_t* active, int64_t ignore_index,
@@ -662,7 +664,7 @@ logp_status_t logp_backward(const uint16_t* logits, int64_t ld, int64_t n, int64
                             dlogits, ld_out, stream);
 }
 
-logp_status_t logp_partials_ex(logp_dtype_t dtype, float inv_temperature, const void* logits,
+logp_status_t logp_partials_ex(int32_t dtype, float inv_temperature, const void* logits,
                                int64_t ld, int64_t n, int64_t vocab_real, int64_t vocab_padded,
                                int64_t col_begin, int64_t col_end, const int64_t* targets,
                                const uint8_t* active, int64_t ignore_index,

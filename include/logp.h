@@ -180,7 +180,8 @@ LOGP_API logp_status_t logp_merge(const logp_partial_t* partials, int64_t ldp, i
                                   float* lse, logp_stats_t* stats, hipStream_t stream);
 
 /* Extended forms: any logits dtype and temperature-scaled scoring.
- *   dtype            element type of logits (and of dlogits in logp_backward_ex).
+ *   dtype            element type of logits (and of dlogits in logp_backward_ex): a
+ *                    logp_dtype_t value, passed as int32_t (other values: LOGP_ERR_ARG).
  *   inv_temperature  1/tau, finite and > 0.  The scored logits are z = fl32(x * inv_temperature),
  *                    one FP32 product per logit, so training and rollout code that use the same
  *                    inv_temperature see the same z (temperatures 1.0 and 0.7 in the provider
@@ -192,13 +193,13 @@ LOGP_API logp_status_t logp_merge(const logp_partial_t* partials, int64_t ldp, i
  * and dlogits are `void*` of the given dtype, and ld / ld_out count elements.  A view takes the
  * 16-byte vector path when its start is 16-byte aligned and ld * element size is a multiple of
  * 16; the results do not depend on which path runs. */
-LOGP_API logp_status_t logp_forward_ex(logp_dtype_t dtype, float inv_temperature,
+LOGP_API logp_status_t logp_forward_ex(int32_t dtype, float inv_temperature,
                                        const void* logits, int64_t ld, int64_t n,
                                        int64_t vocab_real, int64_t vocab_padded,
                                        const int64_t* targets, const uint8_t* active,
                                        int64_t ignore_index, float* logp, float* lse,
                                        logp_stats_t* stats, hipStream_t stream);
-LOGP_API logp_status_t logp_backward_ex(logp_dtype_t dtype, float inv_temperature,
+LOGP_API logp_status_t logp_backward_ex(int32_t dtype, float inv_temperature,
                                         const void* logits, int64_t ld, int64_t n,
                                         int64_t vocab_real, int64_t vocab_padded,
                                         int64_t col_begin, int64_t col_end,
@@ -206,7 +207,7 @@ LOGP_API logp_status_t logp_backward_ex(logp_dtype_t dtype, float inv_temperatur
                                         int64_t ignore_index, const float* grad_logp,
                                         const logp_stats_t* stats, void* dlogits, int64_t ld_out,
                                         hipStream_t stream);
-LOGP_API logp_status_t logp_partials_ex(logp_dtype_t dtype, float inv_temperature,
+LOGP_API logp_status_t logp_partials_ex(int32_t dtype, float inv_temperature,
                                         const void* logits, int64_t ld, int64_t n,
                                         int64_t vocab_real, int64_t vocab_padded,
                                         int64_t col_begin, int64_t col_end,
@@ -227,7 +228,7 @@ LOGP_API logp_status_t logp_check_targets(const int64_t* targets, const uint8_t*
                                           int64_t* bad_count, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
-LOGP_API const char* logp_status_string(logp_status_t status);
+LOGP_API const char* logp_status_string(int32_t status);  /* a logp_status_t value */
 
 #ifdef __cplusplus
 }
