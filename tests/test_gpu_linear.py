@@ -403,3 +403,28 @@ def test_linear_backward_padded_vocabulary():
     torch.cuda.synchronize()
     assert torch.all(pdh == 0) and torch.all(pdW == 0) and pdW.shape == (T, H)
     assert torch.all(part[:, 3, 0] == float("-inf")) and torch.all(part[:, 3, 1:] == 0)
+
+
+def test_linear_grpo_step_chain():
+    """linear_logp_forward -> grpo_loss -> linear_logp_backward on B sequences of T tokens
+    (rows of h in sequence order), each stage checked against the oracle on its own inputs:
+    the logp, then dh and dW for the GRPO gradient the GPU produced."""
+    from deterministic_selected_token_amd import grpo
+    from oracle import grpo_oracle as O
+    B, Tn, H, V = 4, 96, 128, 6000
+    h, W, y = make(B * Tn, H, V, seed=51, scale=2.0, ignore_frac=0.0)
+    say("linear grpo step chain")
+    logp, _, stats = linear.linear_logp_forward(h, W, y, V, V)
+    lp = logp.view(B, Tn)
+    gen = torch.Generator().manual_seed(52)
+    old = (lp + 0.05 * torch.randn((B, Tn), generator=gen).to(DEV)).contiguous()
+    adv = grpo.grpo_advantages(torch.randn(B, generator=gen).to(DEV), 2)
+    loss, _, dlogp = grpo.grpo_loss(lp, old, adv, ref_logp=old, mode="token_mean", beta=0.04)
+    g = dlogp.reshape(-1).contiguous()
+    dh, dW = linear.linear_logp_backward(h, W, y, g, stats, V, V, chunk_cols=4096)
+    torch.cuda.synchronize()
+    o = O.loss(lp.cpu().numpy(), old.cpu().numpy(), old.cpu().numpy(), adv.cpu().numpy(),
+               None, mode="token_mean", beta=0.04)
+    assert abs(grpo.loss_fields(loss)["loss"] - o["loss"]) <= 1e-5 * (1 + abs(o["loss"]))
+    ref = bwd_reference(h, W, y, g, V)
+    say(f"grpo chain: {check_bwd(h, W, y, g, dh, dW, V, ref)}")
