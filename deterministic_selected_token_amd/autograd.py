@@ -1,0 +1,53 @@
+"""torch.autograd binding of the selected-token log-probability.
+
+Marshalling only, like the rest of the package: the forward is ``logp_forward_ex`` and the
+backward ``logp_backward_ex`` (dlogits straight to the logits' dtype); torch only carries the
+tensors and the graph.  ``selected_token_logp(logits, targets)`` is the drop-in for
+``log_softmax(logits).gather(targets)`` in a training loss, with this library's deterministic,
+batch-invariant forward and backward.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import logp_backward_ex, logp_forward_ex
+
+
+class SelectedTokenLogp(torch.autograd.Function):
+    """logp [n] (float32) of ``targets`` under ``logits`` [n, V] (BF16 / FP16 / FP32, scored
+    as fl32(x * inv_temperature)); gradient with respect to ``logits`` only."""
+
+    @staticmethod
+    def forward(ctx, logits, targets, vocab_real, vocab_padded, active, ignore_index,
+                inv_temperature):
+        logp, _, stats = logp_forward_ex(logits, targets, vocab_real, vocab_padded,
+                                         active=active, ignore_index=ignore_index,
+                                         inv_temperature=inv_temperature)
+        ctx.save_for_backward(logits, targets, stats)
+        ctx.active = active
+        ctx.args = (vocab_real, vocab_padded, ignore_index, inv_temperature)
+        return logp
+
+    @staticmethod
+    def backward(ctx, grad_logp):
+        logits, targets, stats = ctx.saved_tensors
+        vocab_real, vocab_padded, ignore_index, inv_temperature = ctx.args
+        if grad_logp.dtype != torch.float32 or not grad_logp.is_contiguous():
+            grad_logp = grad_logp.float().contiguous()
+        dlogits = logp_backward_ex(logits, targets, grad_logp, stats, vocab_real, vocab_padded,
+                                   active=ctx.active, ignore_index=ignore_index,
+                                   inv_temperature=inv_temperature)
+        return dlogits, None, None, None, None, None, None
+
+
+def selected_token_logp(logits: torch.Tensor, targets: torch.Tensor,
+                        vocab_real: Optional[int] = None, vocab_padded: Optional[int] = None,
+                        active=None, ignore_index: int = -100,
+                        inv_temperature: float = 1.0) -> torch.Tensor:
+    """logp[t] = log softmax(fl32(logits[t] * inv_temperature))[targets[t]] (0 for rows that are
+    masked, ignored or out of range), differentiable with respect to ``logits``."""
+    return SelectedTokenLogp.apply(logits, targets, vocab_real, vocab_padded, active,
+                                   ignore_index, inv_temperature)

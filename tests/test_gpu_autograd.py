@@ -1,0 +1,51 @@
+"""The torch.autograd binding: bitwise the library's own forward and backward, and against
+torch float64 autograd of log_softmax + gather on the CPU."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import deterministic_selected_token_amd as dst
+from deterministic_selected_token_amd.autograd import selected_token_logp
+from parity_checks import spacing
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("dtype,inv_t", [(torch.bfloat16, 1.0), (torch.float16, 1 / 0.7),
+                                         (torch.float32, 2.0)])
+def test_autograd_matches_the_library_and_float64(dtype, inv_t):
+    n, V = 37, 3000
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn((n, V), generator=g) * 2).to(dtype)
+    y = torch.randint(0, V, (n,), generator=g)
+    y[5] = -100
+    w = torch.randn(n, generator=g)
+    print(f"[gpu] autograd {dtype} inv_t={inv_t:.3g}", flush=True)
+    xd = x.to(DEV).requires_grad_()
+    logp = selected_token_logp(xd, y.to(DEV), inv_temperature=inv_t)
+    (logp * w.to(DEV)).sum().backward()
+    torch.cuda.synchronize()
+    # bitwise the direct calls
+    lp, _, stats = dst.logp_forward_ex(xd.detach(), y.to(DEV), inv_temperature=inv_t)
+    d = dst.logp_backward_ex(xd.detach(), y.to(DEV), w.to(DEV), stats, inv_temperature=inv_t)
+    torch.cuda.synchronize()
+    assert torch.equal(logp.detach(), lp) and torch.equal(xd.grad, d)
+    # float64 autograd of the scored logits on the CPU
+    it = float(np.float32(inv_t))
+    z = (x.float() * it).double().requires_grad_()  # the scored logits fl32(x * inv_t)
+    ls = torch.log_softmax(z, dim=1)
+    valid = y >= 0
+    ref = torch.where(valid, ls[torch.arange(n), y.clamp(min=0)],
+                      torch.zeros(n, dtype=torch.float64))
+    (ref * w.double()).sum().backward()
+    grad64 = (z.grad * it).numpy()  # d z / d x = inv_t
+    got = xd.grad.float().cpu().double().numpy()
+    assert np.abs(logp.detach().cpu().double().numpy() - ref.detach().numpy()).max() <= 1e-4
+    tol = spacing(grad64, {torch.bfloat16: "bf16", torch.float16: "f16",
+                           torch.float32: "f32"}[dtype]) + 1e-6 * np.abs(grad64).max()
+    assert np.all(np.abs(got - grad64) <= tol), np.abs(got - grad64).max()
+    assert torch.all(xd.grad[5] == 0)
