@@ -51,3 +51,46 @@ def selected_token_logp(logits: torch.Tensor, targets: torch.Tensor,
     masked, ignored or out of range), differentiable with respect to ``logits``."""
     return SelectedTokenLogp.apply(logits, targets, vocab_real, vocab_padded, active,
                                    ignore_index, inv_temperature)
+
+
+class LinearLogp(torch.autograd.Function):
+    """logp [n] (float32) of ``targets`` under the logits hidden W^T (BF16 hidden [n, H] and
+    LM-head weight [V, H]), scored as fl32(acc * inv_temperature); gradients with respect to
+    hidden and weight from linear_logp_backward, accumulated in FP32 and rounded once to the
+    inputs' dtype."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, targets, vocab_real, active, ignore_index,
+                inv_temperature, chunk_cols):
+        from .linear import linear_logp_forward
+        logp, _, stats = linear_logp_forward(hidden, weight, targets, vocab_real,
+                                             weight.shape[0], active=active,
+                                             ignore_index=ignore_index,
+                                             inv_temperature=inv_temperature)
+        ctx.save_for_backward(hidden, weight, targets, stats)
+        ctx.active = active
+        ctx.args = (vocab_real, ignore_index, inv_temperature, chunk_cols)
+        return logp
+
+    @staticmethod
+    def backward(ctx, grad_logp):
+        from .linear import linear_logp_backward
+        hidden, weight, targets, stats = ctx.saved_tensors
+        vocab_real, ignore_index, inv_temperature, chunk_cols = ctx.args
+        if grad_logp.dtype != torch.float32 or not grad_logp.is_contiguous():
+            grad_logp = grad_logp.float().contiguous()
+        dh, dw = linear_logp_backward(hidden, weight, targets, grad_logp, stats, vocab_real,
+                                      weight.shape[0], active=ctx.active,
+                                      ignore_index=ignore_index,
+                                      inv_temperature=inv_temperature, chunk_cols=chunk_cols)
+        return (dh.to(hidden.dtype), dw.to(weight.dtype), None, None, None, None, None, None)
+
+
+def linear_logp(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                vocab_real: Optional[int] = None, active=None, ignore_index: int = -100,
+                inv_temperature: float = 1.0, chunk_cols: int = 4 * 4096) -> torch.Tensor:
+    """logp[t] = log softmax(hidden[t] W^T)[targets[t]] on the matrix cores, differentiable with
+    respect to hidden and weight (rows of W at or past vocab_real are padding)."""
+    vr = weight.shape[0] if vocab_real is None else int(vocab_real)
+    return LinearLogp.apply(hidden, weight, targets, vr, active, ignore_index,
+                            inv_temperature, chunk_cols)

@@ -49,3 +49,25 @@ def test_autograd_matches_the_library_and_float64(dtype, inv_t):
                            torch.float32: "f32"}[dtype]) + 1e-6 * np.abs(grad64).max()
     assert np.all(np.abs(got - grad64) <= tol), np.abs(got - grad64).max()
     assert torch.all(xd.grad[5] == 0)
+
+
+def test_linear_logp_autograd_matches_the_library():
+    from deterministic_selected_token_amd import linear
+    from deterministic_selected_token_amd.autograd import linear_logp
+    n, H, V = 40, 128, 5000
+    g = torch.Generator().manual_seed(4)
+    h = torch.randn((n, H), generator=g).to(torch.bfloat16).to(DEV).requires_grad_()
+    W = (torch.randn((V, H), generator=g) * 0.2).to(torch.bfloat16).to(DEV).requires_grad_()
+    y = torch.randint(0, V, (n,), generator=g).to(DEV)
+    w = torch.randn(n, generator=g).to(DEV)
+    print("[gpu] linear_logp autograd", flush=True)
+    logp = linear_logp(h, W, y, inv_temperature=1 / 0.7, chunk_cols=4096)
+    (logp * w).sum().backward()
+    lp, _, stats = linear.linear_logp_forward(h.detach(), W.detach(), y, V, V,
+                                              inv_temperature=1 / 0.7)
+    dh, dW = linear.linear_logp_backward(h.detach(), W.detach(), y, w, stats, V, V,
+                                         inv_temperature=1 / 0.7, chunk_cols=4096)
+    torch.cuda.synchronize()
+    assert torch.equal(logp.detach(), lp)
+    assert h.grad.dtype == torch.bfloat16 and W.grad.dtype == torch.bfloat16
+    assert torch.equal(h.grad, dh.to(torch.bfloat16)) and torch.equal(W.grad, dW.to(torch.bfloat16))
