@@ -5,7 +5,8 @@
 // the tile in 16 sub-blocks of 256 columns; for each it forms the 256 x 256 logits block on the
 // matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension; each
 // wave holds a 64 x 128 block; the hidden states and weight rows are staged through
-// double-buffered LDS with the next stage's global loads in flight), reduces the block to a
+// double-buffered LDS by direct-to-LDS buffer loads, the next stage's in flight while the
+// matrix cores work on the current one), reduces the block to a
 // per-row (max, sum-exp) through LDS (half the rows at a time, 4 threads per row over 64
 // columns each, then a 2-level lane tree), and folds it into the row's running tile state in
 // LDS.  After the last sub-block the tile's (m, s, sel) partial is written in logp.h's layout,
@@ -38,11 +39,9 @@ constexpr int kThreads = kWM * kWN * kWave;   // 512
 constexpr int kBM = kWM * kTM * 32;           // rows per workgroup
 constexpr int kBN = kWN * kTN * 32;           // columns per sub-block
 constexpr int kBK = 64;                       // hidden elements per LDS stage
-constexpr int kRow = kBK + 8;                 // LDS row stride in elements (144 bytes)
 constexpr int kSubBlocks = kTile / kBN;       // sub-blocks per vocab tile
 constexpr int kChunksA = kBM * kBK / 8 / kThreads;  // 16-byte chunks per thread per stage
-constexpr int kChunksB = kBN * kBK / 8 / kThreads;
-constexpr int kChunksPerRow = kBK / 8;
+constexpr int kChunksB = kBN * kBK / 8 / kThreads;  // (= load instructions per wave)
 
 // Sub-block reduction through LDS: half a row block (kBM / kTM rows) at a time, kRedThreads
 // threads per row, each reducing kRedCols columns.
@@ -56,85 +55,81 @@ static_assert(kChunksB * kThreads * 8 == kBN * kBK, "B stage is whole chunks per
 static_assert(kTile % kBN == 0, "a vocab tile is whole sub-blocks");
 static_assert(kRedCols % 4 == 0 && kHalfRows * kRedThreads == kThreads, "reduction layout");
 
-// The stage arrays are 16-byte aligned so their 16-byte chunks move as single ds_read_b128 /
-// ds_write_b128 instructions.
+// Stage layout: [row][64 hidden elements], 128-byte rows with no padding; the 16-byte chunk c of
+// row r sits at position c ^ swz(r), so that the 16 consecutive rows a fragment read touches
+// fall in distinct banks.  The stages are filled by direct-to-LDS buffer loads (each wave
+// instruction writes 64 consecutive 16-byte slots); out-of-range chunks load as zero.
+constexpr int kStageA = kBM * kBK, kStageB = kBN * kBK;  // elements
+constexpr int kRedBytes = int(sizeof(float)) * kHalfRows * kRedRow;
+constexpr int kStageBytes = 2 * 2 * (kStageA + kStageB);
+constexpr int kPadElems = kRedBytes > kStageBytes ? (kRedBytes - kStageBytes) / 2 : 0;
 struct alignas(16) Smem {
-    alignas(16) uint16_t a[2][kBM * kRow];  // hidden-state stage, [row][k]
-    alignas(16) uint16_t b[2][kBN * kRow];  // weight stage, [vocab row][k]
+    alignas(16) uint16_t a[2][kStageA];  // hidden-state stage
+    alignas(16) uint16_t b[2][kStageB];  // weight stage
+    uint16_t pad[kPadElems];             // the reduction area overlays a, b and pad
     float m[kBM], s[kBM], sel[kBM];  // running tile state per row
     int y_rel[kBM];             // target column inside this tile, or -1
 };
+static_assert(kRedBytes <= kStageBytes + 2 * kPadElems, "the reduction area fits");
 
-// One stage of this thread's chunks in registers (global loads in flight).
-struct Stage {
-    u32x4v a[kChunksA];
-    u32x4v b[kChunksB];
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: loads zero
+
+// The stage loads of one operand block (rows [0, rows) of `base`, row stride ld, H valid
+// elements per row): each load instruction of a wave covers 8 rows, through a buffer resource
+// of its own whose range ends at the last valid element of those rows, so every offset stays
+// small and every load is either inside the operand or out of range (zero).
+template <int N>
+struct OperandLoads {
+    __amdgpu_buffer_rsrc_t rs[N];
+    uint32_t off[N];  // this lane's byte offset at k0 = 0, kOob for rows past the range
 };
 
-static_assert(sizeof(float) * kHalfRows * kRedRow <= sizeof(Smem::a) + sizeof(Smem::b),
-              "the reduction area fits in the stage buffers");
-
-// Loads this thread's 16-byte chunks of one stage: rows [0, kBM) of the hidden-state block at
-// `hb` (n_here of them real) and rows [col0, col0 + kBN) of the weight tile at `wb` (lim_here
-// real), hidden elements [k0, k0 + kBK); out-of-range chunks are zero.  Offsets from the two
-// wave-uniform bases are 32-bit.
-__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ hb, uint32_t ld_h,
-                                           int n_here, const uint16_t* __restrict__ wb,
-                                           uint32_t ld_w, int lim_here, int H, int col0, int k0,
-                                           Stage& st) {
-    const int t = threadIdx.x;
+template <int N>
+__device__ __forceinline__ void plan_operand(const uint16_t* base, uint32_t ld, int rows, int H,
+                                             int wave, int lane, int c,
+                                             OperandLoads<N>& ol) {
 #pragma unroll
-    for (int i = 0; i < kChunksA; ++i) {
-        const int q = t + i * kThreads;
-        const int r = q / kChunksPerRow, k = k0 + (q % kChunksPerRow) * 8;
-        st.a[i] = (r < n_here && k < H)
-                      ? *reinterpret_cast<const u32x4v*>(hb + (uint32_t(r) * ld_h + uint32_t(k)))
-                      : u32x4v{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < kChunksB; ++i) {
-        const int q = t + i * kThreads;
-        const int r = q / kChunksPerRow, k = k0 + (q % kChunksPerRow) * 8;
-        const int col = col0 + r;
-        st.b[i] = (col < lim_here && k < H)
-                      ? *reinterpret_cast<const u32x4v*>(wb + (uint32_t(col) * ld_w + uint32_t(k)))
-                      : u32x4v{0u, 0u, 0u, 0u};
+    for (int i = 0; i < N; ++i) {
+        const int r0 = (i * (kThreads / kWave) + wave) * 8;
+        const int here = std::min(8, std::max(0, rows - r0));
+        const uint32_t bytes = here > 0 ? (uint32_t(here - 1) * ld + uint32_t(H)) * 2u : 0u;
+        ol.rs[i] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(base) + int64_t(r0) * ld, 0, static_cast<int>(bytes),
+            0x00020000);
+        ol.off[i] = (lane >> 3) < here ? (uint32_t(lane >> 3) * ld + uint32_t(8 * c)) * 2u
+                                       : kOob;
     }
 }
 
-__device__ __forceinline__ void store_stage(Smem& sm, int buf, const Stage& st) {
-    const u32x4v (&ra)[kChunksA] = st.a;
-    const u32x4v (&rb)[kChunksB] = st.b;
-    const int t = threadIdx.x;
+template <int N>
+__device__ __forceinline__ void issue_operand(uint16_t* stage, const OperandLoads<N>& ol,
+                                              bool k_ok, int k0, int wave) {
 #pragma unroll
-    for (int i = 0; i < kChunksA; ++i) {
-        const int q = t + i * kThreads;
-        *reinterpret_cast<u32x4v*>(&sm.a[buf][(q / kChunksPerRow) * kRow +
-                                              (q % kChunksPerRow) * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kChunksB; ++i) {
-        const int q = t + i * kThreads;
-        *reinterpret_cast<u32x4v*>(&sm.b[buf][(q / kChunksPerRow) * kRow +
-                                              (q % kChunksPerRow) * 8]) = rb[i];
-    }
+    for (int i = 0; i < N; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ol.rs[i], (lds_vptr)&stage[(i * (kThreads / kWave) + wave) * 512], 16,
+            k_ok ? ol.off[i] + 2u * uint32_t(k0) : kOob, 0, 0, 0);
 }
 
 // The matrix-core steps of one LDS stage: kBK / 16 steps of k, each wave's kTM x kTN tiles.
 __device__ __forceinline__ void mma_stage(const Smem& sm, int buf, int wm, int wn, int lane,
                                           f32x16 (&acc)[kTM][kTN]) {
+    const int q = (lane >> 5) ^ swz(lane & 31);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-        const int k = ks * 16 + 8 * (lane >> 5);
+        const int off = (lane & 31) * kBK + ((2 * ks) ^ q) * 8;
         bf16x8 fa[kTM], fb[kTN];
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
             fa[i] = *reinterpret_cast<const bf16x8*>(
-                &sm.a[buf][(wm * kTM * 32 + i * 32 + (lane & 31)) * kRow + k]);
+                &sm.a[buf][(wm * kTM * 32 + i * 32) * kBK + off]);
 #pragma unroll
         for (int j = 0; j < kTN; ++j)
             fb[j] = *reinterpret_cast<const bf16x8*>(
-                &sm.b[buf][(wn * kTN * 32 + j * 32 + (lane & 31)) * kRow + k]);
+                &sm.b[buf][(wn * kTN * 32 + j * 32) * kBK + off]);
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -144,32 +139,45 @@ __device__ __forceinline__ void mma_stage(const Smem& sm, int buf, int wm, int w
     }
 }
 
+__device__ __forceinline__ void wait_loads_and_sync() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stage loads are in LDS
+    __syncthreads();
+}
+
 // acc += the 256 x 256 block of A B^T for rows [0, n_here) of `hb` and rows
 // [col0, col0 + kBN) of `wb` (rows at or past lim_here and hidden elements at or past H read
 // as zero), in nk stages of kBK hidden elements: the one fixed accumulation order of every
-// logit, shared by the forward and the backward's recomputation.  The global loads of stage
-// kt + 1 are issued before the matrix-core work of stage kt and go to the other LDS buffer
-// after it.  Ends with a barrier (the stage buffers are free afterwards).
+// logit, shared by the forward and the backward's recomputation.  The loads of stage kt + 1
+// go straight to the other LDS buffer while the matrix cores work on stage kt.  Ends with a
+// barrier (the stage buffers are free afterwards).
 __device__ __forceinline__ void block_product(Smem& sm, const uint16_t* __restrict__ hb,
                                               uint32_t ldh, int n_here,
                                               const uint16_t* __restrict__ wb, uint32_t ldw,
                                               int lim_here, int H, int col0, int nk, int wm,
                                               int wn, int lane, f32x16 (&acc)[kTM][kTN]) {
-    Stage rs;
-    load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, 0, rs);
-    store_stage(sm, 0, rs);
-    __syncthreads();
+    const int wave = wm * kWN + wn;
+    // the chunk a lane loads: position lane & 7 of row lane >> 3 of an 8-row group, whose
+    // swizzle is (lane >> 3) ^ (wave & 1) (group bases are multiples of 8; odd groups flip)
+    const int c = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+    OperandLoads<kChunksA> la;
+    OperandLoads<kChunksB> lb;
+    plan_operand(hb, ldh, n_here, H, wave, lane, c, la);
+    plan_operand(wb + int64_t(col0) * ldw, ldw, std::min(kBN, lim_here - col0), H, wave, lane,
+                 c, lb);
+    issue_operand(sm.a[0], la, 8 * c < H, 0, wave);
+    issue_operand(sm.b[0], lb, 8 * c < H, 0, wave);
+    wait_loads_and_sync();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk)
-            load_stage(hb, ldh, n_here, wb, ldw, lim_here, H, col0, (kt + 1) * kBK, rs);
-        // the wave with matrix-core work ready issues first (the other wave on the SIMD is
-        // then in its load / LDS phase): about 3% on the whole kernel
+        if (kt + 1 < nk) {
+            const int k0 = (kt + 1) * kBK;
+            issue_operand(sm.a[cur ^ 1], la, k0 + 8 * c < H, k0, wave);
+            issue_operand(sm.b[cur ^ 1], lb, k0 + 8 * c < H, k0, wave);
+        }
         __builtin_amdgcn_s_setprio(1);
         mma_stage(sm, cur, wm, wn, lane, acc);
         __builtin_amdgcn_s_setprio(0);
-        if (kt + 1 < nk) store_stage(sm, cur ^ 1, rs);
-        __syncthreads();
+        wait_loads_and_sync();
     }
 }
 
@@ -526,9 +534,10 @@ logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hid
         ld_h % 8 != 0 || ld_w % 8 != 0 || ld_h > LINEAR_LOGP_MAX_LD ||
         ld_w > LINEAR_LOGP_MAX_LD || !aligned16(hidden) || !aligned16(weight))
         return LOGP_ERR_SHAPE;
-    // in-kernel offsets from a row block's or a tile's first row are 32-bit
-    static_assert(uint64_t(kTile) * LINEAR_LOGP_MAX_LD < (uint64_t(1) << 32), "tile offsets");
-    static_assert(uint64_t(kBM) * LINEAR_LOGP_MAX_LD < (uint64_t(1) << 32), "block offsets");
+    // in-kernel load offsets (bytes from the first row of an 8-row group) stay below the
+    // out-of-range marker 2^31
+    static_assert(uint64_t(16) * (LINEAR_LOGP_MAX_LD + LINEAR_LOGP_MAX_HIDDEN) < kOob,
+                  "load offsets");
     const int64_t width = col_end - col_begin;
     const int64_t view_tiles = ceil_div(width, kTile);
     if (ldp < view_tiles) return LOGP_ERR_SHAPE;
@@ -594,6 +603,11 @@ logp_status_t linear_logp_backward_ex(
         return LOGP_ERR_SHARD;
     if (chunk_cols < kTile || chunk_cols % kTile != 0 || chunk_cols > LINEAR_LOGP_BWD_MAX_CHUNK)
         return LOGP_ERR_SHAPE;
+    // the products' row strides and reduction lengths (padded rows or chunk columns) keep the
+    // in-kernel load offsets below the out-of-range marker
+    static_assert(uint64_t(16) * 2 * (LINEAR_LOGP_BWD_MAX_ROWS + kBM) < kOob &&
+                      LINEAR_LOGP_BWD_MAX_CHUNK <= LINEAR_LOGP_BWD_MAX_ROWS,
+                  "product load offsets");
     if (n == 0) return LOGP_OK;
     const int64_t H = hidden_size;
     if (H < 1 || H > LINEAR_LOGP_MAX_HIDDEN || H % 8 != 0 || ld_h < H || ld_w < H ||
