@@ -428,3 +428,31 @@ def test_linear_grpo_step_chain():
     assert abs(grpo.loss_fields(loss)["loss"] - o["loss"]) <= 1e-5 * (1 + abs(o["loss"]))
     ref = bwd_reference(h, W, y, g, V)
     say(f"grpo chain: {check_bwd(h, W, y, g, dh, dW, V, ref)}")
+
+
+def test_linear_row_strides_and_shard_views_bitwise():
+    """Hidden states and weight rows read through row strides wider than H (the gaps hold NaN),
+    and a vocab shard of such a weight view, give the bits of the contiguous calls: the staged
+    operands are the same and nothing past H is read."""
+    n, H, V = 300, 200, 9000
+    h, W, y = make(n, H, V, seed=21)
+    hs = torch.full((n, 264), float("nan"), dtype=torch.bfloat16, device=DEV)
+    hs[:, :H] = h
+    Ws = torch.full((V, 208), float("nan"), dtype=torch.bfloat16, device=DEV)
+    Ws[:, :H] = W
+    say("linear row-stride views")
+    a = linear.linear_logp_forward(h, W, y, V, V)
+    b = linear.linear_logp_forward(hs[:, :H], Ws[:, :H], y, V, V)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    g = torch.randn(n, generator=torch.Generator().manual_seed(22)).to(DEV)
+    da = linear.linear_logp_backward(h, W, y, g, a[2], V, V, chunk_cols=4096)
+    db = linear.linear_logp_backward(hs[:, :H], Ws[:, :H], y, g, b[2], V, V, chunk_cols=4096)
+    assert torch.equal(da[0], db[0]) and torch.equal(da[1], db[1])
+    L = dst.logp_num_tiles(V)
+    pa = torch.zeros((n, L, 3), device=DEV)
+    pb = torch.zeros((n, L, 3), device=DEV)
+    linear.linear_logp_partials(h, W[4096:], y, V, V, 4096, 8192, pa[:, 1:])
+    linear.linear_logp_partials(hs[:, :H], Ws[4096:, :H], y, V, V, 4096, 8192, pb[:, 1:])
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pb)
