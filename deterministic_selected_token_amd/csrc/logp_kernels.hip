@@ -344,12 +344,18 @@ __global__ __launch_bounds__(bwd_tile_waves<D>() * kWave) void bwd_kernel(
 }
 
 // Dense, 16-byte aligned views whose width is a multiple of 8 and at least one tile: the
-// view is the flat sequence of its [n, width/8] 8-element vectors and every wave takes 512
-// consecutive vectors (lane l holds vectors 64k + l, so each load instruction still covers
-// contiguous memory).  Same element-wise formulas as bwd_kernel, so the same bits; this split
-// just gives every wave the same amount of work whatever the row width.  A wave's vectors
-// span at most two rows (width >= 4096 columns = 512 vectors).
-template <Dt D, bool SCALED>
+// view is the flat sequence of its [n, width/8] 8-element vectors and every wave takes
+// 64 * NV consecutive vectors (lane l holds vectors 64k + l, so each load instruction covers
+// contiguous memory).  NV is chosen so a wave moves 16 KiB each way (16 vectors per lane for
+// 2-byte types, 8 for FP32), and the host keeps 64 * NV <= vectors per row, so a wave's
+// vectors span at most two rows.  Loads run kLoads deep as a rolling window: the first kLoads
+// are issued up front, and the register slot of each computed vector is refilled with the
+// load kLoads vectors ahead before that vector is stored, so a wave keeps 8 loads in flight
+// over its whole 16 KiB with the registers of 8.  The fast/general exponential path is chosen
+// once per group of kLoads vectors (all of them loaded by then).  Same element-wise formulas
+// as bwd_kernel, so the same bits; the split only gives every wave the same amount of work
+// whatever the row width.
+template <Dt D, bool SCALED, int NV>
 __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
     const typename DtInfo<D>::Storage* logits, int64_t ld, int64_t n, int vpr, int lim,
     int64_t col_begin, int64_t vocab_real, float inv_t, const int64_t* __restrict__ targets,
@@ -357,64 +363,86 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
     const logp_stats_t* __restrict__ stats, typename DtInfo<D>::Storage* dlogits,
     int64_t ld_out) {
     // logits and dlogits may be the same buffer: each vector is loaded and stored by the
-    // same lane, load first.
-    constexpr int kChunk = kWave * kLoads;  // 512 vectors per wave
+    // same lane, load first, and no other lane touches it.
+    using St = typename DtInfo<D>::Storage;
+    static_assert(NV % kLoads == 0, "whole groups of kLoads vectors");
+    constexpr int kChunk = kWave * NV;
     const int64_t total = n * vpr;
     const int64_t q0 = (int64_t(blockIdx.x) * kBwdWaves + wave_id()) * kChunk;
     if (q0 >= total) return;  // whole wave leaves; this kernel has no barrier
     const int lane = lane_id();
 
+    // Wave-uniform geometry: the chunk starts at vector off_a of row_a; its first `split`
+    // vectors lie in row_a and the rest in row_a + 1; only the first `live` exist.
     const int64_t row_a = q0 / vpr;
-    const int64_t sp = (row_a + 1) * vpr - q0;
-    const int split = sp < kChunk ? static_cast<int>(sp) : kChunk;  // vectors in row_a
+    const int off_a = static_cast<int>(q0 - row_a * vpr);
+    const int split = vpr - off_a < kChunk ? vpr - off_a : kChunk;
+    const int64_t left = total - q0;
+    const int live = left < kChunk ? static_cast<int>(left) : kChunk;
     const BwdRow ra = bwd_row<D, SCALED>(row_a, col_begin, vocab_real, inv_t, targets, active,
-                                      ignore_index, grad, stats);
+                                         ignore_index, grad, stats);
     BwdRow rb = ra;
-    if (split < kChunk && row_a + 1 < n)
+    if (split < live)  // the chunk reaches row_a + 1, which then exists
         rb = bwd_row<D, SCALED>(row_a + 1, col_begin, vocab_real, inv_t, targets, active,
                                 ignore_index, grad, stats);
+    // Row bases; the second pair is only dereferenced when the chunk reaches row_a + 1.
+    const St* xa = logits + row_a * ld;
+    const St* xb = xa + ld;
+    St* oa = dlogits + row_a * ld_out;
+    St* ob = oa + ld_out;
+    const int width = vpr * kVec;
 
-    // loads issue at raised wave priority, so a wave that has its row constants gets its 8 KiB
-    // in flight ahead of waves that are computing (six A/B pairs: 0.3-1% on this kernel)
+    // Vector k of this lane: index idx = 64k + lane in the chunk, in row b when idx >= split,
+    // at view column `col`; it is read only when it exists and its row is valid.
+    auto col_of = [&](int idx) { return (off_a + idx - (idx >= split ? vpr : 0)) * kVec; };
+    auto fetch = [&](int k, Raw8<D>& dst) {
+        const int idx = k * kWave + lane;
+        const bool in_b = idx >= split;
+        if (idx < live && (in_b ? rb.valid : ra.valid))
+            load8<D, true>(in_b ? xb : xa, col_of(idx), lim, dst);
+    };
+
+    // the first loads issue at raised wave priority, so a wave that has its row constants
+    // gets its window in flight ahead of waves that are computing
     __builtin_amdgcn_s_setprio(1);
     Raw8<D> w[kLoads];
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        const int idx = k * kWave + lane;
-        const bool in_b = idx >= split;
-        const int64_t row = row_a + (in_b ? 1 : 0);
-        const int col = static_cast<int>(q0 + idx - row * vpr) * kVec;
-        if (q0 + idx < total && (in_b ? rb.valid : ra.valid))
-            load8<D, true>(logits + row * ld, col, lim, w[k]);
-    }
+    for (int k = 0; k < kLoads; ++k) fetch(k, w[k]);
     __builtin_amdgcn_s_setprio(0);
-    bool hit = false;
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        const int idx = k * kWave + lane;
-        const bool in_b = idx >= split;
-        if (q0 + idx < total && (in_b ? rb.valid : ra.valid))
-            hit = hit || below_threshold<D>(w[k], in_b ? rb.thr : ra.thr);
-    }
-    const bool deep = __any(hit);
+    for (int k0 = 0; k0 < NV; k0 += kLoads) {
+        bool hit = false;
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        const int idx = k * kWave + lane;
-        if (q0 + idx >= total) continue;
-        const bool in_b = idx >= split;
-        const int64_t row = row_a + (in_b ? 1 : 0);
-        const BwdRow r = in_b ? rb : ra;
-        const int col = static_cast<int>(q0 + idx - row * vpr) * kVec;
-        float d[kVec];
-        if (!r.valid) {
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) d[e] = 0.0f;
-        } else {
-            bwd_compute_store<D, SCALED>(r, w[k], deep, inv_t, col, lim, d);
+        for (int k = k0; k < k0 + kLoads; ++k) {
+            const int idx = k * kWave + lane;
+            const bool in_b = idx >= split;
+            if (idx < live && (in_b ? rb.valid : ra.valid))
+                hit = hit || below_threshold<D>(w[k - k0], in_b ? rb.thr : ra.thr);
         }
-        store8<D, true>(dlogits + row * ld_out, col, vpr * kVec, d);
+        const bool deep = __any(hit);
+#pragma unroll
+        for (int k = k0; k < k0 + kLoads; ++k) {
+            const int idx = k * kWave + lane;
+            const bool in_b = idx >= split;
+            const BwdRow r = in_b ? rb : ra;
+            const int col = col_of(idx);
+            float d[kVec];
+            if (idx < live && r.valid) {
+                bwd_compute_store<D, SCALED>(r, w[k - k0], deep, inv_t, col, lim, d);
+            } else {
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) d[e] = 0.0f;
+            }
+            if (k + kLoads < NV) fetch(k + kLoads, w[k - k0]);  // refill the freed slot
+            if (idx < live) store8<D, true>(in_b ? ob : oa, col, width, d);
+        }
     }
 }
+
+// Vectors per lane of the flat backward: 16 KiB per wave when the row holds at least one
+// full chunk, otherwise kLoads (a chunk must not span more than two rows).
+template <Dt D>
+constexpr int bwd_flat_nv() { return D == Dt::F32 ? kLoads : 2 * kLoads; }
 
 // --------------------------------------------------------------------- target check
 
@@ -482,10 +510,19 @@ const void* bwd_ptr(bool vin, bool vout) {
                 : reinterpret_cast<const void*>(&bwd_kernel<D, false, false, SCALED>);
 }
 
+template <Dt D, bool SCALED>
+const void* bwd_flat_ptr(int nv) {
+    constexpr int kWide = bwd_flat_nv<D>();
+    if (nv == kWide) return reinterpret_cast<const void*>(&bwd_flat_kernel<D, SCALED, kWide>);
+    return reinterpret_cast<const void*>(&bwd_flat_kernel<D, SCALED, kLoads>);
+}
+
+// flat_nv = 0 selects the (row, tile) kernel, otherwise the flat one with that many vectors
+// per lane.
 template <Dt D>
-const void* bwd_ptr(bool vin, bool vout, bool scaled, bool flat) {
-    if (flat) return scaled ? reinterpret_cast<const void*>(&bwd_flat_kernel<D, true>)
-                            : reinterpret_cast<const void*>(&bwd_flat_kernel<D, false>);
+const void* bwd_ptr(bool vin, bool vout, bool scaled, int flat_nv) {
+    if (flat_nv != 0)
+        return scaled ? bwd_flat_ptr<D, true>(flat_nv) : bwd_flat_ptr<D, false>(flat_nv);
     return scaled ? bwd_ptr<D, true>(vin, vout) : bwd_ptr<D, false>(vin, vout);
 }
 
@@ -633,14 +670,17 @@ logp_status_t logp_backward_ex(int32_t dtype, float inv_temperature, const void*
     const bool vout = vec_ok(dlogits, ld_out, eb);
     const bool scaled = inv_temperature != 1.0f;
     const bool flat = vin && vout && width % kVec == 0 && width >= kTile;
-    const void* k = dtype == LOGP_DTYPE_BF16 ? bwd_ptr<Dt::BF16>(vin, vout, scaled, flat)
-                    : dtype == LOGP_DTYPE_F16 ? bwd_ptr<Dt::F16>(vin, vout, scaled, flat)
-                                              : bwd_ptr<Dt::F32>(vin, vout, scaled, flat);
+    // vectors per lane of the flat kernel: its wide form needs a whole chunk in every row
+    const int wide = f32 ? bwd_flat_nv<Dt::F32>() : bwd_flat_nv<Dt::BF16>();
+    const int flat_nv = !flat ? 0 : width / kVec >= int64_t(kWave) * wide ? wide : kLoads;
+    const void* k = dtype == LOGP_DTYPE_BF16 ? bwd_ptr<Dt::BF16>(vin, vout, scaled, flat_nv)
+                    : dtype == LOGP_DTYPE_F16 ? bwd_ptr<Dt::F16>(vin, vout, scaled, flat_nv)
+                                              : bwd_ptr<Dt::F32>(vin, vout, scaled, flat_nv);
     float inv_t = inv_temperature;
     int li = static_cast<int>(lim);
     if (flat) {
         const int64_t vectors = n * (width / kVec);
-        const int64_t blocks = ceil_div(vectors, int64_t(kBwdWaves) * kWave * kLoads);
+        const int64_t blocks = ceil_div(vectors, int64_t(kBwdWaves) * kWave * flat_nv);
         if (blocks > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
         int vpr = static_cast<int>(width / kVec);
         void* args[] = {&logits, &ld, &n, &vpr, &li, &col_begin, &vocab_real, &inv_t, &targets,

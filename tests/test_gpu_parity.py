@@ -98,6 +98,26 @@ def test_small_shapes(spec):
     full_check(case)
 
 
+# Widths around the two forms of the flat backward (aligned 16-bit views): below 8192
+# columns a wave takes 8 vectors per lane, from 8192 on 16, so its chunk is exactly one row
+# at 8192 and crosses a row boundary above it.  Row counts leave a ragged last chunk.
+FLAT_WIDTHS = [(7, 4096), (5, 8184), (6, 8192), (9, 8200), (3, 24584)]
+
+
+@pytest.mark.parametrize("n,v", FLAT_WIDTHS, ids=[f"n{n}_v{v}" for n, v in FLAT_WIDTHS])
+def test_flat_backward_chunk_geometry(n, v):
+    case = random_case(n, v, sigma=3.0, seed=n + v, inactive_frac=0.2, ignore_frac=0.1,
+                       device=DEV)
+    _, _, stats, d, _, _ = full_check(case)  # aligned view: flat kernel, against the oracle
+    # the same rows in a view 6 bytes off alignment take the (row, tile) kernel: same bits
+    buf = torch.zeros((n, v + 11), dtype=case.logits.dtype, device=DEV)
+    buf[:, 3:3 + v] = case.logits
+    d2 = dst.logp_backward(buf[:, 3:3 + v], case.targets, case.grad, stats, v, v,
+                           active=case.active)
+    torch.cuda.synchronize()
+    assert torch.equal(d.view(torch.int16), d2.view(torch.int16))
+
+
 def test_rows_of_minus_inf_and_masked_tails():
     n, v = 6, 9000
     x = torch.randn((n, v)) * 3
