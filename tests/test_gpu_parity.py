@@ -147,8 +147,11 @@ def test_rows_of_minus_inf_and_masked_tails():
                 bits_of(d[2:]), "minus-inf rows")
 
 
-def test_invalid_rows_do_not_read_logits():
-    case = random_case(8, 5000, sigma=3.0, seed=3, device=DEV)
+@pytest.mark.parametrize("v", [5000, 8200, 24584])
+def test_invalid_rows_do_not_read_logits(v):
+    # 5000 columns: 8 vectors per lane on the flat path; 8200 and 24584: 16, with chunks that
+    # start in a valid row and end in a poisoned one and the reverse
+    case = random_case(8, v, sigma=3.0, seed=3, device=DEV)
     case.targets[[1, 4]] = -100
     case.active = torch.ones(8, dtype=torch.uint8, device=DEV)
     case.active[6] = 0
