@@ -229,19 +229,40 @@ __device__ __forceinline__ int wave_id() {
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 
 
-// Pairwise tree over lanes 0..63 in index order: partners at xor 1, 2, 4, 8, 16, 32.
-// After each step both partners hold the same value (max and + are commutative), so every
-// lane ends with identical bits.
+// Pairwise tree over lanes 0..63 in index order: level k combines the aligned groups of
+// 2^k lanes pairwise (the xor-1, 2, 4, 8, 16, 32 butterfly).  After each level every lane of
+// a group holds the group's value (max and + are commutative, so both partners compute the
+// same bits), which lets a lane take its partner value from ANY lane of the sibling group:
+// DPP quad permutes for levels 1-2, the half-row and row mirrors for levels 3-4, and gfx950's
+// permlane16 / permlane32 swaps (which hand every lane the even and odd row of its 32-lane
+// half, then the low and high half of the wave) for levels 5-6.  Every lane ends with the
+// xor butterfly's bits, without a round trip through the LDS crossbar per level.
+template <int CTRL>
+__device__ __forceinline__ float dpp_lanes(float v) {
+    return __uint_as_float(
+        __builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+
+template <typename Op>
+__device__ __forceinline__ float wave_tree(float v, Op op) {
+    v = op(v, dpp_lanes<0xB1>(v));   // quad_perm [1,0,3,2]: the other lane of the pair
+    v = op(v, dpp_lanes<0x4E>(v));   // quad_perm [2,3,0,1]: the other pair of the quad
+    v = op(v, dpp_lanes<0x141>(v));  // row_half_mirror: the other quad of the 8
+    v = op(v, dpp_lanes<0x140>(v));  // row_mirror: the other 8 of the 16-lane row
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));  // even row, odd row of the 32
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return op(__uint_as_float(h[0]), __uint_as_float(h[1]));  // low half, high half
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    return wave_tree(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v = v + __shfl_xor(v, o, kWave);
-    return v;
+    return wave_tree(v, [](float a, float b) { return a + b; });
 }
 
 // ------------------------------------------------------------------ exp / log
