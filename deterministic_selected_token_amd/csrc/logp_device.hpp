@@ -236,7 +236,8 @@ __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) 
 // DPP quad permutes for levels 1-2, the half-row and row mirrors for levels 3-4, and gfx950's
 // permlane16 / permlane32 swaps (which hand every lane the even and odd row of its 32-lane
 // half, then the low and high half of the wave) for levels 5-6.  Every lane ends with the
-// xor butterfly's bits, without a round trip through the LDS crossbar per level.
+// xor butterfly's bits, without a round trip through the LDS crossbar per level.  Callers run
+// it in wave-uniform control flow, all 64 lanes active: the permutes read every lane.
 template <int CTRL>
 __device__ __forceinline__ float dpp_lanes(float v) {
     return __uint_as_float(
