@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void bwd_flat_kernel(
     // Workgroups take the chunks from the end of the view backwards: after a forward, which
     // streams the rows in order, the first chunks read are the ones the memory-side cache
     // still holds, and the next forward starts on the rows this kernel touched last
-    // (1-2% on the backward inside a step at 32768 x 151936).
+    // (about 1% on the backward inside a step at 32768 x 151936).
     const uint32_t blk = gridDim.x - 1 - blockIdx.x;
     const int64_t q0 = (int64_t(blk) * kBwdWaves + wave_id()) * kChunk;
     if (q0 >= total) return;  // whole wave leaves; this kernel has no barrier
