@@ -76,6 +76,17 @@ def git_sha() -> str:
         return ""
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, target_seconds: float) -> dict:
     """The FP64 oracle (as it stands) on a bounded sample of the workload's rows."""
     import numpy as np
@@ -86,14 +97,14 @@ def cpu_baseline(case, target_seconds: float) -> dict:
     n = case.n
     v = case.vocab_real
 
-    def run(rows):
+    def run(rows, nthreads=threads):
         idx = np.linspace(0, n - 1, rows).astype(np.int64)
         host = case.logits[idx].cpu()
         y = case.targets[idx].cpu().numpy()
         g = case.grad[idx].cpu().numpy()
         t0 = time.perf_counter()
-        oracle.forward(host, y, v, nthreads=threads)
-        oracle.backward(host, y, g, v, want_f64=False, want_bf16=True, nthreads=threads)
+        oracle.forward(host, y, v, nthreads=nthreads)
+        oracle.backward(host, y, g, v, want_f64=False, want_bf16=True, nthreads=nthreads)
         return time.perf_counter() - t0
 
     rows = 16
@@ -104,10 +115,17 @@ def cpu_baseline(case, target_seconds: float) -> dict:
     fwd_b, bwd_b = algorithmic_bytes(rows, rows, v, v, False)
     full_fwd, full_bwd = algorithmic_bytes(n, n, v, v, False)
     gbs = (fwd_b + bwd_b) / dt / 1e9
+    # one thread on 256 rows of the same workload
+    rows1 = min(n, 256)
+    dt1 = run(rows1, nthreads=1)
+    f1, b1 = algorithmic_bytes(rows1, rows1, v, v, False)
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {n} rows of the same workload, FP64 forward + backward "
                       f"(dlogits rounded to BF16), {dt:.2f} s wall",
-            "ms_per_step_extrapolated": round((full_fwd + full_bwd) / (gbs * 1e9) * 1e3, 1)}
+            "ms_per_step_extrapolated": round((full_fwd + full_bwd) / (gbs * 1e9) * 1e3, 1),
+            "one_thread": {"value": round((f1 + b1) / dt1 / 1e9, 4), "unit": "GB/s",
+                           "rows": rows1, "seconds": round(dt1, 3)},
+            "cpu_model": cpu_model()}
 
 
 def time_variants(dst, case, stream, steps: int) -> dict:
