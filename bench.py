@@ -76,6 +76,12 @@ def git_sha() -> str:
         return ""
 
 
+def median(xs) -> float:
+    ys = sorted(xs)
+    k = len(ys) // 2
+    return ys[k] if len(ys) % 2 else 0.5 * (ys[k - 1] + ys[k])
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -552,6 +558,10 @@ def main() -> int:
                    "n": n, "vocab": v, "logits_dtype": "bf16", "grad_dtype": "bf16",
                    "fwd_ms": round(fwd_avg, 4), "bwd_ms": round(bwd_avg, 4),
                    "wall_ms_per_step": round(wall_ms, 4),
+                   "median_ms": {"fwd": round(median(fwd_ms), 4),
+                                 "bwd": round(median(bwd_ms), 4),
+                                 "step": round(median([f + b for f, b in zip(fwd_ms, bwd_ms)]),
+                                               4)},
                    "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_b},
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "step_extra_bytes_beyond_outputs": int(step_extra),
