@@ -479,9 +479,11 @@ def main() -> int:
     # peak memory of one step beyond the resident inputs and preallocated outputs: zero
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
+    free_before = torch.cuda.mem_get_info(dev)[0]  # hipMemGetInfo: device-wide free bytes
     step()
     torch.cuda.synchronize()
     step_extra = torch.cuda.max_memory_allocated() - base
+    free_change = free_before - torch.cuda.mem_get_info(dev)[0]
 
     print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -565,6 +567,11 @@ def main() -> int:
                    "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_b},
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "step_extra_bytes_beyond_outputs": int(step_extra),
+                   "device_free_bytes_change_over_step": int(free_change),
+                   # the pages' peak-memory figure: from before the step, the returned BF16
+                   # gradient included
+                   "peak_gib_incl_returned_grad": round(
+                       (step_extra + dlogits.numel() * dlogits.element_size()) / 2**30, 3),
                    "device": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "torch": torch.__version__, "hip": torch.version.hip, "git": git_sha(),
                    "vs_baseline_basis": "27.2 ms / ms_per_step: the pages' fused kernel, "
