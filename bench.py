@@ -134,6 +134,46 @@ def cpu_baseline(case, target_seconds: float) -> dict:
             "cpu_model": cpu_model()}
 
 
+def time_pages_bench(dst, stream, steps: int) -> dict:
+    """The headline shape on the pages' own bench inputs (randn logits, sigma 1; uniform
+    targets; g = 1 on every row), for comparability with their timings."""
+    import torch
+
+    from workloads import headline_case
+
+    case = headline_case(device=torch.device("cuda", 0), pages_bench=True)
+    n, v = case.n, case.vocab_real
+    x, y, g = case.logits, case.targets, case.grad
+    d = torch.empty((n, v), dtype=torch.bfloat16, device=x.device)
+    logp = torch.empty(n, dtype=torch.float32, device=x.device)
+    lse = torch.empty_like(logp)
+    stats = torch.empty((n, 2), dtype=torch.float32, device=x.device)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dst.logp_forward(x, y, v, v, logp=logp, lse=lse, stats=stats, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dst.logp_backward(x, y, g, stats, v, v, dlogits=d, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(3):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    fwd = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    bwd = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+    total = evs[0][0].elapsed_time(evs[-1][2]) / steps
+    fb, bb = algorithmic_bytes(n, n, v, v, False)
+    del case, x, d
+    return {"fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "ms_per_step": round(total, 4),
+            "gbs": round((fb + bb) / (total * 1e-3) / 1e9, 1)}
+
+
 def time_variants(dst, case, stream, steps: int) -> dict:
     """fwd / bwd times of the _ex entry points for FP16, FP32 and a temperature of 0.7 on the
     headline rows (FP16 / FP32 logits are the BF16 values widened: the same data)."""
@@ -426,7 +466,8 @@ def main() -> int:
                     help="also time logp_partials (4 shards) + logp_merge")
     ap.add_argument("--variants", action="store_true",
                     help="also time FP16 and FP32 logits and BF16 at temperature 0.7 on the "
-                         "same shape, a GRPO step and the GRPO loss alone (reported under "
+                         "same shape, the same shape on the pages' bench inputs (sigma 1, "
+                         "g = 1), a GRPO step and the GRPO loss alone (reported under "
                          "config.variants)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="run a 4 GiB device copy after the timed region (counter scaling)")
@@ -523,6 +564,7 @@ def main() -> int:
                                "merge_ms": round(e[1].elapsed_time(e[2]), 4)}
     if args.variants:
         extra["variants"] = time_variants(dst, case, stream, args.steps)
+        extra["variants"]["bf16_pages_bench_inputs"] = time_pages_bench(dst, stream, args.steps)
         extra["variants"].update(time_grpo(dst, case, stream, args.steps))
         extra["variants"]["linear_logp_fwd"] = time_linear(dst, stream, max(3, args.steps // 4))
         extra["variants"]["linear_logp_fwd_temperature_0.7"] = time_linear(
