@@ -474,9 +474,10 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by rows or vocab tiles without any exchange in the hot loop, "
-              "see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by rows, or by vocabulary tiles with one all-gather of the per-tile "
+              "partials, and a several-GPU run is not part of this benchmark",
+              file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: run as a single process (WORLD_SIZE > 1 is not supported)",
