@@ -118,31 +118,39 @@ def test_flat_backward_chunk_geometry(n, v):
     assert torch.equal(d.view(torch.int16), d2.view(torch.int16))
 
 
-@pytest.mark.parametrize("v", [1024, 8200, 151936])
-def test_uniform_rows_gradient_bits(v):
+UNIFORM = [(1024, "bf16"), (8200, "bf16"), (151936, "bf16"), (8200, "f16"), (8200, "f32"),
+           (151936, "f32")]
+
+
+@pytest.mark.parametrize("v,dt", UNIFORM, ids=[f"v{v}_{dt}" for v, dt in UNIFORM])
+def test_uniform_rows_gradient_bits(v, dt):
     """On a row of equal logits every exp(z - M) is exp(0) = 1 and S = V exactly, so the
     backward's bits are fixed by float32 arithmetic alone: every column gets
-    RNE_bf16(-fl32(g / V)) and the target RNE_bf16(fl32(g - fl32(g / V)))."""
+    round(-fl32(g / V)) and the target round(fl32(g - fl32(g / V))), rounded to nearest even
+    in the logits' dtype.  Rows with a negative maximum take the general path for FP32
+    logits (the fast two-sum needs M >= 0), which must give the same bits."""
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
     n = 12
     rng = np.random.default_rng(v)
     c = torch.from_numpy(rng.normal(0.0, 3.0, size=(n, 1)).astype(np.float32))
-    x = c.expand(n, v).to(torch.bfloat16).contiguous()
+    x = c.expand(n, v).to(tdt).contiguous()
     y = rng.integers(0, v, size=n)
     g = rng.normal(0.0, 1.0, size=n).astype(np.float32)
-    say(f"uniform rows: n={n} V={v}")
+    say(f"uniform rows: n={n} V={v} {dt}")
     logits = x.to(DEV)
     yt = torch.from_numpy(y).to(DEV)
     gt = torch.from_numpy(g).to(DEV)
-    _, _, stats = dst.logp_forward(logits, yt)
-    d = dst.logp_backward(logits, yt, gt, stats)
+    _, _, stats = dst.logp_forward_ex(logits, yt)
+    d = dst.logp_backward_ex(logits, yt, gt, stats)
     torch.cuda.synchronize()
     assert torch.all(stats[:, 1].cpu() == float(v))
     neg = -(g / np.float32(v))                       # float32 division, rounded once
     at_target = (g + neg).astype(np.float32)
     want = np.repeat(neg[:, None], v, axis=1)
     want[np.arange(n), y] = at_target
-    want_bits = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16)  # RNE
-    assert torch.equal(d.cpu().view(torch.int16), want_bits)
+    want_t = torch.from_numpy(want).to(tdt)          # round to nearest even
+    assert torch.equal(d.cpu().view(torch.int16 if dt != "f32" else torch.int32),
+                       want_t.view(torch.int16 if dt != "f32" else torch.int32))
 
 
 def test_rows_of_minus_inf_and_masked_tails():
