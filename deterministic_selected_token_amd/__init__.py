@@ -252,21 +252,41 @@ def logp_backward_ex(logits: torch.Tensor, targets: torch.Tensor, grad_logp: tor
                      inv_temperature)
 
 
+def _shard_slot(partials: torch.Tensor, n: int, col_begin: int, col_end: int) -> int:
+    """Slot of tile col_begin / TILE_COLS in the float32 [n, L, 3] partials buffer, after
+    checking that every tile of the shard [col_begin, col_end) has its slot inside the
+    buffer.  The C side sees only the first slot and the row stride, so a buffer with too
+    few tiles per row would let one row's entries run into the next row's."""
+    if not isinstance(partials, torch.Tensor) or partials.dim() != 3 \
+            or partials.shape[0] != n or partials.shape[2] != 3 \
+            or partials.dtype != torch.float32 or partials.stride(2) != 1 \
+            or partials.stride(1) != 3:
+        raise ValueError("partials must be float32 [n, L, 3] with packed triples")
+    col_begin, col_end = int(col_begin), int(col_end)
+    if col_begin < 0 or col_begin % TILE_COLS != 0:
+        raise ValueError("col_begin must be a non-negative tile boundary")
+    first = col_begin // TILE_COLS
+    tiles = max(1, -(-(col_end - col_begin) // TILE_COLS))
+    if first + tiles > partials.shape[1]:
+        raise ValueError(f"the shard's tiles {first}..{first + tiles - 1} run past the "
+                         f"{partials.shape[1]} tiles per row of the partials buffer")
+    return first
+
+
 def _partials(fn: str, logits, targets, vocab_real, vocab_padded, col_begin, col_end, partials,
               active, ignore_index, stream, inv_temperature):
     ex = fn.endswith("_ex")
+    if not isinstance(logits, torch.Tensor):
+        raise TypeError("logits must be a torch.Tensor")
+    slot = _shard_slot(partials, logits.shape[0], col_begin, col_end)
     logits = _matrix("logits", logits, tuple(DTYPES) if ex else torch.bfloat16)
     n = logits.shape[0]
     dev = logits.device
     targets = _rows("targets", targets, torch.int64, n, dev)
     active = _active(active, n, dev)
-    if partials.dim() != 3 or partials.shape[0] != n or partials.shape[2] != 3 \
-            or partials.dtype != torch.float32 or partials.device != dev \
-            or partials.stride(2) != 1 or partials.stride(1) != 3:
-        raise ValueError("partials must be float32 [n, L, 3] with packed triples")
-    if col_begin % TILE_COLS != 0 or col_begin // TILE_COLS >= partials.shape[1]:
-        raise ValueError("col_begin must be a tile boundary inside the partials buffer")
-    first = partials[:, col_begin // TILE_COLS]
+    if partials.device != dev:
+        raise ValueError(f"partials is on {partials.device}, logits on {dev}")
+    first = partials[:, slot]
     ldp = partials.stride(0) // 3 if partials.stride(0) % 3 == 0 else -1
     args = (_ptr(logits), _ld(logits), n, int(vocab_real), int(vocab_padded), int(col_begin),
             int(col_end), _ptr(targets), _ptr(active), int(ignore_index), first.data_ptr(), ldp,

@@ -174,8 +174,14 @@ __global__ __launch_bounds__(kMergeWaves* kWave) void merge_kernel(
 // --------------------------------------------------------------------------- backward
 
 // Per-row constants of the backward.
-// z - M is exact for unscaled BF16 / FP16 values (short significands, and M is one of
-// them); otherwise its rounding error is carried into the exponential.
+// For unscaled BF16 / FP16 values, z - M is exact in FP32 whenever z = 0 or |z| and |M| lie
+// within a factor of about 2^15 (BF16) or 2^12 (FP16) of each other: the exact difference
+// then needs at most 24 significant bits.  Outside that (a logit very close to zero in a
+// row whose max is far from zero, or far below a small max) the FP32 difference t carries
+// up to half an FP32 spacing of t, so exp(t) is off by at most 2^-24 |t| relative (about
+// 8 FP32 ulps at |t| = 30): far below the 2^-9 spacing of the BF16 result, though it can
+// move a value that lies within that distance of a rounding boundary.  FP32 and scored
+// logits carry the rounding error of t into the exponential instead.
 template <Dt D, bool SCALED>
 __host__ __device__ constexpr bool bwd_two_sum() {
     return SCALED || D == Dt::F32;

@@ -19,8 +19,8 @@ from typing import Optional
 
 import torch
 
-from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _stream, logp_merge,
-               logp_num_tiles)
+from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _shard_slot, _stream,
+               logp_merge, logp_num_tiles)
 
 EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex", "linear_logp_backward",
             "linear_logp_backward_ex", "linear_logp_backward_workspace")
@@ -67,6 +67,9 @@ def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: to
     """Write the (m, s, sel) partials of vocab columns [col_begin, col_end) of the scored
     logits fl32(h W^T * inv_temperature) into the full ``partials`` buffer; ``weight`` is the
     row slice W[col_begin:col_end].  inv_temperature = 1 calls the plain entry point."""
+    if not isinstance(hidden, torch.Tensor):
+        raise TypeError("hidden must be a torch.Tensor")
+    slot = _shard_slot(partials, hidden.shape[0], col_begin, col_end)
     hidden = _bf16_rows("hidden", hidden)
     dev = hidden.device
     weight = _bf16_rows("weight", weight, dev)
@@ -75,16 +78,12 @@ def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: to
         raise ValueError("hidden and weight must have the same hidden size")
     targets = _rows("targets", targets, torch.int64, n, dev)
     active = _active(active, n, dev)
-    if partials.dim() != 3 or partials.shape[0] != n or partials.shape[2] != 3 \
-            or partials.dtype != torch.float32 or partials.device != dev \
-            or partials.stride(2) != 1 or partials.stride(1) != 3:
-        raise ValueError("partials must be float32 [n, L, 3] with packed triples")
-    if col_begin % TILE_COLS != 0 or col_begin // TILE_COLS >= partials.shape[1]:
-        raise ValueError("col_begin must be a tile boundary inside the partials buffer")
+    if partials.device != dev:
+        raise ValueError(f"partials is on {partials.device}, hidden on {dev}")
     rows_needed = max(0, min(col_end, vocab_real) - col_begin)
     if weight.shape[0] < rows_needed:
         raise ValueError(f"weight holds {weight.shape[0]} rows, the range needs {rows_needed}")
-    first = partials[:, col_begin // TILE_COLS]
+    first = partials[:, slot]
     ldp = partials.stride(0) // 3 if partials.stride(0) % 3 == 0 else -1
     args = (_ptr(hidden), _row_stride(hidden), n, H, _ptr(weight), _row_stride(weight),
             int(vocab_real), int(vocab_padded), int(col_begin), int(col_end), _ptr(targets),

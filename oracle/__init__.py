@@ -11,9 +11,10 @@ marshals numpy arrays into it.
 
 Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``):
   forward, backward, tile_partials (BF16, FP16 and FP32 logits; any inv_temperature),
-  merge, rne_bf16, rne_f16, count_bad_targets, backward_elements: pinned.
-  Rows whose valid target logit is -inf while other logits are finite, and rows that
-  hold NaN or +inf logits: parity unpinned (no closed form was written for them).
+  merge, rne_bf16, rne_f16, count_bad_targets, backward_elements: pinned.  Rows whose
+  valid target logit is -inf while other logits are finite are pinned by the 50-digit
+  brute force, whose alphabet holds -inf.
+  Rows that hold NaN or +inf logits: parity unpinned (no closed form was written for them).
 
 ``grpo_oracle.py`` (plain numpy, float64) is the oracle of the GRPO loss on these
 log-probabilities; its pins are in ``tests/test_grpo_oracle_pins.py``.

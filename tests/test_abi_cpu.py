@@ -207,6 +207,29 @@ def test_binding_rejects_cpu_tensors_without_calling_the_library():
         dst.logp_forward(x.float(), y)
 
 
+def test_binding_rejects_partials_too_narrow_for_the_shard():
+    """The C side sees the shard's first partials slot and the row stride only, so the
+    binding must check that the shard's last tile still has a slot in the row: [20T, 39T)
+    into a buffer of 30 tiles per row would write row t's tiles 30..38 over row t + 1."""
+    import torch
+    n = 2
+    x = torch.zeros((n, 19 * T), dtype=torch.bfloat16)
+    y = torch.zeros(n, dtype=torch.int64)
+    for width in (30, 38):
+        with pytest.raises(ValueError, match="run past"):
+            dst.logp_partials(x, y, 39 * T, 39 * T, 20 * T, 39 * T,
+                              torch.zeros((n, width, 3)))
+    with pytest.raises(ValueError, match="run past"):  # a ragged last tile needs its slot too
+        dst.logp_partials_ex(x[:, :T + 5], y, 21 * T + 5, 21 * T + 5, 20 * T, 21 * T + 5,
+                             torch.zeros((n, 21, 3)))
+    # wide enough: the shape checks pass and the next check (device memory) fails
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dst.logp_partials(x, y, 39 * T, 39 * T, 20 * T, 39 * T, torch.zeros((n, 39, 3)))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dst.logp_partials_ex(x[:, :T + 5], y, 21 * T + 5, 21 * T + 5, 20 * T, 21 * T + 5,
+                             torch.zeros((n, 22, 3)))
+
+
 def test_product_path_never_imports_the_oracle():
     for dirpath, _, files in os.walk(PKG):
         for f in files:

@@ -142,3 +142,18 @@ def test_binding_rejects_cpu_and_wrong_dtype():
         linear.linear_logp_forward(h, h, torch.zeros(2, dtype=torch.int64))
     with pytest.raises(TypeError):
         linear.linear_logp_forward(h.float(), h, torch.zeros(2, dtype=torch.int64))
+
+
+def test_binding_rejects_partials_too_narrow_for_the_shard():
+    import torch
+    T = linear.TILE_COLS
+    n, H = 2, 8
+    h = torch.zeros((n, H), dtype=torch.bfloat16)
+    w = torch.zeros((19 * T, H), dtype=torch.bfloat16)
+    y = torch.zeros(n, dtype=torch.int64)
+    with pytest.raises(ValueError, match="run past"):
+        linear.linear_logp_partials(h, w, y, 39 * T, 39 * T, 20 * T, 39 * T,
+                                    torch.zeros((n, 30, 3)))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        linear.linear_logp_partials(h, w, y, 39 * T, 39 * T, 20 * T, 39 * T,
+                                    torch.zeros((n, 39, 3)))
