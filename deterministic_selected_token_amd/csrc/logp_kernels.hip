@@ -247,10 +247,14 @@ __device__ __forceinline__ bool below_threshold(const Raw8<D>& r, float thr) {
             const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(thr, thr);  // round toward zero
             t16 = __builtin_bit_cast(uint32_t, h) & 0xFFFFu;
         }
-        u16x2 mx = __builtin_elementwise_max(__builtin_bit_cast(u16x2, r.w.x),
-                                             __builtin_bit_cast(u16x2, r.w.y));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, r.w.z));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, r.w.w));
+        // The words are copied to plain scalars before the casts: hipcc's front end turns
+        // __builtin_bit_cast of a vector component (r.w.y) into a load from the vector's
+        // first component, which made this test look at 2 of the 8 values.
+        const uint32_t q[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+        u16x2 mx = __builtin_elementwise_max(__builtin_bit_cast(u16x2, q[0]),
+                                             __builtin_bit_cast(u16x2, q[1]));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, q[2]));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, q[3]));
         return mx.x > t16 || mx.y > t16;
     }
 }

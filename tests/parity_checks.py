@@ -5,9 +5,14 @@ Tolerances (written here, used by every GPU parity test):
     the selected-token logp.  Row max M is compared exactly (a max of BF16 values is
     exact in FP32); S to 2e-5 relative (FP32 sums of up to ~1.5e5 exp terms).
   * dlogits (BF16, and FP16 outputs of FP16 logits): at least 99.99% of all
-    N x vocab_real elements equal the round-to-nearest-even of the FP64 value in the output
-    dtype, up to two elements of slack on small samples (FP32 outputs: every element within
-    16 FP32 spacings instead, the FP32 row sum S carrying a few spacings of shared error); the largest |gpu - d64| is at most
+    N x vocab_real BF16 elements equal the round-to-nearest-even of the FP64 value; for FP16
+    outputs at least 1 - 2^-10 of them.  The FP32 value the kernels round carries up to
+    about 4 FP32 spacings of error (g/S, the exponential, the product), so an output lands
+    on the wrong side of a rounding boundary with probability up to 2 * 2^-21 / 2^-10 =
+    2^-10 for FP16's 11 significant bits, and 2^-13 for BF16's 8 (FP32 outputs: every
+    element within 16 FP32 spacings instead, the FP32 row sum S carrying a few spacings of
+    shared error).  The number of elements that are not correctly rounded is printed for
+    every case; the largest |gpu - d64| is at most
     max(1.5e-3 * max|d64|, 1.01 * E_floor), where E_floor = max|RNE(d64) - d64| is the
     error a perfectly rounded BF16 output already has (the pages show every correct
     implementation sharing that floor: the fused-backward pull request, author reply
@@ -27,7 +32,8 @@ import oracle
 
 LOGP_TOL = 1e-4
 SUMEXP_RTOL = 2e-5
-CORRECTLY_ROUNDED_MIN = 0.9999
+CORRECTLY_ROUNDED_MIN = 0.9999            # BF16 outputs
+CORRECTLY_ROUNDED_MIN_F16 = 1.0 - 2.0 ** -10  # FP16 outputs (see above)
 MAXERR_RATIO = 1.5e-3
 
 
@@ -108,6 +114,7 @@ class BackwardTally:
     max_err: float = 0.0
     max_ref: float = 0.0
     floor: float = 0.0
+    dtype: str = ""
     notes: list = field(default_factory=list)
 
     def add_block(self, logits_host, targets, grad, vocab_real, vocab_padded, active,
@@ -119,6 +126,7 @@ class BackwardTally:
                               inv_temperature=inv_temperature)
         d64, rb = ref["d64"], ref["rounded"]
         dt = {np.uint16: "bf16", np.float16: "f16", np.float32: "f32"}[rb.dtype.type]
+        self.dtype = dt
         gpu_vals = np.asarray(gpu_vals)[:, :vocab_padded]
         assert gpu_vals.dtype == rb.dtype, (what, gpu_vals.dtype, rb.dtype)
         gv = as_f64(gpu_vals, dt)
@@ -149,15 +157,23 @@ class BackwardTally:
         assert not bad.any(), (what, np.argwhere(bad)[:5].tolist(),
                                err[bad][:5].tolist(), allow[bad][:5].tolist())
 
-    def finish(self, what: str = "", min_correctly_rounded: float = CORRECTLY_ROUNDED_MIN) -> dict:
+    def finish(self, what: str = "", min_correctly_rounded: float | None = None) -> dict:
+        """Check the accumulated counts; the correctly-rounded bar defaults to the output
+        dtype's (BF16 99.99%, FP16 1 - 2^-10, FP32 none: its per-element bound applies)."""
+        if min_correctly_rounded is None:
+            min_correctly_rounded = {"bf16": CORRECTLY_ROUNDED_MIN,
+                                     "f16": CORRECTLY_ROUNDED_MIN_F16}.get(self.dtype, 0.0)
         frac = self.correctly_rounded / max(1, self.elements)
         gate = max(MAXERR_RATIO * self.max_ref, 1.01 * self.floor)
         out = {"elements": self.elements, "correctly_rounded": frac,
                "max_err": self.max_err, "max_ref": self.max_ref, "floor": self.floor,
                "max_err_over_max": self.max_err / self.max_ref if self.max_ref else 0.0,
                "floor_over_max": self.floor / self.max_ref if self.max_ref else 0.0}
-        # a slack of two elements keeps the fraction meaningful on small samples
         misrounded = self.elements - self.correctly_rounded
-        assert misrounded <= (1.0 - min_correctly_rounded) * self.elements + 2, (what, out)
+        out["misrounded"] = misrounded
+        print(f"[tally] {what}: {misrounded} of {self.elements} {self.dtype} elements not "
+              f"correctly rounded; max err / max {out['max_err_over_max']:.3e} "
+              f"(floor {out['floor_over_max']:.3e})", flush=True)
+        assert misrounded <= (1.0 - min_correctly_rounded) * self.elements, (what, out)
         assert self.max_err <= gate, (what, out)
         return out

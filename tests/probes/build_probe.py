@@ -1,4 +1,5 @@
-"""Build the test probe library tests/probes/libexp2_probe.so (hipcc, gfx950)."""
+"""Build the probe libraries next to this file (hipcc, gfx950): libexp2_probe.so (the tests'
+hardware-exp2 check) and libhbm_ceiling.so (the bench's read and copy ceilings)."""
 
 from __future__ import annotations
 
@@ -12,17 +13,23 @@ sys.path.insert(0, ROOT)
 
 from deterministic_selected_token_amd import build as lib_build  # noqa: E402
 
-SRC = os.path.join(HERE, "exp2_probe.hip")
+PROBES = {"libexp2_probe.so": "exp2_probe.hip", "libhbm_ceiling.so": "hbm_ceiling.hip"}
 OUT = os.path.join(HERE, "libexp2_probe.so")
+CEILING = os.path.join(HERE, "libhbm_ceiling.so")
 
 
-def build() -> str:
+def build() -> list[str]:
     flags = [f for f in lib_build.HIPCC_FLAGS if f != "-fvisibility=hidden"]
-    tmp = OUT + f".tmp{os.getpid()}"
-    subprocess.run([lib_build.hipcc(), *flags, "-o", tmp, SRC], check=True)
-    os.replace(tmp, OUT)
-    return OUT
+    built = []
+    for lib, src in PROBES.items():
+        out = os.path.join(HERE, lib)
+        tmp = out + f".tmp{os.getpid()}"
+        subprocess.run([lib_build.hipcc(), *flags, "-o", tmp, os.path.join(HERE, src)],
+                       check=True)
+        os.replace(tmp, out)
+        built.append(out)
+    return built
 
 
 if __name__ == "__main__":
-    print(build())
+    print("\n".join(build()))

@@ -48,7 +48,7 @@ def case_in(dtype: str, n, v, p=None, ld=None, sigma=3.0, seed=0, **kw):
     return c.to(DEV)
 
 
-def check_ex(case, inv_t=1.0, rows=None, ulps=1.0, min_cr=0.9999):
+def check_ex(case, inv_t=1.0, rows=None, ulps=1.0, min_cr=None):
     x = case.logits[:, :case.vocab_padded]
     logp, lse, stats = dst.logp_forward_ex(x, case.targets, case.vocab_real, case.vocab_padded,
                                            active=case.active, inv_temperature=inv_t)
@@ -94,7 +94,7 @@ DT_SHAPES = [(6, 1), (12, 255), (9, 1031), (16, 10000), (24, 151936)]
 def test_fp16_fp32_logits_parity(dtype, n, v):
     case = case_in(dtype, n, v, seed=v % 97, ignore_frac=0.1, bad_target_frac=0.1)
     say(f"{dtype} logits n={n} V={v}")
-    ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, 0.9999)
+    ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, None)
     _, fwd, bwd = check_ex(case, ulps=ulps, min_cr=min_cr)
     say(f"{dtype} V={v}: {fwd} {bwd}")
 
@@ -105,7 +105,7 @@ def test_temperature_parity(dtype, inv_t):
     case = case_in(dtype, 20, 12345, 12800, sigma=2.0, seed=7, pad_fill=50.0,
                    inactive_frac=0.1, ignore_frac=0.1)
     say(f"{dtype} logits, inv_temperature={inv_t:.4f}")
-    ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, 0.9999)
+    ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, None)
     _, fwd, bwd = check_ex(case, inv_t=inv_t, ulps=ulps, min_cr=min_cr)
     say(f"{dtype} inv_t={inv_t:.4f}: {fwd} {bwd}")
 
@@ -189,7 +189,7 @@ def test_subnormal_gradients_fp16_and_fp32():
     for dtype in ("f16", "f32"):
         case = case_in(dtype, 6, 20000, sigma=30.0, seed=19)
         say(f"{dtype} very spread logits")
-        ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, 0.9999)
+        ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, None)
         check_ex(case, ulps=ulps, min_cr=min_cr)
 
 
@@ -205,6 +205,6 @@ def test_negative_max_and_wide_rows(dtype, inv_t):
     x[6:12, :20000] = (torch.rand((6, 20000), generator=gen) * 22.0 - 20.0).to(x.dtype).to(DEV)
     x[12, :20000] = (torch.rand(20000, generator=gen) * 0.5 - 0.25).to(x.dtype).to(DEV)
     say(f"negative max / wide rows {dtype} inv_t={inv_t:.3f}")
-    ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, 0.9999)
+    ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, None)
     _, fwd, bwd = check_ex(case, inv_t=inv_t, ulps=ulps, min_cr=min_cr)
     say(f"{dtype} inv_t={inv_t:.3f}: {fwd} {bwd}")

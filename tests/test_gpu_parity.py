@@ -182,6 +182,41 @@ def test_rows_of_minus_inf_and_masked_tails():
                 bits_of(d[2:]), "minus-inf rows")
 
 
+DEEP_ONE = [(8192, "bf16"), (8191, "bf16"), (8192, "f16"), (8191, "f16")]
+
+
+@pytest.mark.parametrize("v,dt", DEEP_ONE, ids=[f"v{v}_{dt}" for v, dt in DEEP_ONE])
+def test_one_deep_value_at_every_vector_position(v, dt):
+    """A row whose only logit below M - 87 (or only -inf) sits at position e = 0..7 of its
+    8-element vector: the test that sends a group of vectors to the general exponential path
+    must see every position.  On the fast path a -inf gives NaN and exp(z - M) below 2^-126
+    flushes to zero, where the BF16 result is a subnormal (g = 256 makes g/S about 1 here).
+    Width 8192 takes the flat backward, 8191 the (row, tile) kernel."""
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    n = 16
+    gen = torch.Generator().manual_seed(v)
+    x = torch.randn((n, v), generator=gen)
+    x[:, 100] = 12.0                          # a dominant logit: M = 12, S close to 1
+    cols = [8 * (37 + 3 * r) + (r % 8) for r in range(n)]
+    for r, c in enumerate(cols):
+        x[r, c] = float("-inf") if r >= 8 else 12.0 - 90.0
+    y = torch.randint(0, v, (n,), generator=gen)
+    y[3] = cols[3]                            # targets on a deep value and on a -inf
+    y[12] = cols[12]
+    g = torch.full((n,), 256.0)
+    logits = x.to(tdt).to(DEV)
+    say(f"one deep value per row: V={v} {dt}")
+    _, _, stats = dst.logp_forward_ex(logits, y.to(DEV))
+    d = dst.logp_backward_ex(logits, y.to(DEV), g.to(DEV), stats)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(d.float()))
+    t = BackwardTally()
+    gpu_vals = bits_of(d) if dt == "bf16" else d.cpu().numpy()
+    t.add_block(logits.cpu(), y.numpy(), g.numpy(), v, v, None, -100, gpu_vals,
+                f"one deep value, V={v} {dt}")
+    t.finish(f"one deep value, V={v} {dt}")
+
+
 @pytest.mark.parametrize("v", [5000, 8200, 24584])
 def test_invalid_rows_do_not_read_logits(v):
     # 5000 columns: 8 vectors per lane on the flat path; 8200 and 24584: 16, with chunks that
