@@ -11,11 +11,22 @@ torch.cuda.synchronize() and timed with HIP events on the stream the kernels run
 value = algorithmic bytes of one step / step time, in GB/s:
     forward  2*N*V (logits once) + 24*N (targets, logp, LSE, stats)
     backward 2*N_valid*V (logits once) + 2*N*V (dlogits) + 20*N (targets, g, stats)
-The roofline object reports the dominant kernel (the backward) against 8 TB/s.  The
-cpu_baseline object times the FP64 oracle on a bounded sample of the same rows.
+The roofline object reports the dominant kernel (the backward) against 8 TB/s and against
+the measured copy ceiling, the forward against 8 TB/s and the measured read ceiling (plain
+read and copy kernels of tests/probes/hbm_ceiling.hip, timed in the same run).
 
-Extra flags: --profile-copy adds a plain device copy of known size (for scaling the
-hardware byte counters), --shard-path also times logp_partials + logp_merge.
+Also in the default run, each under config: batch invariance of headline rows recomputed in
+smaller batches; one tensor-parallel rank's share (5 of 38 tiles of the headline rows);
+the mid-size workload (N=4096, padded vocabulary, 5% inactive rows); the vocab-shard
+workload (N=8192, 39 tiles, 1/2/4 shards + merge against the fused forward); N=131072; and
+the headline shape on the pages' bench inputs (sigma 1, g = 1).  The oracle leg runs the
+FP64 oracle on the headline rows and on the pages' inputs, compares the GPU's logp, LSE
+and dlogits with it block by block (top-level "accuracy") and reports its own rate
+("cpu_baseline").
+
+Extra flags: --headline-only (the timed headline step alone), --variants (FP16, FP32,
+temperature, GRPO, linear_logp), --profile-copy (a 4 GiB copy of known size at the end, for
+scaling the hardware byte counters).
 """
 
 from __future__ import annotations
@@ -93,85 +104,388 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(case, target_seconds: float) -> dict:
-    """The FP64 oracle (as it stands) on a bounded sample of the workload's rows."""
-    import numpy as np
-
-    import oracle
-
-    threads = oracle.default_threads()
-    n = case.n
-    v = case.vocab_real
-
-    def run(rows, nthreads=threads):
-        idx = np.linspace(0, n - 1, rows).astype(np.int64)
-        host = case.logits[idx].cpu()
-        y = case.targets[idx].cpu().numpy()
-        g = case.grad[idx].cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.forward(host, y, v, nthreads=nthreads)
-        oracle.backward(host, y, g, v, want_f64=False, want_bf16=True, nthreads=nthreads)
-        return time.perf_counter() - t0
-
-    rows = 16
-    dt = run(rows)
-    if dt < target_seconds / 4:
-        rows = int(min(n, max(rows, rows * target_seconds / max(dt, 1e-3))))
-        dt = run(rows)
-    fwd_b, bwd_b = algorithmic_bytes(rows, rows, v, v, False)
-    full_fwd, full_bwd = algorithmic_bytes(n, n, v, v, False)
-    gbs = (fwd_b + bwd_b) / dt / 1e9
-    # one thread on 256 rows of the same workload
-    rows1 = min(n, 256)
-    dt1 = run(rows1, nthreads=1)
-    f1, b1 = algorithmic_bytes(rows1, rows1, v, v, False)
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {n} rows of the same workload, FP64 forward + backward "
-                      f"(dlogits rounded to BF16), {dt:.2f} s wall",
-            "ms_per_step_extrapolated": round((full_fwd + full_bwd) / (gbs * 1e9) * 1e3, 1),
-            "one_thread": {"value": round((f1 + b1) / dt1 / 1e9, 4), "unit": "GB/s",
-                           "rows": rows1, "seconds": round(dt1, 3)},
-            "cpu_model": cpu_model()}
+CEILING_LIB = os.path.join(ROOT, "tests", "probes", "libhbm_ceiling.so")
+# (vectors of 16 bytes per lane, waves per workgroup); the forward's pattern is 8 vectors in
+# 4-wave workgroups, the backward's 16 vectors in 16-wave workgroups
+READ_SHAPES = ((8, 4), (16, 4), (16, 16), (32, 8))
+COPY_SHAPES = ((8, 16), (16, 16), (16, 8), (32, 8))
 
 
-def time_pages_bench(dst, stream, steps: int) -> dict:
-    """The headline shape on the pages' own bench inputs (randn logits, sigma 1; uniform
-    targets; g = 1 on every row), for comparability with their timings."""
+def load_ceiling_library():
+    import ctypes
+
+    lib = ctypes.CDLL(CEILING_LIB)  # built by __graft_entry__.build() with the test probes
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.hbm_read.argtypes = [P, I64, I32, I32, ctypes.c_uint32, P, P]
+    lib.hbm_read.restype = I32
+    lib.hbm_copy.argtypes = [P, P, I64, I32, I32, P]
+    lib.hbm_copy.restype = I32
+    return lib
+
+
+def hbm_ceiling(stream, gib: int = 10, reps: int = 6) -> dict:
+    """Measured HBM ceilings: a plain streaming read of `gib` GiB and a plain copy of `gib`
+    GiB each way (tests/probes/hbm_ceiling.hip, non-temporal 16-byte accesses), in several
+    wave shapes; GB/s counts the bytes read (read) or read + written (copy)."""
     import torch
 
-    from workloads import headline_case
+    lib = load_ceiling_library()
+    dev = torch.device("cuda", 0)
+    nbytes = gib << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.view(torch.int32).random_()
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    h = stream.cuda_stream
 
-    case = headline_case(device=torch.device("cuda", 0), pages_bench=True)
-    n, v = case.n, case.vocab_real
-    x, y, g = case.logits, case.targets, case.grad
-    d = torch.empty((n, v), dtype=torch.bfloat16, device=x.device)
-    logp = torch.empty(n, dtype=torch.float32, device=x.device)
+    def timed(call) -> float:
+        for _ in range(2):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return median([a.elapsed_time(b) for a, b in evs])
+
+    def check(rc: int):
+        if rc != 0:
+            raise RuntimeError(f"hbm ceiling probe failed ({rc})")
+
+    out = {"read_gbs": 0.0, "copy_gbs": 0.0, "bytes": nbytes,
+           "kernels": "tests/probes/hbm_ceiling.hip (hbm_read, hbm_copy)", "shapes": {}}
+    for nv, waves in READ_SHAPES:
+        ms = timed(lambda: check(lib.hbm_read(src.data_ptr(), nbytes, nv, waves, 0x9E3779B9,
+                                              sink.data_ptr(), h)))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["shapes"][f"read {nv} KiB/wave, {waves} waves/group"] = round(gbs, 1)
+        out["read_gbs"] = max(out["read_gbs"], round(gbs, 1))
+    for nv, waves in COPY_SHAPES:
+        ms = timed(lambda: check(lib.hbm_copy(src.data_ptr(), dst.data_ptr(), nbytes, nv, waves,
+                                              h)))
+        gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+        out["shapes"][f"copy {nv} KiB/wave, {waves} waves/group"] = round(gbs, 1)
+        out["copy_gbs"] = max(out["copy_gbs"], round(gbs, 1))
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def n_valid_rows(case) -> int:
+    """Rows that are active and whose target lies in [0, vocab_real), not ignore_index."""
+    import torch
+
+    y = case.targets
+    ok = (y >= 0) & (y < case.vocab_real) & (y != case.ignore_index)
+    if case.active is not None:
+        ok &= case.active != 0
+    return int(torch.count_nonzero(ok))
+
+
+def time_case(dst, case, stream, steps: int, warmup: int = 2, keep: bool = False) -> dict:
+    """Forward + backward of a workload through the library, HIP events on the launch
+    stream; algorithmic bytes count the logits once for the forward and once (valid rows)
+    for the backward, plus the dlogits write."""
+    import torch
+
+    n, v, p = case.n, case.vocab_real, case.vocab_padded
+    x = case.logits[:, :p]
+    dev = x.device
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
     lse = torch.empty_like(logp)
-    stats = torch.empty((n, 2), dtype=torch.float32, device=x.device)
+    stats = torch.empty((n, 2), dtype=torch.float32, device=dev)
+    d = torch.empty((n, p), dtype=x.dtype, device=dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        dst.logp_forward(x, y, v, v, logp=logp, lse=lse, stats=stats, stream=stream)
+        dst.logp_forward(x, case.targets, v, p, active=case.active, logp=logp, lse=lse,
+                         stats=stats, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        dst.logp_backward(x, y, g, stats, v, v, dlogits=d, stream=stream)
+        dst.logp_backward(x, case.targets, case.grad, stats, v, p, active=case.active,
+                          dlogits=d, stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(3):
+    for _ in range(warmup):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for k in range(steps):
-        step(evs[k])
     torch.cuda.synchronize()
-    fwd = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
-    bwd = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    f_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    b_ms = sum(b.elapsed_time(c) for _, b, c in evs) / steps
     total = evs[0][0].elapsed_time(evs[-1][2]) / steps
-    fb, bb = algorithmic_bytes(n, n, v, v, False)
-    del case, x, d
-    return {"fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "ms_per_step": round(total, 4),
-            "gbs": round((fb + bb) / (total * 1e-3) / 1e9, 1)}
+    fb, bb = algorithmic_bytes(n, n_valid_rows(case), v, p, case.active is not None)
+    out = {"n": n, "vocab_real": v, "vocab_padded": p, "fwd_ms": round(f_ms, 4),
+           "bwd_ms": round(b_ms, 4), "ms_per_step": round(total, 4),
+           "algorithmic_bytes": {"fwd": fb, "bwd": bb},
+           "gbs": round((fb + bb) / (total * 1e-3) / 1e9, 1),
+           "fwd_gbs": round(fb / (f_ms * 1e-3) / 1e9, 1),
+           "bwd_gbs": round(bb / (b_ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round((fb + bb) / (total * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "floor_ms_at_8tbs": round((fb + bb) / (HBM_PEAK_GBS * 1e9) * 1e3, 3)}
+    if keep:
+        out["_outputs"] = (logp, lse, stats, d)
+    return out
+
+
+SHARD_LAYOUTS = {1: (39,), 2: (20, 19), 4: (13, 13, 12, 1)}
+
+
+def time_shard_config(dst, stream, steps: int) -> dict:
+    """The vocab-parallel path on one GPU: N=8192 rows, vocabulary 151936 padded to 159744
+    (39 tiles, the last all padding), logp_partials over 1, 2 and 4 tile-aligned shards
+    (the last 4-shard slice is the all-padding identity) + logp_merge, against the fused
+    forward; the outputs must be bitwise equal."""
+    import torch
+
+    from workloads import shard_case
+
+    case = shard_case(device=torch.device("cuda", 0))
+    n, v, p = case.n, case.vocab_real, case.vocab_padded
+    x, y = case.logits, case.targets
+    L = dst.logp_num_tiles(p)
+
+    def timed(fn, reps):
+        fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+    ref = dst.logp_forward(x, y, v, p, stream=stream)
+    fused_ms = timed(lambda: dst.logp_forward(x, y, v, p, logp=ref[0], lse=ref[1],
+                                              stats=ref[2], stream=stream), steps)
+    fused_bytes = 2 * n * v + 24 * n
+    out = {"workload": "N=8192, vocabulary 151936 padded to 159744 (39 tiles), BF16 "
+                       "~N(0,3^2), uniform targets",
+           "fused_forward": {"ms": round(fused_ms, 4),
+                             "gbs": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1)}}
+    partials = torch.empty((n, L, 3), dtype=torch.float32, device=x.device)
+    for k, tiles in SHARD_LAYOUTS.items():
+        bounds, t0 = [], 0
+        for t in tiles:
+            bounds.append((t0 * dst.TILE_COLS, min((t0 + t) * dst.TILE_COLS, p)))
+            t0 += t
+        got = [torch.empty_like(r) for r in ref]
+
+        def shards():
+            for c0, c1 in bounds:
+                dst.logp_partials(x[:, c0:c1], y, v, p, c0, c1, partials, stream=stream)
+
+        def merge():
+            dst.logp_merge(partials, y, v, logp=got[0], lse=got[1], stats=got[2],
+                           stream=stream)
+
+        part_ms = timed(shards, steps)
+        merge_ms = timed(merge, steps)
+        torch.cuda.synchronize()
+        same = all(torch.equal(a.view(torch.int32), b.view(torch.int32))
+                   for a, b in zip(ref, got))
+        part_bytes = 2 * n * v + 12 * n * L + 8 * n * k
+        out[f"k{k}"] = {"tiles": list(tiles), "partials_ms": round(part_ms, 4),
+                        "merge_ms": round(merge_ms, 4),
+                        "ms": round(part_ms + merge_ms, 4),
+                        "partials_gbs": round(part_bytes / (part_ms * 1e-3) / 1e9, 1),
+                        "bitwise_equal_to_fused": bool(same)}
+    del case, x, partials
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_tp8_share(dst, case, stream, steps: int) -> dict:
+    """One rank's share at tensor-parallel degree 8 over the headline rows: 5 of the 38
+    tiles (20480 columns) of all 32768 rows, held contiguously as a rank holds its shard,
+    reduced to its partials by logp_partials."""
+    import torch
+
+    n, v = case.n, case.vocab_real
+    c1 = 5 * dst.TILE_COLS
+    xs = case.logits[:, :c1].contiguous()
+    partials = torch.empty((n, dst.logp_num_tiles(v), 3), dtype=torch.float32,
+                           device=xs.device)
+
+    def run():
+        dst.logp_partials(xs, case.targets, v, v, 0, c1, partials, stream=stream)
+
+    run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nbytes = 2 * n * c1 + 12 * n * 5 + 8 * n
+    del xs, partials
+    torch.cuda.empty_cache()
+    return {"rows": n, "tiles": 5, "columns": c1, "ms": round(ms, 4),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def batch_invariance(dst, case, outputs, stream) -> dict:
+    """Rows of the headline batch recomputed inside smaller batches (the first B rows, for
+    B = 1, 9, 129, 1025), compared bit for bit with the full batch's logp and dlogits."""
+    import torch
+
+    logp, _, _, d = outputs
+    v = case.vocab_real
+    diff_logp = diff_d = rows = 0
+    for b in (1, 9, 129, 1025):
+        x = case.logits[:b].clone()
+        lp, _, st = dst.logp_forward(x, case.targets[:b], v, v, stream=stream)
+        db = dst.logp_backward(x, case.targets[:b], case.grad[:b], st, v, v, stream=stream)
+        torch.cuda.synchronize()
+        diff_logp += int((lp.view(torch.int32) != logp[:b].view(torch.int32)).sum())
+        diff_d += int((db.view(torch.int16) != d[:b].view(torch.int16)).any(1).sum())
+        rows += b
+    return {"sub_batches": [1, 9, 129, 1025], "rows_compared": rows,
+            "logp_rows_differing": diff_logp, "dlogits_rows_differing": diff_d}
+
+
+def _pcts(err) -> dict:
+    import numpy as np
+
+    e = np.asarray(err, dtype=np.float64)
+    if e.size == 0:
+        return {"max": 0.0, "p99": 0.0, "p95": 0.0}
+    return {"max": float(e.max()), "p99": float(np.percentile(e, 99)),
+            "p95": float(np.percentile(e, 95))}
+
+
+def _compare_dlogits(gpu_bits, d64, rounded, threads: int):
+    """(elements, correctly rounded, max |gpu - d64|, max |d64|, max |RNE(d64) - d64|) of
+    BF16 dlogits blocks; ±0 count as equal.  Row chunks go to a thread pool (numpy releases
+    the GIL in these loops)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    def part(rs):
+        g, r, x = gpu_bits[rs], rounded[rs], d64[rs]
+        same = (g == r) | (((g | r) & 0x7FFF) == 0)
+        gv = (g.astype(np.uint32) << 16).view(np.float32)
+        rv = (r.astype(np.uint32) << 16).view(np.float32)
+        return (g.size, int(same.sum()), float(np.abs(gv - x).max()),
+                float(np.abs(x).max()), float(np.abs(rv - x).max()))
+
+    rows = gpu_bits.shape[0]
+    step = max(1, -(-rows // threads))
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        parts = list(pool.map(part, [slice(i, i + step) for i in range(0, rows, step)]))
+    return (sum(p[0] for p in parts), sum(p[1] for p in parts), max(p[2] for p in parts),
+            max(p[3] for p in parts), max(p[4] for p in parts))
+
+
+def oracle_leg(case, outputs, bwd_rows: int, threads: int, block: int = 512) -> dict:
+    """The FP64 oracle (as it stands) on the same inputs, compared with the GPU's outputs as
+    it goes: the forward on every row, the backward on `bwd_rows` evenly spaced rows (plus
+    every spike row of the headline workload), block by block.  Returns the oracle's wall
+    times and the accuracy of the GPU outputs against it."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    logp_g, lse_g, _, d_g = outputs
+    n, v = case.n, case.vocab_real
+    y_all = case.targets.cpu().numpy()
+    g_all = case.grad.cpu().numpy()
+    logp_h = logp_g.cpu().numpy().astype(np.float64)
+    lse_h = lse_g.cpu().numpy().astype(np.float64)
+    # forward on every row
+    t_fwd = 0.0
+    d_logp, d_lse = [], []
+    for r0 in range(0, n, 4 * block):
+        idx = torch.arange(r0, min(n, r0 + 4 * block), device=case.logits.device)
+        host = case.logits[idx].cpu()
+        rows = idx.cpu().numpy()
+        t0 = time.perf_counter()
+        ref = oracle.forward(host, y_all[rows], v, nthreads=threads)
+        t_fwd += time.perf_counter() - t0
+        fin = np.isfinite(ref["logp"])
+        d_logp.append(np.abs(logp_h[rows][fin] - ref["logp"][fin]))
+        d_lse.append(np.abs(lse_h[rows] - ref["lse"]))
+    # backward on a sample of rows
+    spikes = case.meta.get("spike_row_index", [])
+    sample = np.unique(np.concatenate([np.linspace(0, n - 1, bwd_rows).astype(np.int64),
+                                       np.asarray(spikes, dtype=np.int64)]))
+    t_bwd = 0.0
+    tot = [0, 0, 0.0, 0.0, 0.0]
+    for r0 in range(0, sample.size, block):
+        rows = sample[r0:r0 + block]
+        idx = torch.from_numpy(rows).to(case.logits.device)
+        host = case.logits[idx].cpu()
+        gpu_bits = d_g[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        ref = oracle.backward(host, y_all[rows], g_all[rows], v, want_f64=True,
+                              want_bf16=True, nthreads=threads)
+        t_bwd += time.perf_counter() - t0
+        e, c, me, mr, fl = _compare_dlogits(gpu_bits[:, :v], ref["d64"][:, :v],
+                                            ref["bf16"][:, :v], threads)
+        tot[0] += e
+        tot[1] += c
+        tot[2], tot[3], tot[4] = max(tot[2], me), max(tot[3], mr), max(tot[4], fl)
+    elements, correct, max_err, max_ref, floor = tot
+    acc = {"rows_forward": n, "rows_backward": int(sample.size),
+           "logp_abs_err": _pcts(np.concatenate(d_logp)),
+           "lse_abs_err": _pcts(np.concatenate(d_lse)),
+           "dlogits": {"elements": elements,
+                       "correctly_rounded_pct": round(100.0 * correct / max(1, elements), 5),
+                       "misrounded": elements - correct,
+                       "max_err": max_err, "max_ref": max_ref, "floor": floor,
+                       "max_err_over_max": max_err / max_ref if max_ref else 0.0,
+                       "floor_over_max": floor / max_ref if max_ref else 0.0,
+                       "max_err_over_floor": max_err / floor if floor else 0.0}}
+    return {"fwd_seconds": t_fwd, "bwd_seconds": t_bwd, "fwd_rows": n,
+            "bwd_rows": int(sample.size), "accuracy": acc}
+
+
+def cpu_baseline(leg: dict, case, threads: int) -> dict:
+    """Rate of the oracle legs (forward on every row, backward on the sample) under the
+    same byte accounting as the GPU, plus a one-thread rate on 256 rows."""
+    import numpy as np
+
+    import oracle
+
+    v = case.vocab_real
+    fwd_b, _ = algorithmic_bytes(leg["fwd_rows"], leg["fwd_rows"], v, v, False)
+    _, bwd_b = algorithmic_bytes(leg["bwd_rows"], leg["bwd_rows"], v, v, False)
+    secs = leg["fwd_seconds"] + leg["bwd_seconds"]
+    gbs = (fwd_b + bwd_b) / secs / 1e9
+    full_fwd, full_bwd = algorithmic_bytes(case.n, case.n, v, v, False)
+    rows1 = min(case.n, 256)
+    idx = np.linspace(0, case.n - 1, rows1).astype(np.int64)
+    host = case.logits[idx].cpu()
+    y = case.targets[idx].cpu().numpy()
+    g = case.grad[idx].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.forward(host, y, v, nthreads=1)
+    oracle.backward(host, y, g, v, want_f64=False, want_bf16=True, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    f1, b1 = algorithmic_bytes(rows1, rows1, v, v, False)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the same workload: FP64 forward on all {leg['fwd_rows']} rows "
+                      f"({leg['fwd_seconds']:.2f} s) and FP64 backward on {leg['bwd_rows']} "
+                      f"rows ({leg['bwd_seconds']:.2f} s), each compared with the GPU's "
+                      "outputs block by block (comparison time excluded)",
+            "ms_per_step_extrapolated": round((full_fwd + full_bwd) / (gbs * 1e9) * 1e3, 1),
+            "one_thread": {"value": round((f1 + b1) / dt1 / 1e9, 4), "unit": "GB/s",
+                           "rows": rows1, "seconds": round(dt1, 3)},
+            "cpu_model": cpu_model()}
 
 
 def time_variants(dst, case, stream, steps: int) -> dict:
@@ -461,16 +775,18 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target wall time of the oracle sample (0 disables it)")
-    ap.add_argument("--shard-path", action="store_true",
-                    help="also time logp_partials (4 shards) + logp_merge")
+                    help="0 disables the oracle leg (cpu_baseline and accuracy)")
+    ap.add_argument("--bwd-rows", type=int, default=20480,
+                    help="rows of each workload whose dlogits the oracle checks")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline step only (no ceilings, other workloads or "
+                         "oracle leg): the short run the counter passes profile")
     ap.add_argument("--variants", action="store_true",
                     help="also time FP16 and FP32 logits and BF16 at temperature 0.7 on the "
-                         "same shape, the same shape on the pages' bench inputs (sigma 1, "
-                         "g = 1), a GRPO step and the GRPO loss alone (reported under "
-                         "config.variants)")
+                         "same shape, a GRPO step, the GRPO loss alone and linear_logp "
+                         "(reported under config.variants)")
     ap.add_argument("--profile-copy", action="store_true",
-                    help="run a 4 GiB device copy after the timed region (counter scaling)")
+                    help="end with one 4 GiB hbm_copy of the ceiling probe (counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -487,13 +803,22 @@ def main() -> int:
     import torch
 
     import deterministic_selected_token_amd as dst
-    from workloads import headline_case
+    from workloads import headline_case, long_case, mid_case
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    quick = args.headline_only
+    extra_steps = max(3, args.steps // 4)
+
+    ceiling = None
+    if not quick:
+        print("bench: measuring the HBM read and copy ceilings", file=sys.stderr, flush=True)
+        ceiling = hbm_ceiling(stream)
+
     print("bench: generating the headline workload", file=sys.stderr, flush=True)
     case = headline_case(device=dev)
     n, v = case.n, case.vocab_real
@@ -502,7 +827,6 @@ def main() -> int:
     lse = torch.empty(n, dtype=torch.float32, device=dev)
     stats = torch.empty((n, 2), dtype=torch.float32, device=dev)
     dlogits = torch.empty((n, v), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
         if ev is not None:
@@ -545,27 +869,53 @@ def main() -> int:
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     achieved = bwd_b / (bwd_avg * 1e-3) / 1e9
+    fwd_achieved = fwd_b / (fwd_avg * 1e-3) / 1e9
 
     extra = {}
-    if args.shard_path:
-        L = dst.logp_num_tiles(v)
-        partials = torch.empty((n, L, 3), dtype=torch.float32, device=dev)
-        layout = [(0, 13 * 4096), (13 * 4096, 26 * 4096), (26 * 4096, v)]
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        for rep in range(2):
-            e[0].record(stream)
-            for c0, c1 in layout:
-                dst.logp_partials(x[:, c0:c1], y, v, v, c0, c1, partials, stream=stream)
-            e[1].record(stream)
-            dst.logp_merge(partials, y, v, stream=stream)
-            e[2].record(stream)
-        torch.cuda.synchronize()
-        extra["shard_path"] = {"shards": len(layout),
-                               "partials_ms": round(e[0].elapsed_time(e[1]), 4),
-                               "merge_ms": round(e[1].elapsed_time(e[2]), 4)}
+    accuracy = None
+    cpu = None
+    if not quick:
+        print("bench: batch invariance, tensor-parallel share", file=sys.stderr, flush=True)
+        extra["batch_invariance"] = batch_invariance(
+            dst, case, (logp, lse, stats, dlogits), stream)
+        extra["tp8_rank_share"] = time_tp8_share(dst, case, stream, extra_steps)
+        print("bench: mid-size workload", file=sys.stderr, flush=True)
+        mid = mid_case(device=dev)
+        extra["mid"] = {"workload": "N=4096, vocabulary 151936 padded to 152064 (-inf "
+                                    "pads), BF16 ~N(0,3^2), 5% inactive rows, g = 1/N_active",
+                        **time_case(dst, mid, stream, extra_steps)}
+        del mid
+        print("bench: vocab-shard workload", file=sys.stderr, flush=True)
+        extra["shards"] = time_shard_config(dst, stream, extra_steps)
+        print("bench: 131072-row workload", file=sys.stderr, flush=True)
+        long = long_case(device=dev)
+        extra["long_131072"] = {"workload": "N=131072, V=151936, BF16 ~N(0,3^2), uniform "
+                                            "targets, g ~N(0,1)",
+                                **time_case(dst, long, stream, extra_steps)}
+        del long
+        torch.cuda.empty_cache()
+        print("bench: the pages' bench inputs", file=sys.stderr, flush=True)
+        pages = headline_case(device=dev, pages_bench=True)
+        pages_t = time_case(dst, pages, stream, extra_steps, keep=True)
+        pages_out = pages_t.pop("_outputs")
+        extra["pages_bench_inputs"] = {"workload": "N=32768, V=151936, BF16 randn (sigma 1), "
+                                                   "uniform targets, g = 1", **pages_t}
+        if args.cpu_seconds > 0:
+            import oracle
+
+            threads = oracle.default_threads()
+            print("bench: the oracle on the host, compared with the GPU outputs",
+                  file=sys.stderr, flush=True)
+            leg = oracle_leg(case, (logp, lse, stats, dlogits), args.bwd_rows, threads)
+            leg_pages = oracle_leg(pages, pages_out, args.bwd_rows, threads)
+            accuracy = {"headline": leg["accuracy"], "pages_bench_inputs": leg_pages["accuracy"],
+                        "reference": "FP64 oracle; logp/LSE absolute errors over every row, "
+                                     "dlogits over the sampled rows' N x V elements"}
+            cpu = cpu_baseline(leg, case, threads)
+        del pages, pages_out
+        torch.cuda.empty_cache()
     if args.variants:
         extra["variants"] = time_variants(dst, case, stream, args.steps)
-        extra["variants"]["bf16_pages_bench_inputs"] = time_pages_bench(dst, stream, args.steps)
         extra["variants"].update(time_grpo(dst, case, stream, args.steps))
         extra["variants"]["linear_logp_fwd"] = time_linear(dst, stream, max(3, args.steps // 4))
         extra["variants"]["linear_logp_fwd_temperature_0.7"] = time_linear(
@@ -573,18 +923,32 @@ def main() -> int:
         extra["variants"]["linear_logp_bwd"] = time_linear_backward(
             dst, stream, max(2, args.steps // 8))
     if args.profile_copy:
-        src = torch.empty(1 << 31, dtype=torch.int16, device=dev)  # 4 GiB
+        lib = load_ceiling_library()
+        nbytes = 4 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         dst_buf = torch.empty_like(src)
-        dst_buf.copy_(src)
+        if lib.hbm_copy(src.data_ptr(), dst_buf.data_ptr(), nbytes, 16, 16,
+                        stream.cuda_stream) != 0:
+            raise RuntimeError("hbm_copy failed")
         torch.cuda.synchronize()
-        extra["copy_bytes_each_way"] = src.numel() * 2
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        print("bench: timing the oracle sample on the host", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(case, args.cpu_seconds)
+        extra["copy_bytes_each_way"] = nbytes
 
     props = torch.cuda.get_device_properties(dev)
+    roofline = {"bound": "hbm", "kernel": "bwd_flat_kernel (logp_backward)",
+                "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("bwd"),
+                "algorithmic_bytes_per_launch": bwd_b,
+                "avg_launch_ms": round(bwd_avg, 4),
+                "fwd_kernel": {"achieved": round(fwd_achieved, 2),
+                               "frac": round(fwd_achieved / HBM_PEAK_GBS, 4),
+                               "avg_launch_ms": round(fwd_avg, 4),
+                               "algorithmic_bytes_per_launch": fwd_b,
+                               "traffic": measured_traffic("fwd")}}
+    if ceiling is not None:
+        roofline["ceiling"] = ceiling
+        roofline["frac_of_copy_ceiling"] = round(achieved / ceiling["copy_gbs"], 4)
+        roofline["fwd_kernel"]["frac_of_read_ceiling"] = round(
+            fwd_achieved / ceiling["read_gbs"], 4)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -609,6 +973,7 @@ def main() -> int:
                                                4)},
                    "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_b},
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "floor_ms_at_8tbs": round((fwd_b + bwd_b) / (HBM_PEAK_GBS * 1e9) * 1e3, 3),
                    "step_extra_bytes_beyond_outputs": int(step_extra),
                    "device_free_bytes_change_over_step": int(free_change),
                    # the pages' peak-memory figure: from before the step, the returned BF16
@@ -622,15 +987,8 @@ def main() -> int:
                                         "B200 (randn logits, g = 1; the timing does not "
                                         "depend on the values); context, not a target",
                    **extra},
-        "roofline": {"bound": "hbm", "kernel": "bwd_flat_kernel (logp_backward)",
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("bwd"),
-                     "algorithmic_bytes_per_launch": bwd_b,
-                     "avg_launch_ms": round(bwd_avg, 4),
-                     "fwd_kernel": {"achieved": round(fwd_b / (fwd_avg * 1e-3) / 1e9, 2),
-                                    "avg_launch_ms": round(fwd_avg, 4),
-                                    "algorithmic_bytes_per_launch": fwd_b,
-                                    "traffic": measured_traffic("fwd")}},
+        "roofline": roofline,
+        "accuracy": accuracy,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

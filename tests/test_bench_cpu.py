@@ -53,3 +53,38 @@ def test_traffic_is_null_once_the_kernel_sources_differ(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
     assert bench.measured_traffic("bwd") is None
     assert bench.measured_traffic("fwd") is None
+
+
+def test_oracle_leg_counts_against_known_outputs():
+    """The bench's block-by-block comparison, fed the oracle's own outputs (logp and LSE
+    rounded to float32, dlogits rounded to BF16): every element is correctly rounded and the
+    largest error is the BF16 floor; one planted wrong element is counted."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workloads import random_case
+
+    case = random_case(40, 5000, sigma=3.0, seed=4)
+    case.meta["spike_row_index"] = [5, 7]
+    y = case.targets.numpy()
+    ref = oracle.forward(case.logits, y, 5000)
+    d = oracle.backward(case.logits, y, case.grad.numpy(), 5000)
+    logp = torch.from_numpy(ref["logp"].astype(np.float32))
+    lse = torch.from_numpy(ref["lse"].astype(np.float32))
+    bits = torch.from_numpy(d["bf16"].view(np.int16)).view(torch.bfloat16)
+    leg = bench.oracle_leg(case, (logp, lse, None, bits), bwd_rows=16, threads=3, block=8)
+    acc = leg["accuracy"]
+    assert acc["rows_forward"] == 40 and acc["rows_backward"] == 16  # rows 5, 7 in the spread
+    assert acc["dlogits"]["elements"] == 16 * 5000 and acc["dlogits"]["misrounded"] == 0
+    assert acc["dlogits"]["max_err"] == acc["dlogits"]["floor"] > 0
+    assert acc["logp_abs_err"]["max"] <= 2.0 ** -24 * 20 and acc["lse_abs_err"]["max"] < 1e-5
+    # one element moved by one BF16 spacing on a sampled row
+    wrong = bits.clone()
+    w = wrong.view(torch.int16)
+    w[0, 11] += 1
+    leg2 = bench.oracle_leg(case, (logp, lse, None, wrong), bwd_rows=16, threads=2, block=5)
+    assert leg2["accuracy"]["dlogits"]["misrounded"] == 1
+    assert leg2["accuracy"]["dlogits"]["max_err"] >= acc["dlogits"]["max_err"]
+    cpu = bench.cpu_baseline(leg, case, threads=3)
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] == 3

@@ -13,9 +13,8 @@ import torch
 import deterministic_selected_token_amd as dst
 import oracle
 from parity_checks import BackwardTally, bits_of, check_forward
-from workloads import random_case
+from workloads import long_case, random_case
 from workloads.synth import QWEN_VOCAB
-from workloads.synth import _gen, _normal_bf16_rows  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -100,10 +99,8 @@ def test_check_targets_counts_bad_active_targets():
 def test_long_sequence_131072_rows_bounded_workspace():
     n, v = 131072, QWEN_VOCAB
     say(f"long sequence: n={n} V={v} ({2 * n * v / 2**30:.1f} GiB logits)")
-    gen = _gen(DEV, 77)
-    logits = _normal_bf16_rows(n, v, v, 3.0, gen, DEV)
-    y = torch.randint(0, v, (n,), generator=gen, device=DEV)
-    g = torch.randn((n,), generator=gen, device=DEV)
+    case = long_case(device=DEV, n=n)
+    logits, y, g = case.logits, case.targets, case.grad
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()

@@ -12,6 +12,7 @@ from .synth import (  # noqa: F401
     mid_case,
     headline_case,
     shard_case,
+    long_case,
     sweep_probe_rows,
     sweep_filler_rows,
     random_case,

@@ -25,6 +25,7 @@ PCG64; the large cases are drawn on the requested device with a seeded
             g ~ N(0, 1).
 * sweep     8 probe rows and a pool of 2048 filler rows at V=151936, logits ~ N(0, 3^2),
             uniform targets, g ~ N(0, 1); seeds 0, 1, 2.
+* long      N=131072 rows at V=151936, logits ~ N(0, 3^2), uniform targets, g ~ N(0, 1).
 """
 
 from __future__ import annotations
@@ -219,6 +220,18 @@ def shard_case(device="cuda", seed: int = 3, n: int = 8192) -> Case:
     targets = torch.randint(0, v_real, (n,), generator=gen, device=device, dtype=torch.int64)
     g = torch.randn((n,), generator=gen, device=device, dtype=torch.float32)
     return Case("shard", logits, targets, None, g, v_real, v_pad, meta={"seed": seed})
+
+
+# --------------------------------------------------------------------------- long
+
+def long_case(device="cuda", seed: int = 77, n: int = 131072, vocab: int = QWEN_VOCAB) -> Case:
+    """The extreme row count: n rows at the Qwen vocabulary, logits ~ N(0, 3^2), uniform
+    targets, g ~ N(0, 1) (39.8 GB of BF16 logits at n = 131072)."""
+    gen = _gen(device, seed)
+    logits = _normal_bf16_rows(n, vocab, vocab, 3.0, gen, device)
+    targets = torch.randint(0, vocab, (n,), generator=gen, device=device, dtype=torch.int64)
+    g = torch.randn((n,), generator=gen, device=device, dtype=torch.float32)
+    return Case("long", logits, targets, None, g, vocab, vocab, meta={"seed": seed})
 
 
 # -------------------------------------------------------------------------- sweep
