@@ -34,7 +34,7 @@ LIB_PATH = os.environ.get("DST_AMD_LIB") or os.path.join(_HERE, "liblogp_mi355x.
 STATUS = {
     0: "LOGP_OK", 1: "LOGP_ERR_NULL", 2: "LOGP_ERR_SHAPE", 3: "LOGP_ERR_SHARD",
     4: "LOGP_ERR_DEVICE", 5: "LOGP_ERR_RANGE", 6: "LOGP_ERR_OVERLAP", 7: "LOGP_ERR_HIP",
-    8: "LOGP_ERR_ARG",
+    8: "LOGP_ERR_ARG", 9: "LOGP_ERR_SCRATCH",
 }
 DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}  # logp_dtype_t values
 EXPORTED = ("logp_forward", "logp_backward", "logp_partials", "logp_merge", "logp_num_tiles",

@@ -19,6 +19,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "host_common.hpp"
 #include "linear_logp.h"
@@ -505,6 +506,185 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 }  // namespace
 
+namespace {
+
+// ------------------------------------------------------------------ no-allocation scratch
+//
+// Staging memory of linear_logp_backward_noalloc: one static array per GPU, created with the
+// code object on that device and held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol); the device
+// address is looked up once per device with that device current and kept per device.
+constexpr int64_t kNoallocScratchBytes = LINEAR_LOGP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_address[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on `dev`, which must be the current device.
+logp_status_t scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxScratchDevices) return LOGP_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_address[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return LOGP_ERR_HIP;
+        }
+        g_scratch_address[dev] = p;
+    }
+    *out = g_scratch_address[dev];
+    return LOGP_OK;
+}
+
+// The backward with its staging either in the caller's workspace (use_scratch false) or in
+// this file's static `scratch` array on the launch device (use_scratch true: workspace and
+// workspace_bytes are ignored, and a call needing more than kNoallocScratchBytes is
+// LOGP_ERR_SCRATCH before anything is checked on the device).
+logp_status_t backward_impl(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
+    int64_t ld_dh, float* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream, bool use_scratch) {
+    if (!(inv_temperature > 0.0f) || !std::isfinite(inv_temperature)) return LOGP_ERR_ARG;
+    if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
+        vocab_padded > (int64_t(1) << 31) - 1 - kTile || n > LINEAR_LOGP_BWD_MAX_ROWS)
+        return LOGP_ERR_SHAPE;
+    if (col_begin < 0 || col_end < col_begin || col_end > vocab_padded ||
+        col_begin % kTile != 0 || (col_end % kTile != 0 && col_end != vocab_padded))
+        return LOGP_ERR_SHARD;
+    if (chunk_cols < kTile || chunk_cols % kTile != 0 || chunk_cols > LINEAR_LOGP_BWD_MAX_CHUNK)
+        return LOGP_ERR_SHAPE;
+    // the products' row strides and reduction lengths (padded rows or chunk columns) keep the
+    // in-kernel load offsets below the out-of-range marker
+    static_assert(uint64_t(16) * 2 * (LINEAR_LOGP_BWD_MAX_ROWS + kBM) < kOob &&
+                      LINEAR_LOGP_BWD_MAX_CHUNK <= LINEAR_LOGP_BWD_MAX_ROWS,
+                  "product load offsets");
+    if (n == 0) return LOGP_OK;
+    const int64_t H = hidden_size;
+    if (H < 1 || H > LINEAR_LOGP_MAX_HIDDEN || H % 8 != 0 || ld_h < H || ld_w < H ||
+        ld_h % 8 != 0 || ld_w % 8 != 0 || ld_h > LINEAR_LOGP_MAX_LD ||
+        ld_w > LINEAR_LOGP_MAX_LD || ld_dh < H || ld_dw < H)
+        return LOGP_ERR_SHAPE;
+    const int64_t width = col_end - col_begin;
+    // weight rows actually read: the view's real vocabulary rows (none for an all-padding view,
+    // whose weight pointer may then be NULL)
+    const int64_t lim = std::max<int64_t>(0, std::min(width, vocab_real - col_begin));
+    if (hidden == nullptr || targets == nullptr || grad_logp == nullptr || stats == nullptr ||
+        dhidden == nullptr || (lim > 0 && weight == nullptr) ||
+        (width > 0 && dweight == nullptr) || (!use_scratch && workspace == nullptr))
+        return LOGP_ERR_NULL;
+    if (!aligned16(hidden) || (weight != nullptr && !aligned16(weight)) ||
+        (!use_scratch && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+        return LOGP_ERR_SHAPE;
+    const int64_t need = linear_logp_backward_workspace(n, H, chunk_cols);
+    if (need < 0) return LOGP_ERR_SHAPE;
+    if (use_scratch ? need > kNoallocScratchBytes : workspace_bytes < need)
+        return use_scratch ? LOGP_ERR_SCRATCH : LOGP_ERR_SHAPE;
+    if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
+    const Span in[] = {{hidden, span_bytes(n, ld_h, H, 2)},
+                       {weight, lim > 0 ? span_bytes(lim, ld_w, H, 2) : 0},
+                       {targets, uint64_t(n) * 8},
+                       {active, active ? uint64_t(n) : 0},
+                       {grad_logp, uint64_t(n) * 4},
+                       {stats, uint64_t(n) * sizeof(logp_stats_t)}};
+    // the static scratch array is not a caller buffer: it cannot overlap one, and it is not
+    // checked as one
+    const Span out[] = {{dhidden, span_bytes(n, ld_dh, H, 4)},
+                        {dweight, width > 0 ? span_bytes(width, ld_dw, H, 4) : 0},
+                        {use_scratch ? nullptr : workspace, use_scratch ? 0 : uint64_t(need)}};
+    int dev = -1;
+    logp_status_t st = check_buffers(in, 6, out, 3, stream, &dev);
+    if (st != LOGP_OK) return st;
+    DeviceGuard guard(dev);
+    if (!guard.ok()) return LOGP_ERR_HIP;
+    if (use_scratch) {
+        st = scratch_address(dev, &workspace);  // with the launch device current
+        if (st != LOGP_OK) return st;
+    }
+
+    if (width == 0) {  // no vocabulary columns: this shard contributes dh = 0
+        int cols = static_cast<int>(H);
+        void* args[] = {&dhidden, &ld_dh, &n, &cols};
+        return launch(reinterpret_cast<const void*>(&zero_rows_kernel), dim3(1024), dim3(256),
+                      args, 0, stream);
+    }
+
+    const int64_t n_pad = round_up(n, kBM), h_pad = round_up(H, kBN);
+    const int64_t c_pad_max = round_up(chunk_cols, kBN);
+    uint16_t* ws = static_cast<uint16_t*>(workspace);
+    uint16_t* hT = ws;                      // [h_pad, n_pad]
+    uint16_t* wT = hT + h_pad * n_pad;      // [h_pad, c_pad]
+    uint16_t* dz = wT + h_pad * c_pad_max;  // [n_pad, c_pad]
+    uint16_t* dzT = dz + n_pad * c_pad_max; // [c_pad, n_pad]
+
+    int Hi = static_cast<int>(H), ni = static_cast<int>(n);
+    {  // h^T, zero-padded
+        void* args[] = {&hidden, &ld_h, &ni, &Hi, &hT, const_cast<int64_t*>(&n_pad)};
+        st = launch(reinterpret_cast<const void*>(&transpose_kernel),
+                    dim3(static_cast<uint32_t>(h_pad / kTr), static_cast<uint32_t>(n_pad / kTr)),
+                    dim3(256), args, 0, stream);
+        if (st != LOGP_OK) return st;
+    }
+    const bool scaled = inv_temperature != 1.0f;
+    const void* dz_kernel = scaled ? reinterpret_cast<const void*>(&linear_dz_kernel<true>)
+                                   : reinterpret_cast<const void*>(&linear_dz_kernel<false>);
+    int row_blocks = static_cast<int>(n_pad / kBM);
+    for (int64_t off = 0; off < width; off += chunk_cols) {
+        const int64_t cw = std::min(chunk_cols, width - off);     // chunk columns
+        const int64_t c_pad = round_up(cw, kBN);
+        const int64_t chunk_col0 = col_begin + off;              // global column of the chunk
+        int lim_c = static_cast<int>(std::max<int64_t>(0, std::min(cw, vocab_real - chunk_col0)));
+        const uint16_t* wc = weight + off * ld_w;
+        {  // W^T of the chunk's real rows, zero-padded to [h_pad, c_pad]
+            void* args[] = {&wc, &ld_w, &lim_c, &Hi, &wT, const_cast<int64_t*>(&c_pad)};
+            st = launch(reinterpret_cast<const void*>(&transpose_kernel),
+                        dim3(static_cast<uint32_t>(h_pad / kTr),
+                             static_cast<uint32_t>(c_pad / kTr)),
+                        dim3(256), args, 0, stream);
+            if (st != LOGP_OK) return st;
+        }
+        {  // dz and dz^T
+            int64_t ldz = c_pad, ldzt = n_pad;
+            int64_t cc0 = chunk_col0;
+            float inv_t = inv_temperature;
+            void* args[] = {&hidden, &ld_h, &n,     &Hi,     &wc,          &ld_w,
+                            &lim_c,  &row_blocks,   &cc0,    &vocab_real,  &inv_t,
+                            &targets, &active,      &ignore_index, &grad_logp, &stats,
+                            &dz,     &ldz,          &dzT,    &ldzt};
+            st = launch(dz_kernel, dim3(static_cast<uint32_t>(row_blocks * (c_pad / kBN))),
+                        dim3(kThreads), args, 0, stream);
+            if (st != LOGP_OK) return st;
+        }
+        {  // dh (=|+=) dz W: a = dz [n_pad, c_pad], b = W^T [h_pad, c_pad]
+            int64_t lda = c_pad, ldb = c_pad, ldc = ld_dh;
+            int K = static_cast<int>(c_pad), mr = ni, nr = Hi, mb = row_blocks;
+            void* args[] = {&dz, &lda, &wT, &ldb, &K, &mr, &nr, &mb, &dhidden, &ldc};
+            const void* k = off == 0 ? reinterpret_cast<const void*>(&gemm_tn_kernel<false>)
+                                     : reinterpret_cast<const void*>(&gemm_tn_kernel<true>);
+            st = launch(k, dim3(static_cast<uint32_t>(mb * (h_pad / kBN))), dim3(kThreads),
+                        args, 0, stream);
+            if (st != LOGP_OK) return st;
+        }
+        {  // dW of the chunk's rows = dz^T h: a = dz^T [c_pad, n_pad], b = h^T [h_pad, n_pad]
+            int64_t lda = n_pad, ldb = n_pad, ldc = ld_dw;
+            int K = static_cast<int>(n_pad), mr = static_cast<int>(cw), nr = Hi;
+            int mb = static_cast<int>(c_pad / kBM);
+            float* dwc = dweight + off * ld_dw;
+            void* args[] = {&dzT, &lda, &hT, &ldb, &K, &mr, &nr, &mb, &dwc, &ldc};
+            st = launch(reinterpret_cast<const void*>(&gemm_tn_kernel<false>),
+                        dim3(static_cast<uint32_t>(mb * (h_pad / kBN))), dim3(kThreads), args,
+                        0, stream);
+            if (st != LOGP_OK) return st;
+        }
+    }
+    return LOGP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hidden,
@@ -594,131 +774,22 @@ logp_status_t linear_logp_backward_ex(
     int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
     int64_t ld_dh, float* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
     int64_t chunk_cols, hipStream_t stream) {
-    if (!(inv_temperature > 0.0f) || !std::isfinite(inv_temperature)) return LOGP_ERR_ARG;
-    if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
-        vocab_padded > (int64_t(1) << 31) - 1 - kTile || n > LINEAR_LOGP_BWD_MAX_ROWS)
-        return LOGP_ERR_SHAPE;
-    if (col_begin < 0 || col_end < col_begin || col_end > vocab_padded ||
-        col_begin % kTile != 0 || (col_end % kTile != 0 && col_end != vocab_padded))
-        return LOGP_ERR_SHARD;
-    if (chunk_cols < kTile || chunk_cols % kTile != 0 || chunk_cols > LINEAR_LOGP_BWD_MAX_CHUNK)
-        return LOGP_ERR_SHAPE;
-    // the products' row strides and reduction lengths (padded rows or chunk columns) keep the
-    // in-kernel load offsets below the out-of-range marker
-    static_assert(uint64_t(16) * 2 * (LINEAR_LOGP_BWD_MAX_ROWS + kBM) < kOob &&
-                      LINEAR_LOGP_BWD_MAX_CHUNK <= LINEAR_LOGP_BWD_MAX_ROWS,
-                  "product load offsets");
-    if (n == 0) return LOGP_OK;
-    const int64_t H = hidden_size;
-    if (H < 1 || H > LINEAR_LOGP_MAX_HIDDEN || H % 8 != 0 || ld_h < H || ld_w < H ||
-        ld_h % 8 != 0 || ld_w % 8 != 0 || ld_h > LINEAR_LOGP_MAX_LD ||
-        ld_w > LINEAR_LOGP_MAX_LD || ld_dh < H || ld_dw < H)
-        return LOGP_ERR_SHAPE;
-    const int64_t width = col_end - col_begin;
-    // weight rows actually read: the view's real vocabulary rows (none for an all-padding view,
-    // whose weight pointer may then be NULL)
-    const int64_t lim = std::max<int64_t>(0, std::min(width, vocab_real - col_begin));
-    if (hidden == nullptr || targets == nullptr || grad_logp == nullptr || stats == nullptr ||
-        dhidden == nullptr || (lim > 0 && weight == nullptr) ||
-        (width > 0 && dweight == nullptr) || workspace == nullptr)
-        return LOGP_ERR_NULL;
-    if (!aligned16(hidden) || (weight != nullptr && !aligned16(weight)) ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return LOGP_ERR_SHAPE;
-    const int64_t need = linear_logp_backward_workspace(n, H, chunk_cols);
-    if (need < 0 || workspace_bytes < need) return LOGP_ERR_SHAPE;
-    if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
-    const Span in[] = {{hidden, span_bytes(n, ld_h, H, 2)},
-                       {weight, lim > 0 ? span_bytes(lim, ld_w, H, 2) : 0},
-                       {targets, uint64_t(n) * 8},
-                       {active, active ? uint64_t(n) : 0},
-                       {grad_logp, uint64_t(n) * 4},
-                       {stats, uint64_t(n) * sizeof(logp_stats_t)}};
-    const Span out[] = {{dhidden, span_bytes(n, ld_dh, H, 4)},
-                        {dweight, width > 0 ? span_bytes(width, ld_dw, H, 4) : 0},
-                        {workspace, uint64_t(need)}};
-    int dev = -1;
-    logp_status_t st = check_buffers(in, 6, out, 3, stream, &dev);
-    if (st != LOGP_OK) return st;
-    DeviceGuard guard(dev);
-    if (!guard.ok()) return LOGP_ERR_HIP;
+    return backward_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
+                         vocab_padded, col_begin, col_end, targets, active, ignore_index,
+                         grad_logp, stats, dhidden, ld_dh, dweight, ld_dw, workspace,
+                         workspace_bytes, chunk_cols, stream, false);
+}
 
-    if (width == 0) {  // no vocabulary columns: this shard contributes dh = 0
-        int cols = static_cast<int>(H);
-        void* args[] = {&dhidden, &ld_dh, &n, &cols};
-        return launch(reinterpret_cast<const void*>(&zero_rows_kernel), dim3(1024), dim3(256),
-                      args, 0, stream);
-    }
-
-    const int64_t n_pad = round_up(n, kBM), h_pad = round_up(H, kBN);
-    const int64_t c_pad_max = round_up(chunk_cols, kBN);
-    uint16_t* ws = static_cast<uint16_t*>(workspace);
-    uint16_t* hT = ws;                      // [h_pad, n_pad]
-    uint16_t* wT = hT + h_pad * n_pad;      // [h_pad, c_pad]
-    uint16_t* dz = wT + h_pad * c_pad_max;  // [n_pad, c_pad]
-    uint16_t* dzT = dz + n_pad * c_pad_max; // [c_pad, n_pad]
-
-    int Hi = static_cast<int>(H), ni = static_cast<int>(n);
-    {  // h^T, zero-padded
-        void* args[] = {&hidden, &ld_h, &ni, &Hi, &hT, const_cast<int64_t*>(&n_pad)};
-        st = launch(reinterpret_cast<const void*>(&transpose_kernel),
-                    dim3(static_cast<uint32_t>(h_pad / kTr), static_cast<uint32_t>(n_pad / kTr)),
-                    dim3(256), args, 0, stream);
-        if (st != LOGP_OK) return st;
-    }
-    const bool scaled = inv_temperature != 1.0f;
-    const void* dz_kernel = scaled ? reinterpret_cast<const void*>(&linear_dz_kernel<true>)
-                                   : reinterpret_cast<const void*>(&linear_dz_kernel<false>);
-    int row_blocks = static_cast<int>(n_pad / kBM);
-    for (int64_t off = 0; off < width; off += chunk_cols) {
-        const int64_t cw = std::min(chunk_cols, width - off);     // chunk columns
-        const int64_t c_pad = round_up(cw, kBN);
-        const int64_t chunk_col0 = col_begin + off;              // global column of the chunk
-        int lim_c = static_cast<int>(std::max<int64_t>(0, std::min(cw, vocab_real - chunk_col0)));
-        const uint16_t* wc = weight + off * ld_w;
-        {  // W^T of the chunk's real rows, zero-padded to [h_pad, c_pad]
-            void* args[] = {&wc, &ld_w, &lim_c, &Hi, &wT, const_cast<int64_t*>(&c_pad)};
-            st = launch(reinterpret_cast<const void*>(&transpose_kernel),
-                        dim3(static_cast<uint32_t>(h_pad / kTr),
-                             static_cast<uint32_t>(c_pad / kTr)),
-                        dim3(256), args, 0, stream);
-            if (st != LOGP_OK) return st;
-        }
-        {  // dz and dz^T
-            int64_t ldz = c_pad, ldzt = n_pad;
-            int64_t cc0 = chunk_col0;
-            float inv_t = inv_temperature;
-            void* args[] = {&hidden, &ld_h, &n,     &Hi,     &wc,          &ld_w,
-                            &lim_c,  &row_blocks,   &cc0,    &vocab_real,  &inv_t,
-                            &targets, &active,      &ignore_index, &grad_logp, &stats,
-                            &dz,     &ldz,          &dzT,    &ldzt};
-            st = launch(dz_kernel, dim3(static_cast<uint32_t>(row_blocks * (c_pad / kBN))),
-                        dim3(kThreads), args, 0, stream);
-            if (st != LOGP_OK) return st;
-        }
-        {  // dh (=|+=) dz W: a = dz [n_pad, c_pad], b = W^T [h_pad, c_pad]
-            int64_t lda = c_pad, ldb = c_pad, ldc = ld_dh;
-            int K = static_cast<int>(c_pad), mr = ni, nr = Hi, mb = row_blocks;
-            void* args[] = {&dz, &lda, &wT, &ldb, &K, &mr, &nr, &mb, &dhidden, &ldc};
-            const void* k = off == 0 ? reinterpret_cast<const void*>(&gemm_tn_kernel<false>)
-                                     : reinterpret_cast<const void*>(&gemm_tn_kernel<true>);
-            st = launch(k, dim3(static_cast<uint32_t>(mb * (h_pad / kBN))), dim3(kThreads),
-                        args, 0, stream);
-            if (st != LOGP_OK) return st;
-        }
-        {  // dW of the chunk's rows = dz^T h: a = dz^T [c_pad, n_pad], b = h^T [h_pad, n_pad]
-            int64_t lda = n_pad, ldb = n_pad, ldc = ld_dw;
-            int K = static_cast<int>(n_pad), mr = static_cast<int>(cw), nr = Hi;
-            int mb = static_cast<int>(c_pad / kBM);
-            float* dwc = dweight + off * ld_dw;
-            void* args[] = {&dzT, &lda, &hT, &ldb, &K, &mr, &nr, &mb, &dwc, &ldc};
-            st = launch(reinterpret_cast<const void*>(&gemm_tn_kernel<false>),
-                        dim3(static_cast<uint32_t>(mb * (h_pad / kBN))), dim3(kThreads), args,
-                        0, stream);
-            if (st != LOGP_OK) return st;
-        }
-    }
-    return LOGP_OK;
+logp_status_t linear_logp_backward_noalloc(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
+    int64_t ld_dh, float* dweight, int64_t ld_dw, int64_t chunk_cols, hipStream_t stream) {
+    return backward_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
+                         vocab_padded, col_begin, col_end, targets, active, ignore_index,
+                         grad_logp, stats, dhidden, ld_dh, dweight, ld_dw, nullptr, 0, chunk_cols,
+                         stream, true);
 }
 
 logp_status_t linear_logp_backward(const uint16_t* hidden, int64_t ld_h, int64_t n,

@@ -586,6 +586,9 @@ const char* logp_status_string(int32_t status) {
         case LOGP_ERR_HIP: return "the HIP runtime reported an error";
         case LOGP_ERR_ARG:
             return "unknown dtype, or inv_temperature not a finite positive number";
+        case LOGP_ERR_SCRATCH:
+            return "the call needs more staging memory than the library's static scratch "
+                   "array holds (use the entry point that takes a workspace)";
     }
     return "unknown status";
 }

@@ -23,11 +23,13 @@ from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _shard_slot, _stre
                logp_merge, logp_num_tiles)
 
 EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex", "linear_logp_backward",
-            "linear_logp_backward_ex", "linear_logp_backward_workspace")
+            "linear_logp_backward_ex", "linear_logp_backward_workspace",
+            "linear_logp_backward_noalloc")
 MAX_HIDDEN = 65536
 MAX_LD = 262144
 BWD_MAX_ROWS = 8388608
 BWD_MAX_CHUNK = 1048576
+NOALLOC_SCRATCH_BYTES = 128 << 20
 DEFAULT_CHUNK_COLS = 4 * TILE_COLS
 
 _P, _I64 = ctypes.c_void_p, ctypes.c_int64
@@ -42,6 +44,9 @@ _lib.linear_logp_backward.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64
 _lib.linear_logp_backward.restype = ctypes.c_int32
 _lib.linear_logp_backward_ex.argtypes = [ctypes.c_float] + _lib.linear_logp_backward.argtypes
 _lib.linear_logp_backward_ex.restype = ctypes.c_int32
+_lib.linear_logp_backward_noalloc.argtypes = (_lib.linear_logp_backward_ex.argtypes[:20]
+                                               + [_I64, _P])
+_lib.linear_logp_backward_noalloc.restype = ctypes.c_int32
 _lib.linear_logp_backward_workspace.argtypes = [_I64, _I64, _I64]
 _lib.linear_logp_backward_workspace.restype = _I64
 
@@ -134,13 +139,17 @@ def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: to
                          chunk_cols: int = DEFAULT_CHUNK_COLS,
                          dhidden: Optional[torch.Tensor] = None,
                          dweight: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None, stream=None):
+                         workspace: Optional[torch.Tensor] = None, stream=None,
+                         noalloc: bool = False):
     """(dhidden [n, H] float32, dweight [col_end - col_begin, H] float32): the gradients of
     sum_t grad_logp[t] logp[t] with respect to hidden and to the weight rows
     W[col_begin:col_end] (``weight`` is that row slice), for the logits of linear_logp_forward
     with the same inv_temperature; ``stats`` is the forward's (M, S).  The workspace (a
     uint8 GPU tensor of at least linear_logp_backward_workspace(n, H, chunk_cols) bytes) is
-    allocated with torch when none is passed."""
+    allocated with torch when none is passed.  noalloc=True calls
+    linear_logp_backward_noalloc instead, which stages in the library's static scratch array
+    (at most NOALLOC_SCRATCH_BYTES of workspace) and allocates nothing; pass dhidden and
+    dweight as well to keep torch from allocating them."""
     hidden = _bf16_rows("hidden", hidden)
     dev = hidden.device
     weight = _bf16_rows("weight", weight, dev)
@@ -171,16 +180,23 @@ def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: to
     need = linear_logp_backward_workspace(n, H, chunk_cols)
     if need < 0:
         raise ValueError("n, hidden size or chunk_cols out of range")
+    head = (_ptr(hidden), _row_stride(hidden), n, H, _ptr(weight) if weight.numel() else None,
+            _row_stride(weight), vocab_real, vocab_padded, int(col_begin), col_end,
+            _ptr(targets), _ptr(active), int(ignore_index), _ptr(grad_logp), _ptr(stats),
+            _ptr(dhidden), _row_stride(dhidden) if n else H,
+            _ptr(dweight) if dweight.numel() else None, _row_stride(dweight) if width else H)
+    if noalloc:  # the library's static scratch array: no workspace, nothing allocated
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        _check("linear_logp_backward_noalloc",
+               _lib.linear_logp_backward_noalloc(float(inv_temperature), *head, int(chunk_cols),
+                                                 _stream(dev, stream)))
+        return dhidden, dweight
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 GPU tensor")
-    args = (_ptr(hidden), _row_stride(hidden), n, H, _ptr(weight) if weight.numel() else None,
-            _row_stride(weight), vocab_real, vocab_padded, int(col_begin), col_end,
-            _ptr(targets), _ptr(active), int(ignore_index), _ptr(grad_logp), _ptr(stats),
-            _ptr(dhidden), _row_stride(dhidden) if n else H,
-            _ptr(dweight) if dweight.numel() else None, _row_stride(dweight) if width else H,
-            _ptr(workspace), workspace.numel(), int(chunk_cols), _stream(dev, stream))
+    args = head + (_ptr(workspace), workspace.numel(), int(chunk_cols), _stream(dev, stream))
     if inv_temperature == 1.0:
         _check("linear_logp_backward", _lib.linear_logp_backward(*args))
     else:

@@ -125,6 +125,25 @@ LOGP_API logp_status_t linear_logp_backward_ex(
     int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
     int64_t ld_dh, float* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
     int64_t chunk_cols, hipStream_t stream);
+/* linear_logp_backward_ex for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Every argument is as in
+ * linear_logp_backward_ex; there is no workspace argument.  The staging memory is a static
+ * device array of LINEAR_LOGP_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU
+ * it runs on, from the first call on that GPU until the process ends; a call whose
+ * linear_logp_backward_workspace(n, hidden_size, chunk_cols) exceeds it returns
+ * LOGP_ERR_SCRATCH without launching (e.g. n = 4096, H = 4096 fits with chunk_cols = 4096).
+ * The call allocates nothing and clears nothing: every staging byte a kernel reads was written
+ * earlier in the same call.  All calls on one GPU share that GPU's array, so calls that overlap
+ * on one GPU (on different streams, or from several host threads without ordering) race; a
+ * caller serialises them, e.g. by issuing them on one stream.  Results are bitwise those of
+ * linear_logp_backward_ex with the same chunk_cols. */
+#define LINEAR_LOGP_NOALLOC_SCRATCH_BYTES (128ll << 20)
+LOGP_API logp_status_t linear_logp_backward_noalloc(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
+    int64_t ld_dh, float* dweight, int64_t ld_dw, int64_t chunk_cols, hipStream_t stream);
 /* linear_logp_backward_ex at inv_temperature = 1. */
 LOGP_API logp_status_t linear_logp_backward(
     const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,

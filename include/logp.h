@@ -98,7 +98,9 @@ typedef enum {
     LOGP_ERR_RANGE = 5,   /* an array's extent runs past the end of its allocation */
     LOGP_ERR_OVERLAP = 6, /* an output overlaps an input or another output */
     LOGP_ERR_HIP = 7,     /* the HIP runtime reported an error (query or launch) */
-    LOGP_ERR_ARG = 8      /* unknown dtype, or inv_temperature not finite and positive */
+    LOGP_ERR_ARG = 8,     /* unknown dtype, or inv_temperature not finite and positive */
+    LOGP_ERR_SCRATCH = 9  /* an entry point without a workspace argument needs more staging
+                             memory than its static scratch array holds */
 } logp_status_t;
 
 /* Element type of logits and dlogits for the _ex entry points (PR #495, Tests: the fused

@@ -69,7 +69,7 @@ def test_num_tiles_and_status_strings():
     assert dst.logp_num_tiles(159744) == 39
     assert dst.logp_num_tiles(4096) == 1 and dst.logp_num_tiles(4097) == 2
     assert dst.logp_num_tiles(1) == 1 and dst.logp_num_tiles(0) == 0
-    for code in range(9):
+    for code in range(10):
         s = dst.logp_status_string(code)
         assert s and (code == 0) == (s == "ok")
     assert dst.logp_status_string(99) == "unknown status"

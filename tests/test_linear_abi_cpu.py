@@ -157,3 +157,43 @@ def test_binding_rejects_partials_too_narrow_for_the_shard():
     with pytest.raises(ValueError, match="GPU tensor"):
         linear.linear_logp_partials(h, w, y, 39 * T, 39 * T, 20 * T, 39 * T,
                                     torch.zeros((n, 39, 3)))
+
+
+SCRATCH = 9
+
+
+def call_noalloc(inv_t=1.0, **over):
+    a = dict(h=A, ld_h=64, n=10, H=64, w=A, ld_w=64, vr=5000, vp=5000, c0=0, c1=5000, y=A,
+             act=None, ign=-100, g=A, st=A, dh=A, ld_dh=64, dw=A, ld_dw=64, chunk=4096)
+    a.update(over)
+    return lib.linear_logp_backward_noalloc(
+        inv_t, a["h"], a["ld_h"], a["n"], a["H"], a["w"], a["ld_w"], a["vr"], a["vp"], a["c0"],
+        a["c1"], a["y"], a["act"], a["ign"], a["g"], a["st"], a["dh"], a["ld_dh"], a["dw"],
+        a["ld_dw"], a["chunk"], None)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(n=-1), SHAPE), (dict(c0=100), SHARD), (dict(chunk=4000), SHAPE), (dict(n=0), OK),
+    (dict(h=None), NULL), (dict(dh=None), NULL), (dict(dw=None), NULL), (dict(h=U), SHAPE),
+], ids=lambda v: str(v))
+def test_noalloc_backward_validates_like_the_workspace_entry(over, want):
+    assert call_noalloc(**over) == want == call_bwd(1.0, **over)
+    assert call_noalloc(0.0, **over) == ARG
+
+
+def test_noalloc_backward_rejects_work_beyond_its_scratch_array():
+    """The static scratch array holds LINEAR_LOGP_NOALLOC_SCRATCH_BYTES; a call whose
+    workspace would be larger is refused on the host, before any device check."""
+    text = open(os.path.join(ROOT, "include", "linear_logp.h")).read()
+    m = re.search(r"#define LINEAR_LOGP_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
+    assert int(m.group(1)) << int(m.group(2)) == linear.NOALLOC_SCRATCH_BYTES
+    ws = linear.linear_logp_backward_workspace
+    assert ws(4096, 4096, 4096) == linear.NOALLOC_SCRATCH_BYTES  # the largest that fits
+    big = dict(n=4096, H=4096, ld_h=4096, ld_w=4096, ld_dh=4096, ld_dw=4096)
+    assert call_noalloc(**big, chunk=8192) == SCRATCH
+    assert call_noalloc(**dict(big, n=4097)) == SCRATCH
+    assert call_noalloc(**dict(big, n=8192), chunk=16384) == SCRATCH
+    # the workspace entry point takes the same sizes when its workspace is large enough
+    # (then fails here only at the device check of the fake pointers)
+    assert call_bwd(**big, chunk=8192) == DEVICE
+    assert "static scratch" in linear._lib.logp_status_string(SCRATCH).decode()
