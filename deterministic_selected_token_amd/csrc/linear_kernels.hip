@@ -5,8 +5,9 @@
 // the tile in 16 sub-blocks of 256 columns; for each it forms the 256 x 256 logits block on the
 // matrix cores (v_mfma_f32_32x32x16_bf16, FP32 accumulation over the hidden dimension; each
 // wave holds a 64 x 128 block; the hidden states and weight rows are staged through
-// double-buffered LDS by direct-to-LDS buffer loads, the next stage's in flight while the
-// matrix cores work on the current one), reduces the block to a
+// double-buffered LDS by direct-to-LDS buffer loads, and the two groups of four waves
+// alternate between reading fragments from LDS and feeding the matrix cores), reduces the
+// block to a
 // per-row (max, sum-exp) through LDS (half the rows at a time, 4 threads per row over 64
 // columns each, then a 2-level lane tree), and folds it into the row's running tile state in
 // LDS.  After the last sub-block the tile's (m, s, sel) partial is written in logp.h's layout,
@@ -19,7 +20,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <mutex>
+#include <type_traits>
 
 #include "host_common.hpp"
 #include "linear_logp.h"
@@ -80,12 +83,13 @@ constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: loa
 
 // The stage loads of one operand block (rows [0, rows) of `base`, row stride ld, H valid
 // elements per row): each load instruction of a wave covers 8 rows, through a buffer resource
-// of its own whose range ends at the last valid element of those rows, so every offset stays
-// small and every load is either inside the operand or out of range (zero).
+// of its own whose range ends at the last valid element of those rows.  The lane offset is the
+// same for every group (a lane whose row lies past the group's valid rows is past the range,
+// since ld >= H), so the offsets stay small and out-of-range chunks load as zero.
 template <int N>
 struct OperandLoads {
     __amdgpu_buffer_rsrc_t rs[N];
-    uint32_t off[N];  // this lane's byte offset at k0 = 0, kOob for rows past the range
+    uint32_t off;  // this lane's byte offset inside its 8-row group at k0 = 0
 };
 
 template <int N>
@@ -100,9 +104,8 @@ __device__ __forceinline__ void plan_operand(const uint16_t* base, uint32_t ld, 
         ol.rs[i] = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(base) + int64_t(r0) * ld, 0, static_cast<int>(bytes),
             0x00020000);
-        ol.off[i] = (lane >> 3) < here ? (uint32_t(lane >> 3) * ld + uint32_t(8 * c)) * 2u
-                                       : kOob;
     }
+    ol.off = (uint32_t(lane >> 3) * ld + uint32_t(8 * c)) * 2u;
 }
 
 template <int N>
@@ -112,51 +115,102 @@ __device__ __forceinline__ void issue_operand(uint16_t* stage, const OperandLoad
     for (int i = 0; i < N; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ol.rs[i], (lds_vptr)&stage[(i * (kThreads / kWave) + wave) * 512], 16,
-            k_ok ? ol.off[i] + 2u * uint32_t(k0) : kOob, 0, 0, 0);
+            k_ok ? ol.off + 2u * uint32_t(k0) : kOob, 0, 0, 0);
 }
 
-// The matrix-core steps of one LDS stage: kBK / 16 steps of k, each wave's kTM x kTN tiles.
-__device__ __forceinline__ void mma_stage(const Smem& sm, int buf, int wm, int wn, int lane,
-                                          f32x16 (&acc)[kTM][kTN]) {
+// Ping-pong block product.  The 8 waves form two groups of four, one wave of each group per
+// SIMD (waves 0-3 and 4-7).  A stage of kBK hidden elements is worked in two phases of
+// kBK / 32 MFMA k-steps; each group alternates between reading a phase's fragments from LDS
+// into registers and running that phase's MFMAs back to back, the second group one phase
+// behind the first, with a workgroup barrier between phases: while one wave of a SIMD feeds
+// the matrix core, the other reads LDS.  Stage s + 2's direct-to-LDS loads go into stage s's
+// buffer once both groups have read it: the second group issues its half right after its own
+// last read of stage s, the first group its half one phase later; each waits for its loads
+// just before the barrier that precedes the first read of that stage.
+constexpr int kKsPhase = 2;                    // MFMA k-steps per phase
+constexpr int kPhases = kBK / 16 / kKsPhase;   // phases per stage
+static_assert(kPhases == 2, "two phases per stage");
+
+struct Frags {
+    bf16x8 a[kKsPhase][kTM];
+    bf16x8 b[kKsPhase][kTN];
+};
+
+typedef __attribute__((address_space(3))) const char lds_cchar;
+typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+
+// Byte offsets inside the shared block of this lane's fragment rows for each k-step of a stage
+// (buffer 0, tile 0): one register per k-step and operand; the buffer and tile offsets are
+// constants small enough for the instructions' offset field.  Loads go through a pointer
+// derived from the block itself, so the compiler knows they may alias the direct-to-LDS writes.
+struct FragAddr {
+    uint32_t a[kKsPhase * kPhases], b[kKsPhase * kPhases];
+};
+
+__device__ __forceinline__ FragAddr frag_addr(int wm, int wn, int lane) {
     const int q = (lane >> 5) ^ swz(lane & 31);
+    const uint32_t a0 =
+        uint32_t(offsetof(Smem, a)) + uint32_t((wm * kTM * 32 + (lane & 31)) * kBK * 2);
+    const uint32_t b0 =
+        uint32_t(offsetof(Smem, b)) + uint32_t((wn * kTN * 32 + (lane & 31)) * kBK * 2);
+    FragAddr fa;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-        const int off = (lane & 31) * kBK + ((2 * ks) ^ q) * 8;
-        bf16x8 fa[kTM], fb[kTN];
+    for (int ks = 0; ks < kKsPhase * kPhases; ++ks) {
+        fa.a[ks] = a0 + uint32_t(((2 * ks) ^ q) * 16);
+        fa.b[ks] = b0 + uint32_t(((2 * ks) ^ q) * 16);
+    }
+    return fa;
+}
+
+template <int BUF, int HALF>
+__device__ __forceinline__ void read_frags(const Smem& sm, const FragAddr& fa, Frags& f) {
+    lds_cchar* base = (lds_cchar*)(&sm);
+#pragma unroll
+    for (int kk = 0; kk < kKsPhase; ++kk) {
+        const int ks = HALF * kKsPhase + kk;
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
-            fa[i] = *reinterpret_cast<const bf16x8*>(
-                &sm.a[buf][(wm * kTM * 32 + i * 32) * kBK + off]);
+            f.a[kk][i] = *(lds_frag*)(base + fa.a[ks] + (BUF * kStageA + i * 32 * kBK) * 2);
 #pragma unroll
         for (int j = 0; j < kTN; ++j)
-            fb[j] = *reinterpret_cast<const bf16x8*>(
-                &sm.b[buf][(wn * kTN * 32 + j * 32) * kBK + off]);
+            f.b[kk][j] = *(lds_frag*)(base + fa.b[ks] + (BUF * kStageB + j * 32 * kBK) * 2);
+    }
+}
+
+__device__ __forceinline__ void mma_frags(const Frags& f, f32x16 (&acc)[kTM][kTN]) {
+#pragma unroll
+    for (int kk = 0; kk < kKsPhase; ++kk)
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
 #pragma unroll
             for (int j = 0; j < kTN; ++j)
-                acc[i][j] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j],
+                                                                   acc[i][j], 0, 0, 0);
 }
 
-__device__ __forceinline__ void wait_loads_and_sync() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stage loads are in LDS
-    __syncthreads();
+// A workgroup barrier that also keeps the compiler from moving memory accesses across it (a
+// wavefront-scope fence orders them for the compiler and emits no wait).
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
 // acc += the 256 x 256 block of A B^T for rows [0, n_here) of `hb` and rows
 // [col0, col0 + kBN) of `wb` (rows at or past lim_here and hidden elements at or past H read
 // as zero), in nk stages of kBK hidden elements: the one fixed accumulation order of every
-// logit, shared by the forward and the backward's recomputation.  The loads of stage kt + 1
-// go straight to the other LDS buffer while the matrix cores work on stage kt.  Ends with a
-// barrier (the stage buffers are free afterwards).
+// logit (k ascending into each accumulator), shared by the forward and the backward's
+// recomputation.  Every wave passes the same number of barriers (4 nk + 2); afterwards no
+// load is in flight and the stage buffers are free.
 __device__ __forceinline__ void block_product(Smem& sm, const uint16_t* __restrict__ hb,
                                               uint32_t ldh, int n_here,
                                               const uint16_t* __restrict__ wb, uint32_t ldw,
                                               int lim_here, int H, int col0, int nk, int wm,
                                               int wn, int lane, f32x16 (&acc)[kTM][kTN]) {
     const int wave = wm * kWN + wn;
+    const bool second = wave >= kThreads / kWave / 2;
     // the chunk a lane loads: position lane & 7 of row lane >> 3 of an 8-row group, whose
     // swizzle is (lane >> 3) ^ (wave & 1) (group bases are multiples of 8; odd groups flip)
     const int c = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
@@ -165,21 +219,68 @@ __device__ __forceinline__ void block_product(Smem& sm, const uint16_t* __restri
     plan_operand(hb, ldh, n_here, H, wave, lane, c, la);
     plan_operand(wb + int64_t(col0) * ldw, ldw, std::min(kBN, lim_here - col0), H, wave, lane,
                  c, lb);
+    constexpr int kPerStage = kChunksA + kChunksB;  // load instructions per wave per stage
+    static_assert(kPerStage == 8, "vmcnt immediates below assume 8 loads per stage");
     issue_operand(sm.a[0], la, 8 * c < H, 0, wave);
     issue_operand(sm.b[0], lb, 8 * c < H, 0, wave);
-    wait_loads_and_sync();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            const int k0 = (kt + 1) * kBK;
-            issue_operand(sm.a[cur ^ 1], la, k0 + 8 * c < H, k0, wave);
-            issue_operand(sm.b[cur ^ 1], lb, k0 + 8 * c < H, k0, wave);
-        }
-        __builtin_amdgcn_s_setprio(1);
-        mma_stage(sm, cur, wm, wn, lane, acc);
-        __builtin_amdgcn_s_setprio(0);
-        wait_loads_and_sync();
+    if (nk > 1) {
+        issue_operand(sm.a[1], la, kBK + 8 * c < H, kBK, wave);
+        issue_operand(sm.b[1], lb, kBK + 8 * c < H, kBK, wave);
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): this wave's part of stage 0 landed
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
+    const FragAddr fa = frag_addr(wm, wn, lane);
+    phase_barrier();
+    if (second) phase_barrier();  // the second group runs one phase behind
+    Frags f;
+    // stage s, phase HALF of buffer BUF: read, issue / wait loads, barrier, MFMAs, barrier
+    auto phase = [&](int s, auto buf_c, auto half_c) {
+        constexpr int BUF = decltype(buf_c)::value, HALF = decltype(half_c)::value;
+        read_frags<BUF, HALF>(sm, fa, f);
+        // the second half's reads must be done before the barrier (the buffer is reloaded in
+        // the next phase); the first half's may finish while the barrier synchronizes
+        if (HALF == 1) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        if (second && HALF == 1) {
+            // this group read stage s last: stage s + 2 may go into its buffer; then its part
+            // of stage s + 1 must have landed before the next barrier (the first group reads
+            // stage s + 1 right after it)
+            if (s + 2 < nk) {
+                const int k0 = (s + 2) * kBK;
+                issue_operand(sm.a[BUF], la, k0 + 8 * c < H, k0, wave);
+                issue_operand(sm.b[BUF], lb, k0 + 8 * c < H, k0, wave);
+                __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            }
+        }
+        if (!second && HALF == 0 && s >= 1 && s + 1 < nk) {
+            // the second group finished stage s - 1 one phase ago: stage s + 1 into its buffer
+            const int k0 = (s + 1) * kBK;
+            issue_operand(sm.a[BUF ^ 1], la, k0 + 8 * c < H, k0, wave);
+            issue_operand(sm.b[BUF ^ 1], lb, k0 + 8 * c < H, k0, wave);
+        }
+        phase_barrier();
+        if (HALF == 0) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_setprio(1);
+        mma_frags(f, acc);
+        __builtin_amdgcn_s_setprio(0);
+        if (!second && HALF == 1)
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this group's part of stage s + 1
+        phase_barrier();
+    };
+    int s = 0;
+    for (; s + 1 < nk; s += 2) {
+        phase(s, std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
+        phase(s, std::integral_constant<int, 0>(), std::integral_constant<int, 1>());
+        phase(s + 1, std::integral_constant<int, 1>(), std::integral_constant<int, 0>());
+        phase(s + 1, std::integral_constant<int, 1>(), std::integral_constant<int, 1>());
+    }
+    if (s < nk) {
+        phase(s, std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
+        phase(s, std::integral_constant<int, 0>(), std::integral_constant<int, 1>());
+    }
+    if (!second) phase_barrier();
 }
 
 // 8 waves per workgroup (148 KB of LDS, one workgroup per CU): two waves per SIMD cover each
@@ -269,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
 #pragma unroll
                 for (int q = 0; q < kRedCols / 4; ++q) {
                     const float4 x = *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
-                    mb = fmaxf(mb, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+                    mb = fmaxf(fmaxf(mb, x.x), fmaxf(x.y, fmaxf(x.z, x.w)));
                 }
                 // the selected logit: the thread whose columns hold the target picks it up
                 if (yr >= 0 && yr < kBN && ((yr >> 2) & (kRedThreads - 1)) == part)
@@ -282,10 +383,11 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
                     for (int q = 0; q < kRedCols / 4; ++q) {
                         const float4 x =
                             *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
-                        ls = ls + (x.x == kNegInf ? 0.0f : fwd_exp(x.x - mb));
-                        ls = ls + (x.y == kNegInf ? 0.0f : fwd_exp(x.y - mb));
-                        ls = ls + (x.z == kNegInf ? 0.0f : fwd_exp(x.z - mb));
-                        ls = ls + (x.w == kNegInf ? 0.0f : fwd_exp(x.w - mb));
+                        // exp2(-inf) = +0: a masked column adds +0 without a select
+                        ls = ls + fwd_exp(x.x - mb);
+                        ls = ls + fwd_exp(x.y - mb);
+                        ls = ls + fwd_exp(x.z - mb);
+                        ls = ls + fwd_exp(x.w - mb);
                     }
                 }
 #pragma unroll
