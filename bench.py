@@ -711,9 +711,11 @@ def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
 
 
 def time_linear_backward(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
-                         vocab: int = 151936, chunk_cols: int = 16384) -> dict:
+                         vocab: int = 151936, chunk_cols: int = 16384, out_dtype=None,
+                         cpu_baseline: bool = True) -> dict:
     """linear_logp backward on the same LM-head shape: dz recomputed (2 n V H flops), then
-    dh = dz W and dW = dz^T h (2 n V H flops each), 6 n V H flops per call."""
+    dh = dz W and dW = dz^T h (2 n V H flops each), 6 n V H flops per call; dh and dW written
+    in ``out_dtype`` (float32, or bfloat16 by linear_logp_backward_bf16)."""
     import torch
 
     from deterministic_selected_token_amd import linear
@@ -725,15 +727,17 @@ def time_linear_backward(dst, stream, steps: int, n: int = 8192, hidden: int = 4
         .to(torch.bfloat16)
     y = torch.randint(0, vocab, (n,), generator=gen, device=dev)
     g = torch.randn((n,), generator=gen, device=dev) * 0.01
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
     _, _, stats = linear.linear_logp_forward(h, W, y, vocab, vocab, stream=stream)
-    dh = torch.empty((n, hidden), dtype=torch.float32, device=dev)
-    dW = torch.empty((vocab, hidden), dtype=torch.float32, device=dev)
-    ws = torch.empty(linear.linear_logp_backward_workspace(n, hidden, chunk_cols),
-                     dtype=torch.uint8, device=dev)
+    dh = torch.empty((n, hidden), dtype=out_dtype, device=dev)
+    dW = torch.empty((vocab, hidden), dtype=out_dtype, device=dev)
+    ws_bytes = linear.linear_logp_backward_workspace(n, hidden, chunk_cols, out_dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step():
         linear.linear_logp_backward(h, W, y, g, stats, vocab, vocab, chunk_cols=chunk_cols,
-                                    dhidden=dh, dweight=dW, workspace=ws, stream=stream)
+                                    dhidden=dh, dweight=dW, workspace=ws, stream=stream,
+                                    out_dtype=out_dtype)
 
     step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
@@ -746,6 +750,13 @@ def time_linear_backward(dst, stream, steps: int, n: int = 8192, hidden: int = 4
     ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     flops = 6.0 * n * vocab * hidden
     del h, W, dW, ws
+    out = {"rows": n, "hidden": hidden, "vocab": vocab, "chunk_cols": chunk_cols,
+           "out_dtype": str(out_dtype).replace("torch.", ""), "ms": round(ms, 4),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "workspace_bytes": ws_bytes}
+    if not cpu_baseline:
+        return out
     # the float64 oracle on a bounded sample: 4 rows against the first 16384 vocabulary rows
     import numpy as np
 
@@ -762,11 +773,8 @@ def time_linear_backward(dst, stream, steps: int, n: int = 8192, hidden: int = 4
            "kind": "oracle", "cores": len(os.sched_getaffinity(0)),
            "sample": f"{rows} rows x {cols} vocabulary rows, float64 dz, dh and dW, "
                      f"{dt:.2f} s wall"}
-    return {"rows": n, "hidden": hidden, "vocab": vocab, "chunk_cols": chunk_cols,
-            "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "workspace_bytes": linear.linear_logp_backward_workspace(n, hidden, chunk_cols),
-            "cpu_baseline": cpu}
+    out["cpu_baseline"] = cpu
+    return out
 
 
 def main() -> int:
@@ -922,6 +930,8 @@ def main() -> int:
             dst, stream, max(3, args.steps // 4), inv_temperature=1 / 0.7, cpu_baseline=False)
         extra["variants"]["linear_logp_bwd"] = time_linear_backward(
             dst, stream, max(2, args.steps // 8))
+        extra["variants"]["linear_logp_bwd_bf16_out"] = time_linear_backward(
+            dst, stream, max(2, args.steps // 8), out_dtype=torch.bfloat16, cpu_baseline=False)
     if args.profile_copy:
         lib = load_ceiling_library()
         nbytes = 4 << 30

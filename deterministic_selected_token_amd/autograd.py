@@ -56,8 +56,8 @@ def selected_token_logp(logits: torch.Tensor, targets: torch.Tensor,
 class LinearLogp(torch.autograd.Function):
     """logp [n] (float32) of ``targets`` under the logits hidden W^T (BF16 hidden [n, H] and
     LM-head weight [V, H]), scored as fl32(acc * inv_temperature); gradients with respect to
-    hidden and weight from linear_logp_backward, accumulated in FP32 and rounded once to the
-    inputs' dtype."""
+    hidden and weight from linear_logp_backward_bf16: accumulated in FP32 and rounded once to
+    BF16, the inputs' dtype, inside the library."""
 
     @staticmethod
     def forward(ctx, hidden, weight, targets, vocab_real, active, ignore_index,
@@ -82,8 +82,9 @@ class LinearLogp(torch.autograd.Function):
         dh, dw = linear_logp_backward(hidden, weight, targets, grad_logp, stats, vocab_real,
                                       weight.shape[0], active=ctx.active,
                                       ignore_index=ignore_index,
-                                      inv_temperature=inv_temperature, chunk_cols=chunk_cols)
-        return (dh.to(hidden.dtype), dw.to(weight.dtype), None, None, None, None, None, None)
+                                      inv_temperature=inv_temperature, chunk_cols=chunk_cols,
+                                      out_dtype=torch.bfloat16)
+        return dh, dw, None, None, None, None, None, None
 
 
 def linear_logp(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,

@@ -517,13 +517,29 @@ __global__ __launch_bounds__(kThreads) void linear_dz_kernel(
     }
 }
 
-// c (=|+=) a b^T for one 256 x 256 block: a [m_pad, K] and b [n_pad, K] BF16 with K a
-// multiple of kBK and both zero-padded to whole blocks; FP32 results stored for
-// rows < m_real and columns < n_real.
-template <bool ACCUM>
+// Where gemm_tn_kernel's FP32 block results go.  The BF16 forms round to nearest even once,
+// after the FP32 value is complete; kOutAddBf16 forms that value exactly as kOutAddF32 does
+// (one FP32 add of the stored partial sum and the block's result), so its bits are the
+// rounding of what the FP32 forms would have stored.
+enum GemmOut : int {
+    kOutF32 = 0,     // c32 = acc
+    kOutAddF32 = 1,  // c32 = c32 + acc
+    kOutBf16 = 2,    // c16 = RNE_bf16(acc)
+    kOutAddBf16 = 3, // c16 = RNE_bf16(c32 + acc); c32 is read, not written
+};
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// c = a b^T (stored per OUT) for one 256 x 256 block: a [m_pad, K] and b [n_pad, K] BF16 with
+// K a multiple of kBK and both zero-padded to whole blocks; results stored for rows < m_real
+// and columns < n_real.
+template <int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_tn_kernel(
     const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ b, int64_t ldb,
-    int K, int m_real, int n_real, int m_blocks, float* __restrict__ c, int64_t ldc) {
+    int K, int m_real, int n_real, int m_blocks, float* __restrict__ c32, int64_t ld32,
+    uint16_t* __restrict__ c16, int64_t ld16) {
     __shared__ Smem sm;
     const int mb = static_cast<int>(blockIdx.x % static_cast<uint32_t>(m_blocks));
     const int nb = static_cast<int>(blockIdx.x / static_cast<uint32_t>(m_blocks));
@@ -549,11 +565,29 @@ __global__ __launch_bounds__(kThreads) void gemm_tn_kernel(
                 const int64_t row =
                     row0 + wm * (kTM * 32) + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
                 if (row < m_real && col < n_real) {
-                    float* p = c + row * ldc + col;
-                    *p = ACCUM ? *p + acc[i][j][r] : acc[i][j][r];
+                    const float v = acc[i][j][r];
+                    if constexpr (OUT == kOutF32) {
+                        c32[row * ld32 + col] = v;
+                    } else if constexpr (OUT == kOutAddF32) {
+                        float* p = c32 + row * ld32 + col;
+                        *p = *p + v;
+                    } else if constexpr (OUT == kOutBf16) {
+                        c16[row * ld16 + col] = bf16_bits(v);
+                    } else {
+                        c16[row * ld16 + col] = bf16_bits(c32[row * ld32 + col] + v);
+                    }
                 }
             }
         }
+    }
+}
+
+const void* gemm_tn(int out) {
+    switch (out) {
+        case kOutF32: return reinterpret_cast<const void*>(&gemm_tn_kernel<kOutF32>);
+        case kOutAddF32: return reinterpret_cast<const void*>(&gemm_tn_kernel<kOutAddF32>);
+        case kOutBf16: return reinterpret_cast<const void*>(&gemm_tn_kernel<kOutBf16>);
+        default: return reinterpret_cast<const void*>(&gemm_tn_kernel<kOutAddBf16>);
     }
 }
 
@@ -596,12 +630,13 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
     }
 }
 
-__global__ __launch_bounds__(256) void zero_rows_kernel(float* __restrict__ p, int64_t ld,
+template <typename T>
+__global__ __launch_bounds__(256) void zero_rows_kernel(T* __restrict__ p, int64_t ld,
                                                        int64_t rows, int cols) {
     const int64_t total = rows * cols;
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total;
          i += int64_t(gridDim.x) * 256)
-        p[(i / cols) * ld + i % cols] = 0.0f;
+        p[(i / cols) * ld + i % cols] = T(0);
 }
 
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -639,17 +674,25 @@ logp_status_t scratch_address(int dev, void** out) {
     return LOGP_OK;
 }
 
+// Bytes of the FP32 dhidden accumulator that the BF16-output backward keeps after the FP32
+// backward's staging: [n_pad, h_pad].
+int64_t dh_accumulator_bytes(int64_t n, int64_t hidden_size) {
+    return 4 * round_up(std::max<int64_t>(n, 1), kBM) * round_up(hidden_size, kBN);
+}
+
 // The backward with its staging either in the caller's workspace (use_scratch false) or in
 // this file's static `scratch` array on the launch device (use_scratch true: workspace and
 // workspace_bytes are ignored, and a call needing more than kNoallocScratchBytes is
-// LOGP_ERR_SCRATCH before anything is checked on the device).
+// LOGP_ERR_SCRATCH before anything is checked on the device).  dhidden and dweight are FP32
+// (bf16_out false) or BF16 bits (bf16_out true: dhidden is summed over the chunks in an FP32
+// accumulator after the staging and rounded once, by the last chunk's product).
 logp_status_t backward_impl(
     float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
     const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
     int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
-    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
-    int64_t ld_dh, float* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
-    int64_t chunk_cols, hipStream_t stream, bool use_scratch) {
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, void* dhidden,
+    int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream, bool use_scratch, bool bf16_out) {
     if (!(inv_temperature > 0.0f) || !std::isfinite(inv_temperature)) return LOGP_ERR_ARG;
     if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
         vocab_padded > (int64_t(1) << 31) - 1 - kTile || n > LINEAR_LOGP_BWD_MAX_ROWS)
@@ -681,8 +724,9 @@ logp_status_t backward_impl(
     if (!aligned16(hidden) || (weight != nullptr && !aligned16(weight)) ||
         (!use_scratch && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
         return LOGP_ERR_SHAPE;
-    const int64_t need = linear_logp_backward_workspace(n, H, chunk_cols);
-    if (need < 0) return LOGP_ERR_SHAPE;
+    const int64_t staging = linear_logp_backward_workspace(n, H, chunk_cols);
+    if (staging < 0) return LOGP_ERR_SHAPE;
+    const int64_t need = staging + (bf16_out ? dh_accumulator_bytes(n, H) : 0);
     if (use_scratch ? need > kNoallocScratchBytes : workspace_bytes < need)
         return use_scratch ? LOGP_ERR_SCRATCH : LOGP_ERR_SHAPE;
     if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
@@ -694,8 +738,9 @@ logp_status_t backward_impl(
                        {stats, uint64_t(n) * sizeof(logp_stats_t)}};
     // the static scratch array is not a caller buffer: it cannot overlap one, and it is not
     // checked as one
-    const Span out[] = {{dhidden, span_bytes(n, ld_dh, H, 4)},
-                        {dweight, width > 0 ? span_bytes(width, ld_dw, H, 4) : 0},
+    const int out_size = bf16_out ? 2 : 4;
+    const Span out[] = {{dhidden, span_bytes(n, ld_dh, H, out_size)},
+                        {dweight, width > 0 ? span_bytes(width, ld_dw, H, out_size) : 0},
                         {use_scratch ? nullptr : workspace, use_scratch ? 0 : uint64_t(need)}};
     int dev = -1;
     logp_status_t st = check_buffers(in, 6, out, 3, stream, &dev);
@@ -710,8 +755,9 @@ logp_status_t backward_impl(
     if (width == 0) {  // no vocabulary columns: this shard contributes dh = 0
         int cols = static_cast<int>(H);
         void* args[] = {&dhidden, &ld_dh, &n, &cols};
-        return launch(reinterpret_cast<const void*>(&zero_rows_kernel), dim3(1024), dim3(256),
-                      args, 0, stream);
+        const void* k = bf16_out ? reinterpret_cast<const void*>(&zero_rows_kernel<uint16_t>)
+                                 : reinterpret_cast<const void*>(&zero_rows_kernel<float>);
+        return launch(k, dim3(1024), dim3(256), args, 0, stream);
     }
 
     const int64_t n_pad = round_up(n, kBM), h_pad = round_up(H, kBN);
@@ -721,6 +767,12 @@ logp_status_t backward_impl(
     uint16_t* wT = hT + h_pad * n_pad;      // [h_pad, c_pad]
     uint16_t* dz = wT + h_pad * c_pad_max;  // [n_pad, c_pad]
     uint16_t* dzT = dz + n_pad * c_pad_max; // [c_pad, n_pad]
+    // FP32 dhidden: the caller's output, or (BF16 output) the accumulator after the staging
+    float* dh32 = bf16_out ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                                      staging)
+                           : static_cast<float*>(dhidden);
+    const int64_t ld32 = bf16_out ? h_pad : ld_dh;
+    uint16_t* dh16 = bf16_out ? static_cast<uint16_t*>(dhidden) : nullptr;
 
     int Hi = static_cast<int>(H), ni = static_cast<int>(n);
     {  // h^T, zero-padded
@@ -760,23 +812,25 @@ logp_status_t backward_impl(
                         dim3(kThreads), args, 0, stream);
             if (st != LOGP_OK) return st;
         }
-        {  // dh (=|+=) dz W: a = dz [n_pad, c_pad], b = W^T [h_pad, c_pad]
-            int64_t lda = c_pad, ldb = c_pad, ldc = ld_dh;
+        {  // dh (= | +=) dz W: a = dz [n_pad, c_pad], b = W^T [h_pad, c_pad]
+            const bool first = off == 0, last = off + chunk_cols >= width;
+            int out = first ? kOutF32 : kOutAddF32;
+            if (bf16_out && last) out = first ? kOutBf16 : kOutAddBf16;
+            int64_t lda = c_pad, ldb = c_pad, l32 = ld32, l16 = ld_dh;
             int K = static_cast<int>(c_pad), mr = ni, nr = Hi, mb = row_blocks;
-            void* args[] = {&dz, &lda, &wT, &ldb, &K, &mr, &nr, &mb, &dhidden, &ldc};
-            const void* k = off == 0 ? reinterpret_cast<const void*>(&gemm_tn_kernel<false>)
-                                     : reinterpret_cast<const void*>(&gemm_tn_kernel<true>);
-            st = launch(k, dim3(static_cast<uint32_t>(mb * (h_pad / kBN))), dim3(kThreads),
-                        args, 0, stream);
+            void* args[] = {&dz, &lda, &wT, &ldb, &K, &mr, &nr, &mb, &dh32, &l32, &dh16, &l16};
+            st = launch(gemm_tn(out), dim3(static_cast<uint32_t>(mb * (h_pad / kBN))),
+                        dim3(kThreads), args, 0, stream);
             if (st != LOGP_OK) return st;
         }
         {  // dW of the chunk's rows = dz^T h: a = dz^T [c_pad, n_pad], b = h^T [h_pad, n_pad]
             int64_t lda = n_pad, ldb = n_pad, ldc = ld_dw;
             int K = static_cast<int>(n_pad), mr = static_cast<int>(cw), nr = Hi;
             int mb = static_cast<int>(c_pad / kBM);
-            float* dwc = dweight + off * ld_dw;
-            void* args[] = {&dzT, &lda, &hT, &ldb, &K, &mr, &nr, &mb, &dwc, &ldc};
-            st = launch(reinterpret_cast<const void*>(&gemm_tn_kernel<false>),
+            float* dw32 = bf16_out ? nullptr : static_cast<float*>(dweight) + off * ld_dw;
+            uint16_t* dw16 = bf16_out ? static_cast<uint16_t*>(dweight) + off * ld_dw : nullptr;
+            void* args[] = {&dzT, &lda, &hT, &ldb, &K, &mr, &nr, &mb, &dw32, &ldc, &dw16, &ldc};
+            st = launch(gemm_tn(bf16_out ? kOutBf16 : kOutF32),
                         dim3(static_cast<uint32_t>(mb * (h_pad / kBN))), dim3(kThreads), args,
                         0, stream);
             if (st != LOGP_OK) return st;
@@ -879,7 +933,26 @@ logp_status_t linear_logp_backward_ex(
     return backward_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
                          vocab_padded, col_begin, col_end, targets, active, ignore_index,
                          grad_logp, stats, dhidden, ld_dh, dweight, ld_dw, workspace,
-                         workspace_bytes, chunk_cols, stream, false);
+                         workspace_bytes, chunk_cols, stream, false, false);
+}
+
+int64_t linear_logp_backward_bf16_workspace(int64_t n, int64_t hidden_size,
+                                            int64_t chunk_cols) {
+    const int64_t staging = linear_logp_backward_workspace(n, hidden_size, chunk_cols);
+    return staging < 0 ? -1 : staging + dh_accumulator_bytes(n, hidden_size);
+}
+
+logp_status_t linear_logp_backward_bf16(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, uint16_t* dhidden,
+    int64_t ld_dh, uint16_t* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream) {
+    return backward_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
+                         vocab_padded, col_begin, col_end, targets, active, ignore_index,
+                         grad_logp, stats, dhidden, ld_dh, dweight, ld_dw, workspace,
+                         workspace_bytes, chunk_cols, stream, false, true);
 }
 
 logp_status_t linear_logp_backward_noalloc(
@@ -891,7 +964,7 @@ logp_status_t linear_logp_backward_noalloc(
     return backward_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
                          vocab_padded, col_begin, col_end, targets, active, ignore_index,
                          grad_logp, stats, dhidden, ld_dh, dweight, ld_dw, nullptr, 0, chunk_cols,
-                         stream, true);
+                         stream, true, false);
 }
 
 logp_status_t linear_logp_backward(const uint16_t* hidden, int64_t ld_h, int64_t n,

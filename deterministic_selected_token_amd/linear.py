@@ -24,7 +24,8 @@ from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _shard_slot, _stre
 
 EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex", "linear_logp_backward",
             "linear_logp_backward_ex", "linear_logp_backward_workspace",
-            "linear_logp_backward_noalloc")
+            "linear_logp_backward_noalloc", "linear_logp_backward_bf16",
+            "linear_logp_backward_bf16_workspace")
 MAX_HIDDEN = 65536
 MAX_LD = 262144
 BWD_MAX_ROWS = 8388608
@@ -49,6 +50,11 @@ _lib.linear_logp_backward_noalloc.argtypes = (_lib.linear_logp_backward_ex.argty
 _lib.linear_logp_backward_noalloc.restype = ctypes.c_int32
 _lib.linear_logp_backward_workspace.argtypes = [_I64, _I64, _I64]
 _lib.linear_logp_backward_workspace.restype = _I64
+_lib.linear_logp_backward_bf16.argtypes = _lib.linear_logp_backward_ex.argtypes
+_lib.linear_logp_backward_bf16.restype = ctypes.c_int32
+_lib.linear_logp_backward_bf16_workspace.argtypes = [_I64, _I64, _I64]
+_lib.linear_logp_backward_bf16_workspace.restype = _I64
+_OUT_DTYPES = (torch.float32, torch.bfloat16)
 
 
 def _bf16_rows(name: str, t: torch.Tensor, device=None) -> torch.Tensor:
@@ -126,9 +132,15 @@ def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: tor
 
 
 def linear_logp_backward_workspace(n: int, hidden_size: int,
-                                   chunk_cols: int = DEFAULT_CHUNK_COLS) -> int:
-    """Workspace bytes that linear_logp_backward needs (-1 when out of range)."""
-    return int(_lib.linear_logp_backward_workspace(int(n), int(hidden_size), int(chunk_cols)))
+                                   chunk_cols: int = DEFAULT_CHUNK_COLS,
+                                   out_dtype: torch.dtype = torch.float32) -> int:
+    """Workspace bytes that linear_logp_backward needs for gradients of ``out_dtype`` (-1 when
+    out of range)."""
+    if out_dtype not in _OUT_DTYPES:
+        raise ValueError(f"out_dtype must be one of {_OUT_DTYPES}")
+    fn = _lib.linear_logp_backward_workspace if out_dtype == torch.float32 \
+        else _lib.linear_logp_backward_bf16_workspace
+    return int(fn(int(n), int(hidden_size), int(chunk_cols)))
 
 
 def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
@@ -140,16 +152,22 @@ def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: to
                          dhidden: Optional[torch.Tensor] = None,
                          dweight: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None,
-                         noalloc: bool = False):
-    """(dhidden [n, H] float32, dweight [col_end - col_begin, H] float32): the gradients of
+                         noalloc: bool = False, out_dtype: torch.dtype = torch.float32):
+    """(dhidden [n, H], dweight [col_end - col_begin, H]) of ``out_dtype``: the gradients of
     sum_t grad_logp[t] logp[t] with respect to hidden and to the weight rows
     W[col_begin:col_end] (``weight`` is that row slice), for the logits of linear_logp_forward
-    with the same inv_temperature; ``stats`` is the forward's (M, S).  The workspace (a
-    uint8 GPU tensor of at least linear_logp_backward_workspace(n, H, chunk_cols) bytes) is
-    allocated with torch when none is passed.  noalloc=True calls
+    with the same inv_temperature; ``stats`` is the forward's (M, S).  out_dtype float32 calls
+    linear_logp_backward(_ex); bfloat16 calls linear_logp_backward_bf16, whose outputs are the
+    FP32 results rounded once to nearest even inside the library.  The workspace (a uint8 GPU
+    tensor of at least linear_logp_backward_workspace(n, H, chunk_cols, out_dtype) bytes) is
+    allocated with torch when none is passed.  noalloc=True (float32 only) calls
     linear_logp_backward_noalloc instead, which stages in the library's static scratch array
     (at most NOALLOC_SCRATCH_BYTES of workspace) and allocates nothing; pass dhidden and
     dweight as well to keep torch from allocating them."""
+    if out_dtype not in _OUT_DTYPES:
+        raise ValueError(f"out_dtype must be one of {_OUT_DTYPES}")
+    if noalloc and out_dtype != torch.float32:
+        raise ValueError("noalloc writes float32 gradients only")
     hidden = _bf16_rows("hidden", hidden)
     dev = hidden.device
     weight = _bf16_rows("weight", weight, dev)
@@ -170,14 +188,15 @@ def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: to
     if weight.shape[0] < rows_needed:
         raise ValueError(f"weight holds {weight.shape[0]} rows, the range needs {rows_needed}")
     if dhidden is None:
-        dhidden = torch.empty((n, H), dtype=torch.float32, device=dev)
+        dhidden = torch.empty((n, H), dtype=out_dtype, device=dev)
     if dweight is None:
-        dweight = torch.empty((width, H), dtype=torch.float32, device=dev)
+        dweight = torch.empty((width, H), dtype=out_dtype, device=dev)
     for name, t, rows in (("dhidden", dhidden, n), ("dweight", dweight, width)):
-        if t.dtype != torch.float32 or t.device != dev or t.dim() != 2 or \
+        if t.dtype != out_dtype or t.device != dev or t.dim() != 2 or \
                 t.shape[0] != rows or t.shape[1] != H or (H > 1 and t.stride(1) != 1):
-            raise ValueError(f"{name} must be float32 [{rows}, {H}] with unit column stride")
-    need = linear_logp_backward_workspace(n, H, chunk_cols)
+            raise ValueError(f"{name} must be {out_dtype} [{rows}, {H}] with unit column "
+                             "stride")
+    need = linear_logp_backward_workspace(n, H, chunk_cols, out_dtype)
     if need < 0:
         raise ValueError("n, hidden size or chunk_cols out of range")
     head = (_ptr(hidden), _row_stride(hidden), n, H, _ptr(weight) if weight.numel() else None,
@@ -197,7 +216,10 @@ def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: to
     if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 GPU tensor")
     args = head + (_ptr(workspace), workspace.numel(), int(chunk_cols), _stream(dev, stream))
-    if inv_temperature == 1.0:
+    if out_dtype == torch.bfloat16:
+        _check("linear_logp_backward_bf16",
+               _lib.linear_logp_backward_bf16(float(inv_temperature), *args))
+    elif inv_temperature == 1.0:
         _check("linear_logp_backward", _lib.linear_logp_backward(*args))
     else:
         _check("linear_logp_backward_ex",

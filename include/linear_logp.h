@@ -144,6 +144,28 @@ LOGP_API logp_status_t linear_logp_backward_noalloc(
     int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
     int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, float* dhidden,
     int64_t ld_dh, float* dweight, int64_t ld_dw, int64_t chunk_cols, hipStream_t stream);
+/* linear_logp_backward_ex with the gradients written in BF16, the dtype of hidden and W (PR #495
+ * "zero-workspace backward for generic CUDA fused logp", Summary: the gradient is written in
+ * the inputs' dtype).  Every argument is as in linear_logp_backward_ex except:
+ *   dhidden       [n, ld_dh] BF16 bits: RNE_bf16 of the FP32 dhidden linear_logp_backward_ex
+ *                 forms (its sum over the chunks is kept in FP32 in the workspace and rounded
+ *                 once, so the bits are those of rounding that entry point's output to nearest
+ *                 even);
+ *   dweight       [col_end - col_begin, ld_dw] BF16 bits: RNE_bf16 of its FP32 dweight;
+ *   workspace     at least linear_logp_backward_bf16_workspace(n, H, chunk_cols) bytes: the
+ *                 FP32 entry point's workspace followed by the FP32 dhidden accumulator
+ *                 (4 x n x H bytes, each padded to a multiple of 256).
+ * A vocab-parallel caller that adds the ranks' dhidden should add FP32 partials (the FP32 entry
+ * point) and round the total: rounding each rank's dhidden first is a different result. */
+LOGP_API int64_t linear_logp_backward_bf16_workspace(int64_t n, int64_t hidden_size,
+                                                     int64_t chunk_cols); /* -1 out of range */
+LOGP_API logp_status_t linear_logp_backward_bf16(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, uint16_t* dhidden,
+    int64_t ld_dh, uint16_t* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream);
 /* linear_logp_backward_ex at inv_temperature = 1. */
 LOGP_API logp_status_t linear_logp_backward(
     const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,

@@ -67,7 +67,13 @@ def test_linear_logp_autograd_matches_the_library():
                                               inv_temperature=1 / 0.7)
     dh, dW = linear.linear_logp_backward(h.detach(), W.detach(), y, w, stats, V, V,
                                          inv_temperature=1 / 0.7, chunk_cols=4096)
+    dh16, dW16 = linear.linear_logp_backward(h.detach(), W.detach(), y, w, stats, V, V,
+                                             inv_temperature=1 / 0.7, chunk_cols=4096,
+                                             out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(logp.detach(), lp)
     assert h.grad.dtype == torch.bfloat16 and W.grad.dtype == torch.bfloat16
+    # the gradients are the library's BF16 outputs: the FP32 ones rounded to nearest even
+    assert torch.equal(h.grad.view(torch.int16), dh16.view(torch.int16))
+    assert torch.equal(W.grad.view(torch.int16), dW16.view(torch.int16))
     assert torch.equal(h.grad, dh.to(torch.bfloat16)) and torch.equal(W.grad, dW.to(torch.bfloat16))

@@ -456,3 +456,74 @@ def test_linear_row_strides_and_shard_views_bitwise():
     linear.linear_logp_partials(hs[:, :H], Ws[4096:, :H], y, V, V, 4096, 8192, pb[:, 1:])
     torch.cuda.synchronize()
     assert torch.equal(pa, pb)
+
+
+BF16_CASES = [
+    # n, H, V, Vp, chunk, (c0, c1) or None, inv_t
+    (70, 128, 9000, None, 4096, None, 1.0),             # 3 chunks: FP32 sum, rounded once
+    (257, 200, 5000, None, 8192, None, 1 / 0.7),        # 1 chunk: rounded straight away
+    (300, 64, 3 * T + 500, 4 * T, 4096, (T, 4 * T), 1.0),  # shard with padding columns
+    (33, 4096, 4100, None, 4096, None, 2.0),            # wide H, ragged last chunk
+]
+
+
+@pytest.mark.parametrize("n,H,V,Vp,chunk,shard,inv_t", BF16_CASES,
+                         ids=[f"n{c[0]}_H{c[1]}_V{c[2]}_ch{c[4]}" for c in BF16_CASES])
+def test_linear_backward_bf16_output_is_the_rounded_fp32(n, H, V, Vp, chunk, shard, inv_t):
+    """linear_logp_backward_bf16 writes the FP32 entry point's dh and dW rounded once to
+    nearest even: bitwise torch's float32 -> bfloat16 conversion of them, over one and several
+    chunks, a vocab shard and a temperature; and within the oracle's bound plus half a BF16
+    spacing."""
+    Vp = V if Vp is None else Vp
+    h, W, y = make(n, H, V, Vp, seed=n + H + 3, scale=2.0, pad_value=0.0)
+    active = (torch.arange(n, device=DEV) % 5 != 2).to(torch.uint8)
+    c0, c1 = (0, Vp) if shard is None else shard
+    Wv = W[c0:c1]
+    say(f"linear backward bf16 output n={n} H={H} V={V} Vp={Vp} chunk={chunk} shard={c0}:{c1}")
+    g = (torch.randn(n, generator=torch.Generator().manual_seed(n)) * 0.5).to(DEV)
+    _, _, stats = linear.linear_logp_forward(h, W, y, V, Vp, active=active,
+                                             inv_temperature=inv_t)
+    kw = dict(col_begin=c0, col_end=c1, active=active, inv_temperature=inv_t, chunk_cols=chunk)
+    dh32, dW32 = linear.linear_logp_backward(h, Wv, y, g, stats, V, Vp, **kw)
+    need = linear.linear_logp_backward_workspace(n, H, chunk, torch.bfloat16)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)  # contents irrelevant
+    dh16 = torch.full((n, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dW16 = torch.full((c1 - c0, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    for _ in range(2):  # the second call sees the first one's accumulator contents
+        linear.linear_logp_backward(h, Wv, y, g, stats, V, Vp, **kw, workspace=ws,
+                                    dhidden=dh16, dweight=dW16, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(dh16.view(torch.int16), dh32.to(torch.bfloat16).view(torch.int16))
+        assert torch.equal(dW16.view(torch.int16), dW32.to(torch.bfloat16).view(torch.int16))
+    # against the oracle: the FP32 bound of check_bwd widened by one rounding to BF16
+    if shard is None:
+        ref = bwd_reference(h, W, y, g, V, active=active, inv_t=inv_t)
+        hc, Wc = h.cpu().double().numpy(), W.cpu()[:V].double().numpy()
+        tol_dh = (2.0 ** -8 + (V / 16 + 2) * 2.0 ** -24) * (ref["scale"] @ np.abs(Wc))
+        tol_dh = tol_dh + 2.0 ** -8 * (np.abs(ref["dh"]) + tol_dh) + 1e-30
+        e_dh = np.abs(dh16.float().cpu().numpy().astype(np.float64) - ref["dh"])
+        assert np.all(e_dh <= tol_dh), e_dh.max()
+        tol_dW = (2.0 ** -8 + (n / 16 + 2) * 2.0 ** -24) * (ref["scale"].T @ np.abs(hc))
+        tol_dW = tol_dW + 2.0 ** -8 * (np.abs(ref["dW"]) + tol_dW) + 1e-30
+        e_dW = np.abs(dW16.float().cpu().numpy().astype(np.float64)[:V] - ref["dW"])
+        assert np.all(e_dW <= tol_dW), e_dW.max()
+    assert torch.all(dW16[max(0, V - c0):].float() == 0)  # padding rows of the view
+    say(f"bf16 output n={n} H={H}: bitwise the rounded FP32 gradients")
+
+
+def test_linear_backward_bf16_empty_shard_and_zero_rows():
+    """An empty vocab range writes dh = +0 in BF16; n = 0 writes nothing."""
+    n, H, V = 50, 128, 5000
+    h, W, y = make(n, H, V, seed=61)
+    g = torch.ones(n, device=DEV)
+    _, _, stats = linear.linear_logp_forward(h, W, y, V, V)
+    say("linear backward bf16 empty shard")
+    dh = torch.full((n, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    z, zw = linear.linear_logp_backward(h, W[:0], y, g, stats, V, V, col_begin=0, col_end=0,
+                                        dhidden=dh, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert z is dh and zw.shape == (0, H) and torch.all(dh.view(torch.int16) == 0)
+    e = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    a, b = linear.linear_logp_backward(e, W, y[:0], g[:0], stats[:0], V, V,
+                                       out_dtype=torch.bfloat16)
+    assert a.shape == (0, H) and b.shape == (V, H)

@@ -197,3 +197,55 @@ def test_noalloc_backward_rejects_work_beyond_its_scratch_array():
     # (then fails here only at the device check of the fake pointers)
     assert call_bwd(**big, chunk=8192) == DEVICE
     assert "static scratch" in linear._lib.logp_status_string(SCRATCH).decode()
+
+
+def call_bwd16(inv_t=1.0, **over):
+    a = dict(h=A, ld_h=64, n=10, H=64, w=A, ld_w=64, vr=5000, vp=5000, c0=0, c1=5000, y=A,
+             act=None, ign=-100, g=A, st=A, dh=A, ld_dh=64, dw=A, ld_dw=64, ws=A,
+             wsb=1 << 40, chunk=4096)
+    a.update(over)
+    return lib.linear_logp_backward_bf16(
+        inv_t, a["h"], a["ld_h"], a["n"], a["H"], a["w"], a["ld_w"], a["vr"], a["vp"], a["c0"],
+        a["c1"], a["y"], a["act"], a["ign"], a["g"], a["st"], a["dh"], a["ld_dh"], a["dw"],
+        a["ld_dw"], a["ws"], a["wsb"], a["chunk"], None)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(n=-1), SHAPE), (dict(vr=0), SHAPE), (dict(c0=100), SHARD), (dict(c1=4097), SHARD),
+    (dict(chunk=4000), SHAPE), (dict(n=0), OK), (dict(n=2 ** 23 + 1), SHAPE),
+    (dict(h=None), NULL), (dict(w=None), NULL), (dict(dh=None), NULL), (dict(dw=None), NULL),
+    (dict(ws=None), NULL), (dict(ld_dh=32), SHAPE), (dict(ld_dw=32), SHAPE), (dict(h=U), SHAPE),
+    (dict(ws=W16), SHAPE), (dict(wsb=1000), SHAPE),
+], ids=lambda v: str(v))
+def test_bf16_backward_validates_like_the_fp32_entry(over, want):
+    assert call_bwd16(**over) == want == call_bwd(1.0, **over)
+    assert call_bwd16(float("nan"), **over) == ARG
+
+
+def test_bf16_backward_workspace_adds_the_fp32_dh_accumulator():
+    import torch
+    ws, ws16 = linear.linear_logp_backward_workspace, lib.linear_logp_backward_bf16_workspace
+    for n, H, c in ((8192, 4096, 16384), (1, 8, 4096), (0, 8, 4096), (300, 200, 8192)):
+        n_pad, h_pad = -(-max(n, 1) // 256) * 256, -(-H // 256) * 256
+        assert ws16(n, H, c) == ws(n, H, c) + 4 * n_pad * h_pad
+        assert linear.linear_logp_backward_workspace(n, H, c, torch.bfloat16) == ws16(n, H, c)
+    assert ws16(-1, 8, 4096) == -1 and ws16(10, 0, 4096) == -1 and ws16(10, 8, 0) == -1
+    # a workspace that holds the FP32 staging but not the accumulator is short for BF16
+    fp32_only = ws(10, 64, 4096)
+    assert call_bwd16(wsb=fp32_only) == SHAPE
+    assert call_bwd16(wsb=ws16(10, 64, 4096)) == DEVICE  # then the fake pointers' device check
+    assert call_bwd(wsb=fp32_only) == DEVICE
+    with pytest.raises(ValueError, match="out_dtype"):
+        linear.linear_logp_backward_workspace(10, 64, 4096, torch.float16)
+
+
+def test_binding_bf16_output_arguments():
+    import torch
+    h = torch.zeros((2, 8), dtype=torch.bfloat16)
+    y = torch.zeros(2, dtype=torch.int64)
+    st = torch.zeros((2, 2))
+    with pytest.raises(ValueError, match="out_dtype"):
+        linear.linear_logp_backward(h, h, y, st[:, 0], st, out_dtype=torch.float16)
+    with pytest.raises(ValueError, match="noalloc"):
+        linear.linear_logp_backward(h, h, y, st[:, 0], st, noalloc=True,
+                                    out_dtype=torch.bfloat16)
