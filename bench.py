@@ -109,6 +109,7 @@ CEILING_LIB = os.path.join(ROOT, "tests", "probes", "libhbm_ceiling.so")
 # 4-wave workgroups, the backward's 16 vectors in 16-wave workgroups
 READ_SHAPES = ((8, 4), (16, 4), (16, 16), (32, 8))
 COPY_SHAPES = ((8, 16), (16, 16), (16, 8), (32, 8))
+MFMA_CEILING_LIB = os.path.join(ROOT, "tests", "probes", "libmfma_ceiling.so")
 
 
 def load_ceiling_library():
@@ -171,6 +172,82 @@ def hbm_ceiling(stream, gib: int = 10, reps: int = 6) -> dict:
     del src, dst
     torch.cuda.empty_cache()
     return out
+
+
+def mfma_ceiling(stream, reps: int = 5) -> dict:
+    """Measured dense BF16 matrix-core ceiling (tests/probes/mfma_ceiling.hip): chains of
+    independent v_mfma_f32_32x32x16_bf16 on register operands whose bits keep changing (the
+    ceiling), and on fixed operands (`static_operands`: less switching, less power, a higher
+    clock), no memory traffic, 1024 workgroups of the two wave shapes of the linear_logp
+    kernels, about 6 ms per launch; TFLOP/s of the median launch."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(MFMA_CEILING_LIB)  # built by __graft_entry__.build() with the probes
+    lib.mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mfma_bf16.restype = ctypes.c_int
+    lib.mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    lib.mfma_bf16_flops.restype = ctypes.c_double
+    dev = torch.device("cuda", 0)
+    groups, iters = 1024, 5000
+    out = {"tflops": 0.0, "static_operands_tflops": 0.0,
+           "kernel": "tests/probes/mfma_ceiling.hip (mfma_bf16)", "shapes": {}}
+    for waves, toggle in ((4, 1), (8, 1), (4, 0), (8, 0)):
+        sink = torch.empty(groups * waves * 64, dtype=torch.float32, device=dev)
+
+        def call(seed):
+            if lib.mfma_bf16(waves, groups, iters, seed, toggle, sink.data_ptr(),
+                             stream.cuda_stream):
+                raise RuntimeError("mfma ceiling probe failed")
+
+        call(1)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            call(2 + i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = median([a.elapsed_time(b) for a, b in evs])
+        tf = lib.mfma_bf16_flops(waves, groups, iters) / (ms * 1e-3) / 1e12
+        out["shapes"][f"{waves} waves/group, {'128 x 128' if waves == 4 else '64 x 128'} "
+                      f"per wave, {'switching' if toggle else 'fixed'} operands"] = round(tf, 1)
+        key = "tflops" if toggle else "static_operands_tflops"
+        out[key] = max(out[key], round(tf, 1))
+    return out
+
+
+def vendor_gemm_reference(stream, reps: int = 7, n: int = 8192, hidden: int = 4096,
+                          vocab: int = 151936) -> dict:
+    """Context, not part of the path: the unfused logits GEMM h W^T -> BF16 [n, V] through
+    torch.matmul (hipBLASLt) on the linear_logp shape; it forms and writes the logits and does
+    no reduction.  Its choice of kernel, and so its summation order, may change with n."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    h = torch.randn((n, hidden), generator=gen, device=dev).to(torch.bfloat16)
+    W = (torch.randn((vocab, hidden), generator=gen, device=dev) * (3.0 / hidden ** 0.5)) \
+        .to(torch.bfloat16)
+    out = torch.empty((n, vocab), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            torch.matmul(h, W.t(), out=out)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            torch.matmul(h, W.t(), out=out)
+            b.record(stream)
+    torch.cuda.synchronize()
+    ms = median([a.elapsed_time(b) for a, b in evs])
+    del h, W, out
+    torch.cuda.empty_cache()
+    return {"what": "torch.matmul(h, W.t()) -> bf16 logits (hipBLASLt), unfused, no reduction",
+            "rows": n, "hidden": hidden, "vocab": vocab, "ms": round(ms, 4),
+            "tflops": round(2.0 * n * vocab * hidden / (ms * 1e-3) / 1e12, 1)}
 
 
 def n_valid_rows(case) -> int:
@@ -795,6 +872,10 @@ def main() -> int:
                          "(reported under config.variants)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="end with one 4 GiB hbm_copy of the ceiling probe (counter scaling)")
+    ap.add_argument("--linear-forward-only", action="store_true",
+                    help="only three linear_logp forward calls on the 8192 x 4096 x 151936 "
+                         "shape, one JSON line (the short run the linear counter passes "
+                         "profile)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -819,6 +900,14 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.linear_forward_only:
+        lin = time_linear(dst, stream, 3, cpu_baseline=False)
+        print(json.dumps({"metric": "linear_logp forward TFLOP/s (8192 x 4096 x 151936)",
+                          "value": lin["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": 3,
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": "linear_logp forward only", **lin}}),
+              flush=True)
+        return 0
     quick = args.headline_only
     extra_steps = max(3, args.steps // 4)
 
@@ -932,6 +1021,13 @@ def main() -> int:
             dst, stream, max(2, args.steps // 8))
         extra["variants"]["linear_logp_bwd_bf16_out"] = time_linear_backward(
             dst, stream, max(2, args.steps // 8), out_dtype=torch.bfloat16, cpu_baseline=False)
+        mc = mfma_ceiling(stream)
+        extra["variants"]["mfma_bf16_ceiling"] = mc
+        extra["variants"]["vendor_gemm_reference"] = vendor_gemm_reference(stream)
+        for key in ("linear_logp_fwd", "linear_logp_fwd_temperature_0.7", "linear_logp_bwd",
+                    "linear_logp_bwd_bf16_out"):
+            v = extra["variants"][key]
+            v["frac_of_measured_mfma_ceiling"] = round(v["tflops"] / mc["tflops"], 4)
     if args.profile_copy:
         lib = load_ceiling_library()
         nbytes = 4 << 30

@@ -1,5 +1,6 @@
 """Build the probe libraries next to this file (hipcc, gfx950): libexp2_probe.so (the tests'
-hardware-exp2 check) and libhbm_ceiling.so (the bench's read and copy ceilings)."""
+hardware-exp2 check), libhbm_ceiling.so (the bench's read and copy ceilings) and
+libmfma_ceiling.so (the bench's dense BF16 matrix-core ceiling)."""
 
 from __future__ import annotations
 
@@ -13,9 +14,11 @@ sys.path.insert(0, ROOT)
 
 from deterministic_selected_token_amd import build as lib_build  # noqa: E402
 
-PROBES = {"libexp2_probe.so": "exp2_probe.hip", "libhbm_ceiling.so": "hbm_ceiling.hip"}
+PROBES = {"libexp2_probe.so": "exp2_probe.hip", "libhbm_ceiling.so": "hbm_ceiling.hip",
+          "libmfma_ceiling.so": "mfma_ceiling.hip"}
 OUT = os.path.join(HERE, "libexp2_probe.so")
 CEILING = os.path.join(HERE, "libhbm_ceiling.so")
+MFMA_CEILING = os.path.join(HERE, "libmfma_ceiling.so")
 
 
 def build() -> list[str]:

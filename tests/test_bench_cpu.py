@@ -88,3 +88,33 @@ def test_oracle_leg_counts_against_known_outputs():
     assert leg2["accuracy"]["dlogits"]["max_err"] >= acc["dlogits"]["max_err"]
     cpu = bench.cpu_baseline(leg, case, threads=3)
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] == 3
+
+
+def test_ceiling_probes_validate_arguments_on_the_host():
+    """The bench's ceiling probes refuse bad arguments before any launch (code 1), and the
+    matrix-core probe's flop count is its MFMA count times 2 x 32 x 32 x 16."""
+    import ctypes
+    import os
+
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes")
+    mfma = ctypes.CDLL(os.path.join(here, "libmfma_ceiling.so"))
+    mfma.mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    mfma.mfma_bf16_flops.restype = ctypes.c_double
+    mfma.mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                               ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    per = 2.0 * 32 * 32 * 16
+    assert mfma.mfma_bf16_flops(4, 1024, 5000) == 1024 * 4 * 5000 * 16 * per
+    assert mfma.mfma_bf16_flops(8, 256, 10) == 256 * 8 * 10 * 8 * per
+    for bad in ((2, 1, 1), (4, 0, 1), (4, 1, 0), (8, 1 << 31, 1)):
+        assert mfma.mfma_bf16_flops(*bad) == -1.0
+        assert mfma.mfma_bf16(*bad, 1, 1, ctypes.c_void_p(0x1000), None) == 1
+    assert mfma.mfma_bf16(4, 1, 1, 1, 1, None, None) == 1
+    assert mfma.mfma_bf16(4, 1, 1, 1, 2, ctypes.c_void_p(0x1000), None) == 1  # toggle 0 or 1
+    hbm = ctypes.CDLL(os.path.join(here, "libhbm_ceiling.so"))
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    hbm.hbm_read.argtypes = [P, I64, I32, I32, ctypes.c_uint32, P, P]
+    hbm.hbm_copy.argtypes = [P, P, I64, I32, I32, P]
+    a, b = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x8000000)
+    assert hbm.hbm_read(a, 1 << 20, 7, 4, 0, b, None) == 1      # no such shape
+    assert hbm.hbm_read(a, 1000, 8, 4, 0, b, None) == 1         # not whole chunks
+    assert hbm.hbm_copy(a, ctypes.c_void_p(0x10010), 1 << 20, 8, 4, None) == 1  # overlap
