@@ -86,7 +86,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Shapes offered: vectors_per_lane in {8, 16, 32} (8, 16, 32 KiB per wave) and waves per
 // workgroup in {4, 8, 16} (32 vectors per lane with 4 or 8 waves only: at 16 waves a lane
-// has 128 registers, too few for 32 vectors in flight).  Returns 0 on success, 1 for bad arguments (nothing launched),
+// has 128 registers, too few for 32 vectors in flight); reads also with 2 vectors per lane
+// in 4-wave and 4 vectors in 8-wave workgroups (smaller footprints read about 1% faster).  Returns 0 on success, 1 for bad arguments (nothing launched),
 // 2 for a launch error.  The caller owns every buffer; sink is one device uint32.
 CEILING_API int hbm_read(const void* src, int64_t bytes, int vectors_per_lane, int waves,
                          uint32_t key, uint32_t* sink, hipStream_t stream) {
@@ -96,6 +97,7 @@ CEILING_API int hbm_read(const void* src, int64_t bytes, int vectors_per_lane, i
     hipError_t e = hipErrorInvalidValue;
 #define READ_CASE(NV, W) \
     if (vectors_per_lane == NV && waves == W) e = launch_read<NV, W>(src, chunks, key, sink, stream);
+    READ_CASE(2, 4) READ_CASE(4, 8)
     READ_CASE(8, 4) READ_CASE(8, 8) READ_CASE(8, 16)
     READ_CASE(16, 4) READ_CASE(16, 8) READ_CASE(16, 16)
     READ_CASE(32, 4) READ_CASE(32, 8)
