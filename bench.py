@@ -728,9 +728,9 @@ def grpo_oracle_rate(lp, old, ref, adv, mask, nbytes: int) -> dict:
 def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
                 vocab: int = 151936, inv_temperature: float = 1.0,
                 cpu_baseline: bool = True) -> dict:
-    """linear_logp forward (linear_logp_partials + logp_merge) on n rows of a Qwen3-8B-shaped
-    LM head (hidden 4096, vocabulary 151936), logits scored at inv_temperature: 2 n V H flops
-    on the matrix cores."""
+    """linear_logp forward (linear_logp_partials with its balancing workspace + logp_merge) on
+    n rows of a Qwen3-8B-shaped LM head (hidden 4096, vocabulary 151936), logits scored at
+    inv_temperature: 2 n V H flops on the matrix cores."""
     import torch
 
     from deterministic_selected_token_amd import linear
@@ -745,12 +745,15 @@ def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
     partials = torch.empty((n, L, 3), dtype=torch.float32, device=dev)
     logp = torch.empty(n, dtype=torch.float32, device=dev)
     lse, stats = torch.empty_like(logp), torch.empty((n, 2), dtype=torch.float32, device=dev)
+    # the balanced launch (last rounds spread over every CU; the same bits)
+    ws = torch.empty(linear.linear_logp_partials_workspace(n, vocab, 0, vocab),
+                     dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         linear.linear_logp_partials(h, W, y, vocab, vocab, 0, vocab, partials, stream=stream,
-                                    inv_temperature=inv_temperature)
+                                    inv_temperature=inv_temperature, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
         dst.logp_merge(partials, y, vocab, logp=logp, lse=lse, stats=stats, stream=stream)
@@ -768,6 +771,7 @@ def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
     flops = 2.0 * n * vocab * hidden
     out = {"rows": n, "hidden": hidden, "vocab": vocab, "inv_temperature": inv_temperature,
            "partials_ms": round(k_ms, 4), "merge_ms": round(m_ms, 4),
+           "partials_workspace_bytes": ws.numel(),
            "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1),
            "frac_of_bf16_peak": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     if not cpu_baseline:
@@ -785,6 +789,46 @@ def time_linear(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
         "kind": "oracle", "cores": len(os.sched_getaffinity(0)),
         "sample": f"{rows} of the {n} rows, float64 logits and log-softmax, {dt:.2f} s wall "
                   "(including the float64 copy of W)"}
+    return out
+
+
+def time_linear_shard(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
+                      vocab: int = 151936, tiles: int = 5) -> dict:
+    """linear_logp_partials of one tensor-parallel rank's share at degree 8 (5 of the 38
+    4096-column tiles of W, 160 (row block, tile) workgroups for 256 CUs), with and without the
+    balancing workspace (the same bits): ms and TFLOP/s of each."""
+    import torch
+
+    from deterministic_selected_token_amd import linear
+
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev).manual_seed(13)
+    width = tiles * dst.TILE_COLS
+    h = torch.randn((n, hidden), generator=gen, device=dev).to(torch.bfloat16)
+    W = (torch.randn((width, hidden), generator=gen, device=dev) * (3.0 / hidden ** 0.5)) \
+        .to(torch.bfloat16)
+    y = torch.randint(0, vocab, (n,), generator=gen, device=dev)
+    partials = torch.empty((n, dst.logp_num_tiles(vocab), 3), dtype=torch.float32, device=dev)
+    ws = torch.empty(linear.linear_logp_partials_workspace(n, vocab, 0, width),
+                     dtype=torch.uint8, device=dev)
+    flops = 2.0 * n * width * hidden
+    out = {"rows": n, "hidden": hidden, "columns": width, "tiles": tiles}
+    for key, workspace in (("balanced", ws), ("one_launch", None)):
+        def call():
+            linear.linear_logp_partials(h, W, y, vocab, vocab, 0, width, partials,
+                                        stream=stream, workspace=workspace)
+        call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = median([a.elapsed_time(b) for a, b in evs])
+        out[key] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    del h, W, ws
+    torch.cuda.empty_cache()
     return out
 
 
@@ -1018,6 +1062,8 @@ def main() -> int:
         extra["variants"]["linear_logp_fwd"] = time_linear(dst, stream, max(3, args.steps // 4))
         extra["variants"]["linear_logp_fwd_temperature_0.7"] = time_linear(
             dst, stream, max(3, args.steps // 4), inv_temperature=1 / 0.7, cpu_baseline=False)
+        extra["variants"]["linear_logp_partials_tp8_rank"] = time_linear_shard(
+            dst, stream, max(5, args.steps // 4))
         extra["variants"]["linear_logp_bwd"] = time_linear_backward(
             dst, stream, max(2, args.steps // 8))
         extra["variants"]["linear_logp_bwd_bf16_out"] = time_linear_backward(

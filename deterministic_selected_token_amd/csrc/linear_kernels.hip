@@ -283,6 +283,103 @@ __device__ __forceinline__ void block_product(Smem& sm, const uint16_t* __restri
     if (!second) phase_barrier();
 }
 
+// One step of the tile's fold over its sub-blocks (the contract's order, b = 0 .. 15):
+// (m, s) <- (max(m, mb), s exp(m - m') + ls exp(mb - m')), terms of -inf maxima are 0.
+__device__ __forceinline__ void fold_subblock(float& m, float& s, float mb, float ls) {
+    const float m_new = fmaxf(m, mb);
+    const float a = m == kNegInf ? 0.0f : s * fwd_exp(m - m_new);
+    const float b = mb == kNegInf ? 0.0f : ls * fwd_exp(mb - m_new);
+    m = m_new;
+    s = a + b;
+}
+
+// Reduction of one 256 x 256 sub-block of scored logits (this wave's accumulators) through
+// LDS (the stage buffers are free when it starts; it ends with a barrier after the last LDS
+// read), one half of the row block at a time: each wave writes fl32(acc * inv_t) (masked
+// columns as -inf; inv_t = 1 leaves acc unchanged), then 4 threads per row reduce 64 columns
+// each and combine by a 2-level lane tree.  For each row r of the block (0..255):
+// on_sel(r, z) with the target's scored logit when the row's target column in the tile
+// (y_rel[r]) lies in this sub-block, and on_stats(r, mb, ls) with the sub-block's max and
+// sum-exp, both from one thread.  col_tile0: the sub-block's first column in the tile;
+// lim_tile: the tile's real columns (columns at or past it are masked).
+template <bool SCALED, typename OnSel, typename OnStats>
+__device__ __forceinline__ void reduce_subblock(Smem& sm, f32x16 (&acc)[kTM][kTN], int wm,
+                                                int wn, int lane, float inv_t, int col_tile0,
+                                                int lim_tile, const int* y_rel, OnSel on_sel,
+                                                OnStats on_stats) {
+    float* red = reinterpret_cast<float*>(&sm.a[0][0]);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int col = wn * (kTN * 32) + j * 32 + (lane & 31);  // in the sub-block
+            const bool ok = col_tile0 + col < lim_tile;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hr = wm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+                const float z = SCALED ? acc[i][j][r] * inv_t : acc[i][j][r];
+                red[hr * kRedRow + col] = ok ? z : kNegInf;
+            }
+        }
+        __syncthreads();
+        {
+            const int t = threadIdx.x;
+            const int hr = t / kRedThreads, part = t % kRedThreads;
+            const int row = (hr / 32) * (kTM * 32) + i * 32 + (hr % 32);  // in the block
+            // two passes over the row's columns in LDS (max, then the sum), so no row values
+            // stay in registers beside the accumulators of the other half
+            const int yr = y_rel[row] - col_tile0;  // target column in the sub-block
+            const float* src = &red[hr * kRedRow + 4 * part];
+            float mb = kNegInf;
+#pragma unroll
+            for (int q = 0; q < kRedCols / 4; ++q) {
+                const float4 x = *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
+                mb = fmaxf(fmaxf(mb, x.x), fmaxf(x.y, fmaxf(x.z, x.w)));
+            }
+            // the selected logit: the thread whose columns hold the target picks it up
+            if (yr >= 0 && yr < kBN && ((yr >> 2) & (kRedThreads - 1)) == part)
+                on_sel(row, red[hr * kRedRow + yr]);
+#pragma unroll
+            for (int o = 1; o < kRedThreads; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o, kWave));
+            float ls = 0.0f;
+            if (mb != kNegInf) {
+#pragma unroll
+                for (int q = 0; q < kRedCols / 4; ++q) {
+                    const float4 x = *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
+                    // exp2(-inf) = +0: a masked column adds +0 without a select
+                    ls = ls + fwd_exp(x.x - mb);
+                    ls = ls + fwd_exp(x.y - mb);
+                    ls = ls + fwd_exp(x.z - mb);
+                    ls = ls + fwd_exp(x.w - mb);
+                }
+            }
+#pragma unroll
+            for (int o = 1; o < kRedThreads; o <<= 1) ls = ls + __shfl_xor(ls, o, kWave);
+            if (part == 0) on_stats(row, mb, ls);
+        }
+        __syncthreads();
+    }
+}
+
+// Row constants of one (row block, tile): y_rel[t] = the target's column inside the tile for a
+// valid row whose target lies in it, else -1.
+// Used by the fold kernel only: in a kernel with a block product, calling it (rather than
+// writing the same conditions inline) made the compiler move the product's load descriptors
+// to vector registers and wrap every load in a loop over their distinct values.
+__device__ __forceinline__ int tile_target(int64_t row, int64_t n, const int64_t* targets,
+                                           const uint8_t* active, int64_t ignore_index,
+                                           int64_t vocab_real, int64_t tile_view_col0) {
+    int yr = -1;
+    if (row < n) {
+        int64_t y;
+        if (row_valid(targets, active, ignore_index, vocab_real, row, y)) {
+            const int64_t c = y - tile_view_col0;
+            if (c >= 0 && c < kTile) yr = static_cast<int>(c);
+        }
+    }
+    return yr;
+}
+
 // 8 waves per workgroup (148 KB of LDS, one workgroup per CU): two waves per SIMD cover each
 // other's global-load latency.
 // SCALED = false is the unit temperature: the multiply by inv_t (exact at 1) is left out, as
@@ -338,71 +435,10 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
         block_product(sm, hb, ldh, n_here, wb, ldw, lim_here, H, col0, nk, wm, wn, lane, acc);
-
-        // ---- sub-block reduction through LDS (the stage buffers are free now), one half of
-        // the row block at a time: each wave writes its scored accumulators
-        // fl32(acc * inv_t) (masked columns as -inf; inv_t = 1 leaves acc unchanged),
-        // then 4 threads per row reduce 64 columns each and combine by a 2-level lane tree.
-        float* red = reinterpret_cast<float*>(&sm.a[0][0]);
-#pragma unroll
-        for (int i = 0; i < kTM; ++i) {
-#pragma unroll
-            for (int j = 0; j < kTN; ++j) {
-                const int col = wn * (kTN * 32) + j * 32 + (lane & 31);  // in the sub-block
-                const bool ok = tile_col0 + sb * kBN + col < lim;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int hr = wm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-                    const float z = SCALED ? acc[i][j][r] * inv_t : acc[i][j][r];
-                    red[hr * kRedRow + col] = ok ? z : kNegInf;
-                }
-            }
-            __syncthreads();
-            {
-                const int t = threadIdx.x;
-                const int hr = t / kRedThreads, part = t % kRedThreads;
-                const int row = (hr / 32) * (kTM * 32) + i * 32 + (hr % 32);  // in the block
-                // two passes over the row's columns in LDS (max, then the sum), so no row
-                // values stay in registers beside the accumulators of the other half
-                const int yr = sm.y_rel[row] - sb * kBN;  // target column in the sub-block
-                const float* src = &red[hr * kRedRow + 4 * part];
-                float mb = kNegInf;
-#pragma unroll
-                for (int q = 0; q < kRedCols / 4; ++q) {
-                    const float4 x = *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
-                    mb = fmaxf(fmaxf(mb, x.x), fmaxf(x.y, fmaxf(x.z, x.w)));
-                }
-                // the selected logit: the thread whose columns hold the target picks it up
-                if (yr >= 0 && yr < kBN && ((yr >> 2) & (kRedThreads - 1)) == part)
-                    sm.sel[row] = red[hr * kRedRow + yr];
-#pragma unroll
-                for (int o = 1; o < kRedThreads; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o, kWave));
-                float ls = 0.0f;
-                if (mb != kNegInf) {
-#pragma unroll
-                    for (int q = 0; q < kRedCols / 4; ++q) {
-                        const float4 x =
-                            *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
-                        // exp2(-inf) = +0: a masked column adds +0 without a select
-                        ls = ls + fwd_exp(x.x - mb);
-                        ls = ls + fwd_exp(x.y - mb);
-                        ls = ls + fwd_exp(x.z - mb);
-                        ls = ls + fwd_exp(x.w - mb);
-                    }
-                }
-#pragma unroll
-                for (int o = 1; o < kRedThreads; o <<= 1) ls = ls + __shfl_xor(ls, o, kWave);
-                if (part == 0) {
-                    const float m_old = sm.m[row];
-                    const float m_new = fmaxf(m_old, mb);
-                    const float a = m_old == kNegInf ? 0.0f : sm.s[row] * fwd_exp(m_old - m_new);
-                    const float b = mb == kNegInf ? 0.0f : ls * fwd_exp(mb - m_new);
-                    sm.m[row] = m_new;
-                    sm.s[row] = a + b;
-                }
-            }
-            __syncthreads();
-        }
+        reduce_subblock<SCALED>(
+            sm, acc, wm, wn, lane, inv_t, col0, lim_here, sm.y_rel,
+            [&](int row, float z) { sm.sel[row] = z; },
+            [&](int row, float mb, float ls) { fold_subblock(sm.m[row], sm.s[row], mb, ls); });
         // the next sub-block's first barrier orders these LDS updates before any reuse
     }
     __syncthreads();
@@ -419,6 +455,105 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
     }
 }
 
+// ------------------------------------------------------------- balanced last rounds
+//
+// linear_partials_kernel runs one workgroup per (row block, tile), 16 sub-blocks each, so a
+// launch whose workgroup count is not a multiple of the CU count ends with a partly empty
+// round that still lasts 16 sub-blocks.  linear_logp_partials_ws runs whole rounds with it
+// (tiles [0, tile0)) and spreads the sub-blocks of the remaining tiles over every CU: each
+// task computes one sub-block's per-row (max, sum-exp) and target logit into the workspace,
+// and linear_fold_kernel folds a tile's sub-blocks in order b = 0, 1, ... with the same
+// fold_subblock steps, so the partials are bitwise those of the one-kernel launch (fully
+// masked sub-blocks, which leave the fold's state unchanged bit for bit, are not computed).
+
+// Task j: row block j % row_blocks of sub-block pair p = j / row_blocks, which is sub-block
+// p % kSubBlocks of tile tile0 + p / kSubBlocks (only the last tile with real columns has
+// fewer than kSubBlocks, and its pairs come last).  Workgroup g takes tasks g, g + grid, ...
+// With row blocks fastest, the tasks in flight share sub-blocks of W the way the workgroups
+// of linear_partials_kernel share tiles.
+template <bool SCALED>
+__global__ __launch_bounds__(kThreads) void linear_split_kernel(
+    const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
+    const uint16_t* __restrict__ w, int64_t ld_w, int lim, int row_blocks, int64_t col_begin,
+    int64_t vocab_real, float inv_t, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ active, int64_t ignore_index, int tile0, int tasks,
+    float2* __restrict__ ws_stats, float* __restrict__ ws_sel) {
+    __shared__ Smem sm;
+    const int lane = lane_id(), wave = wave_id();
+    const int wm = wave / kWN, wn = wave % kWN;
+    const uint32_t ldh = static_cast<uint32_t>(ld_h), ldw = static_cast<uint32_t>(ld_w);
+    const int nk = (H + kBK - 1) / kBK;
+    for (int j = static_cast<int>(blockIdx.x); j < tasks; j += static_cast<int>(gridDim.x)) {
+        const int rb_idx = j % row_blocks, pair = j / row_blocks;
+        const int tile = tile0 + pair / kSubBlocks, sb = pair % kSubBlocks;
+        const int64_t row0 = int64_t(rb_idx) * kBM;
+        const int tile_col0 = tile * kTile, col0 = sb * kBN;
+        // the previous task's reduction ended with a barrier after its last read of y_rel;
+        // block_product's barriers order these writes before this task's reduction
+        if (threadIdx.x < kBM) {
+            const int64_t row = row0 + threadIdx.x;
+            int yr = -1;
+            if (row < n) {
+                int64_t y;
+                if (row_valid(targets, active, ignore_index, vocab_real, row, y)) {
+                    const int64_t c = y - col_begin - tile_col0;
+                    if (c >= 0 && c < kTile) yr = static_cast<int>(c);
+                }
+            }
+            sm.y_rel[threadIdx.x] = yr;
+        }
+        const uint16_t* hb = h + row0 * ld_h;
+        const uint16_t* wb = w + int64_t(tile_col0) * ld_w;
+        const int n_here = static_cast<int>(std::min<int64_t>(kBM, n - row0));
+        const int lim_here = lim - tile_col0;
+        f32x16 acc[kTM][kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < kTN; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+        block_product(sm, hb, ldh, n_here, wb, ldw, lim_here, H, col0, nk, wm, wn, lane, acc);
+        float2* st = ws_stats + int64_t(j) * kBM;
+        float* se = ws_sel + int64_t(j) * kBM;
+        reduce_subblock<SCALED>(
+            sm, acc, wm, wn, lane, inv_t, col0, lim_here, sm.y_rel,
+            [&](int row, float z) { se[row] = z; },
+            [&](int row, float mb, float ls) { st[row] = make_float2(mb, ls); });
+    }
+}
+
+// One workgroup per (row block, tile of [tile0, view_tiles)), one thread per row: the tile's
+// partial from its sub-blocks' workspace entries.  nsb_last: sub-blocks of tile real_tiles - 1
+// (the last with real columns); tiles at or past real_tiles have none.
+__global__ __launch_bounds__(kBM) void linear_fold_kernel(
+    int64_t n, int row_blocks, int tile0, int real_tiles, int nsb_last,
+    const float2* __restrict__ ws_stats, const float* __restrict__ ws_sel,
+    const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
+    int64_t ignore_index, int64_t vocab_real, int64_t col_begin,
+    logp_partial_t* __restrict__ partials, int64_t ldp) {
+    const int rb_idx = static_cast<int>(blockIdx.x % static_cast<uint32_t>(row_blocks));
+    const int tile = tile0 + static_cast<int>(blockIdx.x / static_cast<uint32_t>(row_blocks));
+    const int r = threadIdx.x;
+    const int64_t row = int64_t(rb_idx) * kBM + r;
+    if (row >= n) return;
+    const int nsb = tile < real_tiles - 1 ? kSubBlocks : (tile == real_tiles - 1 ? nsb_last : 0);
+    const int64_t pair0 = int64_t(tile - tile0) * kSubBlocks;
+    float m = kNegInf, s = 0.0f;
+    for (int b = 0; b < nsb; ++b) {
+        const float2 v = ws_stats[((pair0 + b) * row_blocks + rb_idx) * kBM + r];
+        fold_subblock(m, s, v.x, v.y);
+    }
+    float sel = 0.0f;
+    const int yr = tile_target(row, n, targets, active, ignore_index, vocab_real,
+                               col_begin + int64_t(tile) * kTile);
+    if (yr >= 0) sel = ws_sel[((pair0 + yr / kBN) * row_blocks + rb_idx) * kBM + r];
+    logp_partial_t p;
+    p.max = m;
+    p.sumexp = s;
+    p.sel = sel;
+    partials[row * ldp + tile] = p;
+}
 
 // ------------------------------------------------------------------------------ backward
 //
@@ -839,17 +974,43 @@ logp_status_t backward_impl(
     return LOGP_OK;
 }
 
-}  // namespace
+// Compute units of `dev` (cached; the launch device is current when this is called).
+int compute_units(int dev) {
+    static std::mutex mu;
+    static int cached[kMaxScratchDevices] = {};
+    if (dev < 0 || dev >= kMaxScratchDevices) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            cus < 1) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
 
-extern "C" {
+// Sub-blocks (pairs) of the tiles [t0, view tiles) that hold real columns: every tile before
+// the last real one has kSubBlocks, that one ceil(its real columns / kBN).
+int64_t split_pairs(int64_t lim, int64_t t0) {
+    if (lim <= 0) return 0;
+    const int64_t real_tiles = ceil_div(lim, kTile);
+    if (t0 >= real_tiles) return 0;
+    const int64_t nsb_last = ceil_div(lim - (real_tiles - 1) * kTile, kBN);
+    return (real_tiles - 1 - t0) * kSubBlocks + nsb_last;
+}
 
-logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hidden,
-                                      int64_t ld_h, int64_t n, int64_t hidden_size,
-                                      const uint16_t* weight, int64_t ld_w, int64_t vocab_real,
-                                      int64_t vocab_padded, int64_t col_begin, int64_t col_end,
-                                      const int64_t* targets, const uint8_t* active,
-                                      int64_t ignore_index, logp_partial_t* partials,
-                                      int64_t ldp, hipStream_t stream) {
+constexpr int64_t kSplitTaskBytes = int64_t(kBM) * (sizeof(float2) + sizeof(float));
+
+logp_status_t partials_impl(float inv_temperature, const uint16_t* hidden, int64_t ld_h,
+                            int64_t n, int64_t hidden_size, const uint16_t* weight, int64_t ld_w,
+                            int64_t vocab_real, int64_t vocab_padded, int64_t col_begin,
+                            int64_t col_end, const int64_t* targets, const uint8_t* active,
+                            int64_t ignore_index, logp_partial_t* partials, int64_t ldp,
+                            void* workspace, int64_t workspace_bytes, hipStream_t stream) {
     if (!(inv_temperature > 0.0f) || !std::isfinite(inv_temperature)) return LOGP_ERR_ARG;
     if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
         vocab_padded > (int64_t(1) << 31) - 1 - kTile)
@@ -857,6 +1018,9 @@ logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hid
     if (col_begin < 0 || col_end < col_begin || col_end > vocab_padded ||
         col_begin % kTile != 0 || (col_end % kTile != 0 && col_end != vocab_padded))
         return LOGP_ERR_SHARD;
+    if (workspace_bytes < 0 ||
+        (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+        return LOGP_ERR_SHAPE;
     if (n == 0 || col_end == col_begin) return LOGP_OK;
     // weight rows actually read: the view's real vocabulary rows (none for an all-padding view,
     // whose weight pointer may then be NULL)
@@ -878,28 +1042,113 @@ logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hid
     const int64_t view_tiles = ceil_div(width, kTile);
     if (ldp < view_tiles) return LOGP_ERR_SHAPE;
     if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
+    const int64_t row_blocks = ceil_div(n, kBM);
+    if (row_blocks * view_tiles > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
     const Span in[] = {{hidden, span_bytes(n, ld_h, H, 2)},
                        {weight, lim > 0 ? span_bytes(lim, ld_w, H, 2) : 0},
                        {targets, uint64_t(n) * 8},
                        {active, active ? uint64_t(n) : 0}};
-    const Span out[] = {{partials, span_bytes(n, ldp, view_tiles, sizeof(logp_partial_t))}};
+    const Span out[] = {{partials, span_bytes(n, ldp, view_tiles, sizeof(logp_partial_t))},
+                        {workspace, workspace != nullptr ? uint64_t(workspace_bytes) : 0}};
     int dev = -1;
-    logp_status_t st = check_buffers(in, 4, out, 1, stream, &dev);
+    logp_status_t st = check_buffers(in, 4, out, 2, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
     if (!guard.ok()) return LOGP_ERR_HIP;
-    const int64_t row_blocks = ceil_div(n, kBM);
-    if (row_blocks * view_tiles > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
+
+    // Split the work when the workspace allows it and the balanced schedule is shorter: whole
+    // rounds of one workgroup per (row block, tile) for the tiles [0, t0), then the sub-blocks
+    // of the rest spread over every CU (in units of one sub-block's time per CU, plus two for
+    // the fold launch).
+    int64_t t0 = view_tiles, tasks = 0;
+    const int cus = workspace != nullptr ? compute_units(dev) : 0;
+    if (cus > 0) {
+        const int64_t items = row_blocks * view_tiles;
+        const int64_t c0 = ((items / cus) * cus) / row_blocks;  // whole tiles in whole rounds
+        const int64_t t_split = row_blocks * split_pairs(lim, c0);
+        const int64_t one = ceil_div(items, cus) * kSubBlocks;
+        const int64_t two = ceil_div(row_blocks * c0, cus) * kSubBlocks + ceil_div(t_split, cus) + 2;
+        if (two < one && t_split * kSplitTaskBytes <= workspace_bytes && t_split <= 0x7FFFFFFF) {
+            t0 = c0;
+            tasks = t_split;
+        }
+    }
     int Hi = static_cast<int>(H), lim_i = static_cast<int>(lim);
     int rbk = static_cast<int>(row_blocks);
-    void* args[] = {&hidden,    &ld_h,       &n,     &Hi,     &weight,       &ld_w,
-                    &lim_i,     &rbk,        &col_begin,     &vocab_real,   &inv_temperature,
-                    &targets,   &active,     &ignore_index,  &partials,     &ldp};
-    const void* kernel = inv_temperature == 1.0f
-                             ? reinterpret_cast<const void*>(&linear_partials_kernel<false>)
-                             : reinterpret_cast<const void*>(&linear_partials_kernel<true>);
-    return launch(kernel, dim3(static_cast<uint32_t>(row_blocks * view_tiles)), dim3(kThreads),
-                  args, 0, stream);
+    if (t0 > 0) {
+        void* args[] = {&hidden,    &ld_h,       &n,     &Hi,     &weight,       &ld_w,
+                        &lim_i,     &rbk,        &col_begin,     &vocab_real,   &inv_temperature,
+                        &targets,   &active,     &ignore_index,  &partials,     &ldp};
+        const void* kernel = inv_temperature == 1.0f
+                                 ? reinterpret_cast<const void*>(&linear_partials_kernel<false>)
+                                 : reinterpret_cast<const void*>(&linear_partials_kernel<true>);
+        st = launch(kernel, dim3(static_cast<uint32_t>(row_blocks * t0)), dim3(kThreads), args,
+                    0, stream);
+        if (st != LOGP_OK) return st;
+    }
+    if (t0 == view_tiles) return LOGP_OK;
+    float2* ws_stats = static_cast<float2*>(workspace);
+    float* ws_sel = reinterpret_cast<float*>(ws_stats + tasks * kBM);
+    int tile0 = static_cast<int>(t0), ntask = static_cast<int>(tasks);
+    if (tasks > 0) {
+        void* args[] = {&hidden,  &ld_h,      &n,          &Hi,           &weight,
+                        &ld_w,    &lim_i,     &rbk,        &col_begin,    &vocab_real,
+                        &inv_temperature, &targets, &active, &ignore_index, &tile0,
+                        &ntask,   &ws_stats,  &ws_sel};
+        const void* kernel = inv_temperature == 1.0f
+                                 ? reinterpret_cast<const void*>(&linear_split_kernel<false>)
+                                 : reinterpret_cast<const void*>(&linear_split_kernel<true>);
+        st = launch(kernel, dim3(static_cast<uint32_t>(std::min<int64_t>(cus, tasks))),
+                    dim3(kThreads), args, 0, stream);
+        if (st != LOGP_OK) return st;
+    }
+    const int64_t real_tiles = lim > 0 ? ceil_div(lim, kTile) : 0;
+    int rt = static_cast<int>(real_tiles);
+    int nsb_last = lim > 0 ? static_cast<int>(ceil_div(lim - (real_tiles - 1) * kTile, kBN)) : 0;
+    void* fa[] = {&n,       &rbk,          &tile0,  &rt,        &nsb_last,   &ws_stats,
+                  &ws_sel,  &targets,      &active, &ignore_index, &vocab_real, &col_begin,
+                  &partials, &ldp};
+    return launch(reinterpret_cast<const void*>(&linear_fold_kernel),
+                  dim3(static_cast<uint32_t>(row_blocks * (view_tiles - t0))), dim3(kBM), fa, 0,
+                  stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t linear_logp_partials_workspace(int64_t n, int64_t vocab_real, int64_t col_begin,
+                                       int64_t col_end) {
+    if (n < 0 || vocab_real < 1 || col_begin < 0 || col_end < col_begin ||
+        n > (int64_t(1) << 40) || col_end > (int64_t(1) << 31))
+        return -1;
+    const int64_t lim = std::max<int64_t>(0, std::min(col_end - col_begin, vocab_real - col_begin));
+    return ceil_div(std::max<int64_t>(n, 1), kBM) * split_pairs(lim, 0) * kSplitTaskBytes;
+}
+
+logp_status_t linear_logp_partials_ws(float inv_temperature, const uint16_t* hidden,
+                                      int64_t ld_h, int64_t n, int64_t hidden_size,
+                                      const uint16_t* weight, int64_t ld_w, int64_t vocab_real,
+                                      int64_t vocab_padded, int64_t col_begin, int64_t col_end,
+                                      const int64_t* targets, const uint8_t* active,
+                                      int64_t ignore_index, logp_partial_t* partials,
+                                      int64_t ldp, void* workspace, int64_t workspace_bytes,
+                                      hipStream_t stream) {
+    return partials_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
+                         vocab_padded, col_begin, col_end, targets, active, ignore_index,
+                         partials, ldp, workspace, workspace_bytes, stream);
+}
+
+logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hidden,
+                                      int64_t ld_h, int64_t n, int64_t hidden_size,
+                                      const uint16_t* weight, int64_t ld_w, int64_t vocab_real,
+                                      int64_t vocab_padded, int64_t col_begin, int64_t col_end,
+                                      const int64_t* targets, const uint8_t* active,
+                                      int64_t ignore_index, logp_partial_t* partials,
+                                      int64_t ldp, hipStream_t stream) {
+    return partials_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
+                         vocab_padded, col_begin, col_end, targets, active, ignore_index,
+                         partials, ldp, nullptr, 0, stream);
 }
 
 logp_status_t linear_logp_partials(const uint16_t* hidden, int64_t ld_h, int64_t n,

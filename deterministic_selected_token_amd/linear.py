@@ -22,7 +22,8 @@ import torch
 from . import (TILE_COLS, _active, _check, _lib, _ptr, _rows, _shard_slot, _stream,
                logp_merge, logp_num_tiles)
 
-EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex", "linear_logp_backward",
+EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex", "linear_logp_partials_ws",
+            "linear_logp_partials_workspace", "linear_logp_backward",
             "linear_logp_backward_ex", "linear_logp_backward_workspace",
             "linear_logp_backward_noalloc", "linear_logp_backward_bf16",
             "linear_logp_backward_bf16_workspace")
@@ -39,6 +40,11 @@ _lib.linear_logp_partials.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64
 _lib.linear_logp_partials.restype = ctypes.c_int32
 _lib.linear_logp_partials_ex.argtypes = [ctypes.c_float] + _lib.linear_logp_partials.argtypes
 _lib.linear_logp_partials_ex.restype = ctypes.c_int32
+_lib.linear_logp_partials_ws.argtypes = (_lib.linear_logp_partials_ex.argtypes[:-1]
+                                         + [_P, _I64, _P])
+_lib.linear_logp_partials_ws.restype = ctypes.c_int32
+_lib.linear_logp_partials_workspace.argtypes = [_I64, _I64, _I64, _I64]
+_lib.linear_logp_partials_workspace.restype = _I64
 _lib.linear_logp_backward.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64,
                                       _P, _P, _I64, _P, _P, _P, _I64, _P, _I64, _P, _I64, _I64,
                                       _P]
@@ -71,13 +77,25 @@ def _row_stride(t: torch.Tensor) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else int(max(t.shape[1], t.stride(0), 8))
 
 
+def linear_logp_partials_workspace(n: int, vocab_real: int, col_begin: int,
+                                   col_end: int) -> int:
+    """Workspace bytes with which linear_logp_partials can always balance its last rounds
+    (-1 when out of range)."""
+    return int(_lib.linear_logp_partials_workspace(int(n), int(vocab_real), int(col_begin),
+                                                   int(col_end)))
+
+
 def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
                          vocab_real: int, vocab_padded: int, col_begin: int, col_end: int,
                          partials: torch.Tensor, active=None, ignore_index: int = -100,
-                         stream=None, inv_temperature: float = 1.0) -> torch.Tensor:
+                         stream=None, inv_temperature: float = 1.0,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Write the (m, s, sel) partials of vocab columns [col_begin, col_end) of the scored
     logits fl32(h W^T * inv_temperature) into the full ``partials`` buffer; ``weight`` is the
-    row slice W[col_begin:col_end].  inv_temperature = 1 calls the plain entry point."""
+    row slice W[col_begin:col_end].  With a ``workspace`` (a contiguous uint8 GPU tensor,
+    linear_logp_partials_workspace bytes always suffice) linear_logp_partials_ws balances the
+    launch's last rounds over every CU, with bitwise the same partials; without one,
+    inv_temperature = 1 calls the plain entry point."""
     if not isinstance(hidden, torch.Tensor):
         raise TypeError("hidden must be a torch.Tensor")
     slot = _shard_slot(partials, hidden.shape[0], col_begin, col_end)
@@ -99,7 +117,14 @@ def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: to
     args = (_ptr(hidden), _row_stride(hidden), n, H, _ptr(weight), _row_stride(weight),
             int(vocab_real), int(vocab_padded), int(col_begin), int(col_end), _ptr(targets),
             _ptr(active), int(ignore_index), first.data_ptr(), ldp, _stream(dev, stream))
-    if inv_temperature == 1.0:
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != dev or \
+                workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor on the same "
+                             "device")
+        _check("linear_logp_partials_ws", _lib.linear_logp_partials_ws(
+            float(inv_temperature), *args[:-1], _ptr(workspace), workspace.numel(), args[-1]))
+    elif inv_temperature == 1.0:
         _check("linear_logp_partials", _lib.linear_logp_partials(*args))
     else:
         _check("linear_logp_partials_ex",
@@ -113,19 +138,26 @@ def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: tor
                         partials: Optional[torch.Tensor] = None,
                         logp: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                         stats: Optional[torch.Tensor] = None, stream=None,
-                        inv_temperature: float = 1.0):
+                        inv_temperature: float = 1.0,
+                        workspace: Optional[torch.Tensor] = None, balance: bool = True):
     """logp, LSE and (M, S) of the scored logits fl32(h W^T * inv_temperature) over the
     whole vocabulary: linear_logp_partials over all tiles, then logp_merge -> (logp, lse,
-    stats)."""
+    stats).  balance=True (the default) passes a workspace, allocated with torch when none is
+    given, so that the last rounds spread over every CU; the results are the same bits."""
     vocab_padded = weight.shape[0] if vocab_padded is None else int(vocab_padded)
     vocab_real = vocab_padded if vocab_real is None else int(vocab_real)
     n = hidden.shape[0]
     L = logp_num_tiles(vocab_padded)
     if partials is None:
         partials = torch.empty((n, L, 3), dtype=torch.float32, device=hidden.device)
+    if balance and workspace is None and n > 0:
+        need = linear_logp_partials_workspace(n, vocab_real, 0, vocab_padded)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
     linear_logp_partials(hidden, weight, targets, vocab_real, vocab_padded, 0, vocab_padded,
                          partials, active=active, ignore_index=ignore_index, stream=stream,
-                         inv_temperature=inv_temperature)
+                         inv_temperature=inv_temperature,
+                         workspace=workspace if balance else None)
     return logp_merge(partials, targets, vocab_real, num_tiles=L, active=active,
                       ignore_index=ignore_index, logp=logp, lse=lse, stats=stats,
                       stream=stream)

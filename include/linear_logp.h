@@ -86,6 +86,37 @@ LOGP_API logp_status_t linear_logp_partials_ex(float inv_temperature, const uint
                                                int64_t ignore_index, logp_partial_t* partials,
                                                int64_t ldp, hipStream_t stream);
 
+/* linear_logp_partials_ex with a caller workspace that lets the launch balance its last rounds
+ * (same source passages as linear_logp_partials).  One workgroup per (256-row block, tile)
+ * leaves a launch whose workgroup count is not a multiple of the device's compute-unit count
+ * with a final round that still lasts a whole tile; with the workspace, the call runs the
+ * whole rounds that way and spreads the 256-column sub-blocks of the remaining tiles over
+ * every compute unit, each writing its rows' (m_b, s_b) and target logit to the workspace, then
+ * folds each tile's sub-blocks in the contract's order b = 0, 1, ... (sub-blocks with no real
+ * column leave the fold unchanged bit for bit and are skipped).  The partials are bitwise those
+ * of linear_logp_partials_ex at every shape; the call decides from the device's compute-unit
+ * count whether the split shortens the schedule and otherwise launches as
+ * linear_logp_partials_ex does.
+ *   workspace        device memory, 256-byte aligned, owned by the caller, contents irrelevant
+ *                    on entry, not overlapping any other argument (LOGP_ERR_OVERLAP); NULL or
+ *                    fewer bytes than the split needs means no split.
+ *   workspace_bytes  its size; linear_logp_partials_workspace(n, vocab_real, col_begin,
+ *                    col_end) bytes always suffice (3072 bytes per 256-row block and
+ *                    256-column sub-block of the view's real columns).
+ * Every other argument and error as in linear_logp_partials_ex; a misaligned workspace or
+ * negative workspace_bytes is LOGP_ERR_SHAPE. */
+LOGP_API int64_t linear_logp_partials_workspace(int64_t n, int64_t vocab_real, int64_t col_begin,
+                                                int64_t col_end);  /* -1 when out of range */
+LOGP_API logp_status_t linear_logp_partials_ws(float inv_temperature, const uint16_t* hidden,
+                                               int64_t ld_h, int64_t n, int64_t hidden_size,
+                                               const uint16_t* weight, int64_t ld_w,
+                                               int64_t vocab_real, int64_t vocab_padded,
+                                               int64_t col_begin, int64_t col_end,
+                                               const int64_t* targets, const uint8_t* active,
+                                               int64_t ignore_index, logp_partial_t* partials,
+                                               int64_t ldp, void* workspace,
+                                               int64_t workspace_bytes, hipStream_t stream);
+
 /* Backward of linear_logp: the gradients of sum over valid rows t of g_t logp_t (logp of the
  * scored logits z = fl32(acc(h W^T) * inv_temperature) of linear_logp_partials_ex) with respect
  * to h and to the shard's rows of W.  The derivative through logp is the logp path's backward

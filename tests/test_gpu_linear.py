@@ -527,3 +527,42 @@ def test_linear_backward_bf16_empty_shard_and_zero_rows():
     a, b = linear.linear_logp_backward(e, W, y[:0], g[:0], stats[:0], V, V,
                                        out_dtype=torch.bfloat16)
     assert a.shape == (0, H) and b.shape == (V, H)
+
+
+BALANCED = [
+    # n, H, V, Vp, (c0, c1) view or None, inv_t
+    (8192, 256, 151936, 151936, None, 1.0),                 # 1216 items: whole rounds + split
+    (8192, 256, 151936, 151936, (4 * T, 9 * T), 1 / 0.7),   # a 5-tile view: all split
+    (2048, 128, 151936, 152064, (36 * T, 152064), 1.0),     # the last real and a padding tile
+    (4100, 128, 70000, 18 * T, None, 1.0),                  # ragged rows, padded vocabulary
+    (33, 64, 5000, 5000, None, 2.0),                        # a single round: all split
+]
+
+
+@pytest.mark.parametrize("n,H,V,Vp,view,inv_t", BALANCED,
+                         ids=[f"n{c[0]}_V{c[2]}_{'view' if c[4] else 'full'}" for c in BALANCED])
+def test_linear_balanced_partials_are_bitwise(n, H, V, Vp, view, inv_t):
+    """linear_logp_partials_ws (last rounds spread over every CU, sub-blocks folded from the
+    workspace) writes bitwise the partials of the one-kernel launch, on views, padding and
+    ragged shapes; a workspace too small for the split gives the same bits too."""
+    h, W, y = make(n, H, V, Vp, seed=n + V, scale=2.0, pad_value=float("nan"))
+    c0, c1 = (0, Vp) if view is None else view
+    L = dst.logp_num_tiles(Vp)
+    say(f"balanced partials n={n} H={H} V={V}/{Vp} view=[{c0},{c1})")
+    outs = []
+    for ws_bytes in (None, linear.linear_logp_partials_workspace(n, V, c0, c1), 256):
+        P = torch.full((n, L, 3), float("nan"), device=DEV)
+        ws = None if ws_bytes is None else torch.full((max(ws_bytes, 1),), 0x5A,
+                                                      dtype=torch.uint8, device=DEV)
+        linear.linear_logp_partials(h, W[c0:], y, V, Vp, c0, c1, P, inv_temperature=inv_t,
+                                    workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(P)
+    for P in outs[1:]:
+        assert torch.equal(P.view(torch.int32), outs[0].view(torch.int32))
+    if view is None:
+        a = linear.linear_logp_forward(h, W, y, V, Vp, inv_temperature=inv_t, balance=False)
+        b = linear.linear_logp_forward(h, W, y, V, Vp, inv_temperature=inv_t)
+        torch.cuda.synchronize()
+        for u, v in zip(a, b):
+            assert torch.equal(u.view(torch.int32), v.view(torch.int32))

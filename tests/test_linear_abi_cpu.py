@@ -249,3 +249,42 @@ def test_binding_bf16_output_arguments():
     with pytest.raises(ValueError, match="noalloc"):
         linear.linear_logp_backward(h, h, y, st[:, 0], st, noalloc=True,
                                     out_dtype=torch.bfloat16)
+
+
+def call_ws(inv_t=1.0, ws=A, wsb=1 << 30, **over):
+    a = dict(h=A, ld_h=64, n=10, H=64, w=A, ld_w=64, vr=5000, vp=5000, c0=0, c1=5000, y=A,
+             act=None, ign=-100, p=A, ldp=2)
+    a.update(over)
+    return lib.linear_logp_partials_ws(inv_t, a["h"], a["ld_h"], a["n"], a["H"], a["w"],
+                                       a["ld_w"], a["vr"], a["vp"], a["c0"], a["c1"], a["y"],
+                                       a["act"], a["ign"], a["p"], a["ldp"], ws, wsb, None)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(n=-1), SHAPE), (dict(c0=100), SHARD), (dict(n=0), OK), (dict(h=None), NULL),
+    (dict(w=U), SHAPE), (dict(ldp=1), SHAPE), (dict(H=60, ld_h=64, ld_w=64), SHAPE),
+], ids=lambda v: str(v))
+def test_balanced_partials_validate_like_the_plain_entry(over, want):
+    assert call_ws(**over) == want == call_ex(1.0, **over)
+    assert call_ws(0.0, **over) == ARG
+
+
+def test_balanced_partials_workspace_checks():
+    # a workspace must be 256-byte aligned and its size non-negative; NULL means no split
+    assert call_ws(ws=ctypes.c_void_p(0x10010)) == SHAPE
+    assert call_ws(wsb=-1) == SHAPE
+    assert call_ws(ws=None, wsb=0) == DEVICE  # then the fake pointers' device check
+    assert call_ws() == DEVICE
+
+
+def test_balanced_partials_workspace_size():
+    """3072 bytes (a float2 and a float per row of a 256-row block) per row block and
+    256-column sub-block holding real columns of the view."""
+    q = linear.linear_logp_partials_workspace
+    assert q(8192, 151936, 0, 151936) == 32 * 594 * 3072            # 593.5 sub-blocks, rounded up
+    assert q(8192, 151936, 0, 152064) == q(8192, 151936, 0, 151936)   # padding adds nothing
+    assert q(8192, 151936, 16384, 36864) == 32 * 80 * 3072            # 5 tiles of a view
+    assert q(300, 8200, 0, 12288) == 2 * 33 * 3072                    # ragged rows and columns
+    assert q(0, 100, 0, 4096) == q(1, 100, 0, 4096) == 3072
+    assert q(10, 5000, 8192, 12288) == 0                              # an all-padding view
+    assert q(-1, 10, 0, 10) == -1 and q(10, 0, 0, 10) == -1 and q(10, 10, 5, 4) == -1
