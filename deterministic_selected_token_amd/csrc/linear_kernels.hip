@@ -7,11 +7,14 @@
 // wave holds a 64 x 128 block; the hidden states and weight rows are staged through
 // double-buffered LDS by direct-to-LDS buffer loads, and the two groups of four waves
 // alternate between reading fragments from LDS and feeding the matrix cores), reduces the
-// block to a
-// per-row (max, sum-exp) through LDS (half the rows at a time, 4 threads per row over 64
-// columns each, then a 2-level lane tree), and folds it into the row's running tile state in
-// LDS.  After the last sub-block the tile's (m, s, sel) partial is written in logp.h's layout,
-// and logp_merge completes the forward.  The logits never leave the chip.
+// block to a per-row (max, sum-exp) through LDS (half the rows at a time, 4 threads per row
+// over 64 columns each, then a 2-level lane tree), and folds it into the row's running tile
+// state in LDS.  After the last sub-block the tile's (m, s, sel) partial is written in logp.h's
+// layout, and logp_merge completes the forward.  The logits never leave the chip.  With a
+// workspace the launch's last rounds are balanced: the remaining tiles' sub-blocks spread over
+// every CU and are folded afterwards in the same order (linear_split_kernel,
+// linear_fold_kernel).  The backward recomputes each logits block with the same product and
+// forms dh and dW with TN products (linear_dz_kernel, gemm_tn_kernel).
 //
 // Sources: PR #495 (Summary) names the fused LM-head + logp op; issue #241 ("PR 3", "PR6")
 // and PR #314 (Tensor Parallel doc) fix the per-tile partials and their merge.
