@@ -103,6 +103,24 @@ def test_linear_qwen_width_sampled():
     say(f"qwen width: {res}")
 
 
+def test_linear_full_batch_balanced_sampled():
+    """8192 rows of the Qwen3-8B LM head (H = 4096, V = 151936) through the balanced launch
+    (whole rounds of the per-tile kernel, the last tiles' sub-blocks spread over every CU and
+    folded from the workspace): rows from the first, middle and last row blocks against the
+    oracle, and every row bitwise equal to the one-kernel launch."""
+    n, H, V = 8192, 4096, 151936
+    h, W, y = make(n, H, V, seed=8192)
+    say(f"linear balanced full batch n={n} H={H} V={V}, workspace "
+        f"{linear.linear_logp_partials_workspace(n, V, 0, V)} B")
+    rows = np.array([0, 1, 255, 256, 1000, 2047, 4096, 5555, 7935, 7936, 8190, 8191])
+    res, got = check(h, W, y, V, rows=rows)
+    say(f"balanced full batch: {res}")
+    ref = linear.linear_logp_forward(h, W, y, V, balance=False)
+    torch.cuda.synchronize()
+    for u, v in zip(got, ref):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
 def test_linear_masks_and_targets():
     h, W, y = make(70, 128, 9000, seed=7, ignore_frac=0.0)
     y[0] = 0
