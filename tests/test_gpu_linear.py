@@ -103,19 +103,21 @@ def test_linear_qwen_width_sampled():
     say(f"qwen width: {res}")
 
 
-def test_linear_full_batch_balanced_sampled():
+@pytest.mark.parametrize("inv_t", [1.0, 1 / 0.7], ids=["unit", "inv_t1.43"])
+def test_linear_full_batch_balanced_sampled(inv_t):
     """8192 rows of the Qwen3-8B LM head (H = 4096, V = 151936) through the balanced launch
     (whole rounds of the per-tile kernel, the last tiles' sub-blocks spread over every CU and
-    folded from the workspace): rows from the first, middle and last row blocks against the
-    oracle, and every row bitwise equal to the one-kernel launch."""
+    folded from the workspace), at unit temperature and scored at 1/0.7: rows from the first,
+    middle and last row blocks against the oracle, and every row bitwise equal to the
+    one-kernel launch."""
     n, H, V = 8192, 4096, 151936
     h, W, y = make(n, H, V, seed=8192)
-    say(f"linear balanced full batch n={n} H={H} V={V}, workspace "
+    say(f"linear balanced full batch n={n} H={H} V={V} inv_t={inv_t:.4g}, workspace "
         f"{linear.linear_logp_partials_workspace(n, V, 0, V)} B")
     rows = np.array([0, 1, 255, 256, 1000, 2047, 4096, 5555, 7935, 7936, 8190, 8191])
-    res, got = check(h, W, y, V, rows=rows)
+    res, got = check(h, W, y, V, rows=rows, inv_t=inv_t)
     say(f"balanced full batch: {res}")
-    ref = linear.linear_logp_forward(h, W, y, V, balance=False)
+    ref = linear.linear_logp_forward(h, W, y, V, balance=False, inv_temperature=inv_t)
     torch.cuda.synchronize()
     for u, v in zip(got, ref):
         assert torch.equal(u.view(torch.int32), v.view(torch.int32))
