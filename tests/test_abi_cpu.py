@@ -48,6 +48,60 @@ def test_every_declared_function_is_exported():
     assert exported == set(names)  # nothing else with the prefixes leaks out
 
 
+C_CONSUMER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "logp.h"
+#include "grpo_loss.h"
+#include "linear_logp.h"
+
+typedef void (*fn_t)(void);
+/* every declared entry point, so that the link must resolve each one */
+static const fn_t entry_points[] = {
+%(table)s
+};
+
+int main(void) {
+    const uint16_t* fake = (const uint16_t*)(uintptr_t)0x1000; /* never dereferenced */
+    if (logp_num_tiles(151936) != 38 || logp_num_tiles(159744) != 39) return 1;
+    if (strcmp(logp_status_string(LOGP_OK), "ok") != 0) return 2;
+    /* host validation only: nothing is launched for these */
+    if (logp_forward(fake, 151936, -1, 151936, 151936, (const int64_t*)fake, NULL, -100,
+                     (float*)(uintptr_t)0x1000, NULL, NULL, NULL) != LOGP_ERR_SHAPE) return 3;
+    if (logp_forward(fake, 151936, 0, 151936, 151936, NULL, NULL, -100, NULL, NULL, NULL,
+                     NULL) != LOGP_OK) return 4;
+    if (linear_logp_partials_workspace(8192, 151936, 0, 151936) != (int64_t)32 * 594 * 3072)
+        return 5;
+    printf("%%d entry points linked\n", (int)(sizeof entry_points / sizeof entry_points[0]));
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None or not os.path.isdir("/opt/rocm/include"),
+                    reason="needs gcc and the ROCm headers")
+def test_headers_compile_and_link_as_c99():
+    """include/*.h are plain C: a C99 program (the HIP runtime's own headers taken as system
+    headers, ours under -pedantic -Werror) that names every declared entry point links
+    against the built library and runs its host-side calls."""
+    names = declared_functions()
+    table = "\n".join(f"    (fn_t){name}," for name in names)
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "consumer.c")
+        exe = os.path.join(tmp, "consumer")
+        with open(src, "w") as f:
+            f.write(C_CONSUMER % {"table": table})
+        cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+               "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-isystem", "/opt/rocm/include", src,
+               "-L", PKG, "-llogp_mi355x", f"-Wl,-rpath,{PKG}",
+               "-Wl,-rpath-link,/opt/rocm/lib", "-o", exe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0, (r.returncode, r.stderr)
+        assert r.stdout.strip() == f"{len(names)} entry points linked"
+
+
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert re.search(r"#define LOGP_TILE_COLS (\d+)", text).group(1) == str(dst.TILE_COLS)
