@@ -48,7 +48,7 @@ def case_in(dtype: str, n, v, p=None, ld=None, sigma=3.0, seed=0, **kw):
     return c.to(DEV)
 
 
-def check_ex(case, inv_t=1.0, rows=None, ulps=1.0, min_cr=None):
+def check_ex(case, inv_t=1.0, rows=None, ulps=1.0, min_cr=None, cr_skip_targets=False):
     x = case.logits[:, :case.vocab_padded]
     logp, lse, stats = dst.logp_forward_ex(x, case.targets, case.vocab_real, case.vocab_padded,
                                            active=case.active, inv_temperature=inv_t)
@@ -64,7 +64,7 @@ def check_ex(case, inv_t=1.0, rows=None, ulps=1.0, min_cr=None):
     fwd = check_forward_scaled(host[rt], y[rows], case.vocab_real, None if act is None
                                else act[rows], logp.cpu().numpy()[rows],
                                lse.cpu().numpy()[rows], stats.cpu().numpy()[rows], inv_t)
-    t = BackwardTally()
+    t = BackwardTally(cr_skip_targets=cr_skip_targets)
     t.add_block(host[rt], y[rows], g[rows], case.vocab_real, case.vocab_padded,
                 None if act is None else act[rows], -100, host_values(d[rt.to(DEV)]),
                 case.name, inv_temperature=inv_t, ulps=ulps)

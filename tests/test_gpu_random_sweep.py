@@ -1,0 +1,138 @@
+"""Seeded random sweep over the shapes, dtypes and options of both GPU paths, each case against
+the FP64 oracle and the bitwise contract.
+
+Every case draws its configuration from its own seed (numpy PCG64): for the logp path the
+logits dtype (BF16, FP16, FP32), rows, real and padded vocabulary (with a share of tile-edge
+widths), the row stride, the temperature, the logit scale and the shares of ignored, bad and
+inactive targets; for linear_logp the rows, hidden size, real and padded vocabulary and
+temperature.  Checks, with the tolerances of the dedicated tests (test_gpu_dtypes.py,
+test_gpu_linear.py):
+  - logp forward and backward against the oracle on every row (the correctly-rounded share
+    of dlogits counted over the non-target entries: at V = 7 and scores of spread 20 a
+    dominant target's g' (1 - p) cancels in FP32 in a sizeable share of the rows, and the
+    per-element bound, with its 2^-20 |g'| term at the target, holds it instead);
+  - a random tile-aligned shard layout of the partials merged back bitwise to the forward,
+    and the backward of a random column range bitwise equal to that range of the full one;
+  - linear_logp's forward against the oracle on every row, the balanced launch bitwise equal
+    to the one-kernel launch, a random shard layout merged back bitwise, and the backward's
+    dh and dW against the oracle.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import deterministic_selected_token_amd as dst
+from deterministic_selected_token_amd import linear
+from test_gpu_dtypes import case_in, check_ex, same_bits
+from test_gpu_linear import bwd_reference, bwd_run, check, check_bwd, make
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+T = dst.TILE_COLS
+EDGE_WIDTHS = [1, 7, T - 1, T, T + 1, 2 * T, 3 * T - 8, 5 * T + 3]
+
+
+def say(msg: str):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def random_layout(rng, tiles: int) -> list[int]:
+    """Tiles per shard, summing to `tiles`, 1 to 4 shards."""
+    k = int(rng.integers(1, min(4, tiles) + 1))
+    cuts = sorted(rng.choice(np.arange(1, tiles), size=k - 1, replace=False).tolist()) \
+        if k > 1 else []
+    edges = [0] + cuts + [tiles]
+    return [b - a for a, b in zip(edges, edges[1:])]
+
+
+def logp_config(seed: int) -> dict:
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "f16", "f32"][seed % 3]
+    vr = int(rng.choice(EDGE_WIDTHS)) if rng.random() < 0.4 else int(rng.integers(1, 20000))
+    vp = vr + (0 if rng.random() < 0.5 else int(rng.integers(1, 2 * T)))
+    ld = vp + (0 if rng.random() < 0.5 else int(rng.integers(1, 64)))
+    return dict(rng=rng, dtype=dtype, n=int(rng.integers(1, 97)), vr=vr, vp=vp, ld=ld,
+                inv_t=float(rng.choice([1.0, 1 / 0.7, 2.0, 0.5])),
+                sigma=float(rng.choice([1.0, 3.0, 10.0])),
+                ignore=float(rng.choice([0.0, 0.1])), bad=float(rng.choice([0.0, 0.1])),
+                inactive=float(rng.choice([0.0, 0.2])))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_logp_random_case(seed):
+    c = logp_config(seed)
+    rng, dtype, n, vr, vp, ld, inv_t = (c[k] for k in ("rng", "dtype", "n", "vr", "vp", "ld",
+                                                       "inv_t"))
+    say(f"logp sweep seed={seed}: {dtype} n={n} V={vr}/{vp} ld={ld} inv_t={inv_t:.4g} "
+        f"sigma={c['sigma']}")
+    case = case_in(dtype, n, vr, vp, ld=ld, sigma=c["sigma"], seed=seed,
+                   ignore_frac=c["ignore"], bad_target_frac=c["bad"],
+                   inactive_frac=c["inactive"])
+    ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, None)
+    (logp, lse, stats, d), fwd, bwd = check_ex(case, inv_t=inv_t, ulps=ulps, min_cr=min_cr,
+                                               cr_skip_targets=True)
+    say(f"seed={seed}: {fwd} {bwd}")
+
+    # a random tile-aligned shard layout merges back to the forward's bits
+    x = case.logits[:, :vp]
+    L = dst.logp_num_tiles(vp)
+    layout = random_layout(rng, L) if L > 1 else [1]
+    partials = torch.full((n, L, 3), float("nan"), dtype=torch.float32, device=DEV)
+    c0 = 0
+    for tiles in layout:
+        c1 = min(vp, c0 + tiles * T)
+        dst.logp_partials_ex(x[:, c0:c1], case.targets, vr, vp, c0, c1, partials,
+                             active=case.active, inv_temperature=inv_t)
+        c0 = c1
+    got = dst.logp_merge(partials, case.targets, vr, active=case.active)
+    assert all(same_bits(u, w) for u, w in zip((logp, lse, stats), got)), layout
+
+    # the backward of a random column range is that range of the full backward
+    b0 = int(rng.integers(0, vp))
+    b1 = int(rng.integers(b0 + 1, vp + 1))
+    part = dst.logp_backward_ex(x[:, b0:b1], case.targets, case.grad, stats, vr, vp,
+                                col_begin=b0, col_end=b1, active=case.active,
+                                inv_temperature=inv_t)
+    torch.cuda.synchronize()
+    assert same_bits(part, d[:, b0:b1]), (b0, b1)
+
+
+def linear_config(seed: int) -> dict:
+    rng = np.random.default_rng(2000 + seed)
+    V = int(rng.choice(EDGE_WIDTHS[1:])) if rng.random() < 0.3 else int(rng.integers(1, 12000))
+    Vp = V + (0 if rng.random() < 0.5 else int(rng.integers(1, 2 * T)))
+    return dict(rng=rng, n=int(rng.integers(1, 300)),
+                H=int(8 * rng.integers(1, 80)), V=V, Vp=Vp,
+                inv_t=float(rng.choice([1.0, 1 / 0.7, 2.0])))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_linear_random_case(seed):
+    c = linear_config(seed)
+    rng, n, H, V, Vp, inv_t = (c[k] for k in ("rng", "n", "H", "V", "Vp", "inv_t"))
+    say(f"linear sweep seed={seed}: n={n} H={H} V={V}/{Vp} inv_t={inv_t:.4g}")
+    h, W, y = make(n, H, V, Vp, seed=3000 + seed, scale=2.0, pad_value=float("nan"))
+    res, got = check(h, W, y, V, Vp, inv_t=inv_t)
+    ref = linear.linear_logp_forward(h, W, y, V, Vp, inv_temperature=inv_t, balance=False)
+    torch.cuda.synchronize()
+    assert all(same_bits(u, w) for u, w in zip(got, ref))
+
+    L = dst.logp_num_tiles(Vp)
+    layout = random_layout(rng, L) if L > 1 else [1]
+    partials = torch.full((n, L, 3), float("nan"), dtype=torch.float32, device=DEV)
+    c0 = 0
+    for tiles in layout:
+        c1 = min(Vp, c0 + tiles * T)
+        linear.linear_logp_partials(h, W[c0:c1], y, V, Vp, c0, c1, partials,
+                                    inv_temperature=inv_t)
+        c0 = c1
+    merged = dst.logp_merge(partials, y, V)
+    assert all(same_bits(u, w) for u, w in zip(got, merged)), layout
+
+    g, _, dh, dW, _ = bwd_run(h, W, y, V, Vp, inv_t=inv_t, chunk=T, seed=seed)
+    bref = bwd_reference(h, W, y, g, V, inv_t=inv_t)
+    bres = check_bwd(h, W, y, g, dh, dW, V, bref)
+    say(f"seed={seed}: {res} {bres}")
