@@ -15,7 +15,9 @@ test_gpu_linear.py):
     and the backward of a random column range bitwise equal to that range of the full one;
   - linear_logp's forward against the oracle on every row, the balanced launch bitwise equal
     to the one-kernel launch, a random shard layout merged back bitwise, and the backward's
-    dh and dW against the oracle.
+    dh and dW against the oracle;
+  - the GRPO loss (random sequences, lengths, row strides, reductions, clip bounds, KL weight,
+    ratio spread, masks with empty sequences, global normalizers) against its oracle.
 """
 
 from __future__ import annotations
@@ -26,7 +28,9 @@ import torch
 
 import deterministic_selected_token_amd as dst
 from deterministic_selected_token_amd import linear
+from deterministic_selected_token_amd import grpo
 from test_gpu_dtypes import case_in, check_ex, same_bits
+from test_gpu_grpo import check_against_oracle, make_batch
 from test_gpu_linear import bwd_reference, bwd_run, check, check_bwd, make
 
 pytestmark = pytest.mark.gpu
@@ -136,3 +140,31 @@ def test_linear_random_case(seed):
     bref = bwd_reference(h, W, y, g, V, inv_t=inv_t)
     bres = check_bwd(h, W, y, g, dh, dW, V, bref)
     say(f"seed={seed}: {res} {bres}")
+
+
+def grpo_config(seed: int) -> dict:
+    rng = np.random.default_rng(4000 + seed)
+    n = int(rng.integers(1, 65))
+    T_ = int(rng.choice([1, 255, 256, 257, 4096])) if rng.random() < 0.3 \
+        else int(rng.integers(1, 5000))
+    return dict(n=n, T=T_, ld=T_ + (0 if rng.random() < 0.5 else int(rng.integers(1, 40))),
+                mode=list(grpo.MODES)[seed % 3], beta=float(rng.choice([0.0, 0.04, 0.3])),
+                use_ref=bool(rng.random() < 0.7), use_mask=bool(rng.random() < 0.7),
+                eps_low=float(rng.choice([0.1, 0.2])), eps_high=float(rng.choice([0.2, 0.28])),
+                spread=float(rng.choice([0.05, 0.3, 2.0])),
+                empty=tuple(int(r) for r in rng.choice(n, size=min(n, 2), replace=False))
+                if rng.random() < 0.4 else (),
+                norm_tokens=int(rng.choice([0, 0, 10000])), norm_seqs=int(rng.choice([0, 0, 96])))
+
+
+@pytest.mark.parametrize("seed", range(18))
+def test_grpo_random_case(seed):
+    c = grpo_config(seed)
+    say(f"grpo sweep seed={seed}: {c}")
+    b = make_batch(c["n"], c["T"], seed=5000 + seed, spread=c["spread"], ld=c["ld"],
+                   empty_rows=c["empty"] if c["use_mask"] else ())
+    L, o = check_against_oracle(b, c["T"], c["mode"], c["beta"], eps_low=c["eps_low"],
+                                eps_high=c["eps_high"], use_ref=c["use_ref"],
+                                use_mask=c["use_mask"], norm_tokens=c["norm_tokens"],
+                                norm_seqs=c["norm_seqs"])
+    say(f"seed={seed}: loss {L['loss']:.6g} vs {o['loss']:.6g}")
