@@ -65,6 +65,28 @@ struct TokenTerms {
     bool clipped;
 };
 
+// The KL estimator exp(d) - d - 1.  expm1(d) - d cancels when |d| is small (the result is
+// about d^2 / 2 while expm1(d) carries an error of about 2^-23 |d|), so for |d| < 1 it is
+// formed as d^2 times the Taylor series of (e^d - 1 - d) / d^2 = sum_k d^(k-2) / k!,
+// k = 2..13 (the first omitted term is below 2^-31 of the sum there), by Horner's rule with
+// fused multiply-adds; for |d| >= 1, as expm1(d) - d, which then loses under 2 bits.
+__device__ __forceinline__ float kl_estimator(float d, float em) {
+    if (!(fabsf(d) < 1.0f)) return em - d;
+    float p = 1.0f / 6227020800.0f;                // 1/13!
+    p = __builtin_fmaf(p, d, 1.0f / 479001600.0f);  // 1/12!
+    p = __builtin_fmaf(p, d, 1.0f / 39916800.0f);   // 1/11!
+    p = __builtin_fmaf(p, d, 1.0f / 3628800.0f);    // 1/10!
+    p = __builtin_fmaf(p, d, 1.0f / 362880.0f);     // 1/9!
+    p = __builtin_fmaf(p, d, 1.0f / 40320.0f);      // 1/8!
+    p = __builtin_fmaf(p, d, 1.0f / 5040.0f);       // 1/7!
+    p = __builtin_fmaf(p, d, 1.0f / 720.0f);        // 1/6!
+    p = __builtin_fmaf(p, d, 1.0f / 120.0f);        // 1/5!
+    p = __builtin_fmaf(p, d, 1.0f / 24.0f);         // 1/4!
+    p = __builtin_fmaf(p, d, 1.0f / 6.0f);          // 1/3!
+    p = __builtin_fmaf(p, d, 0.5f);                 // 1/2!
+    return (d * d) * p;
+}
+
 // The GRPO terms of one active token (see include/grpo_loss.h for the definitions).
 __device__ __forceinline__ TokenTerms grpo_token(float lp, float old, float ref, bool has_ref,
                                                  float A, const Objective& o) {
@@ -77,7 +99,7 @@ __device__ __forceinline__ TokenTerms grpo_token(float lp, float old, float ref,
     if (has_ref) {
         const float e = ref - lp;
         const float em = expm1f(e);
-        t.kl = em - e;
+        t.kl = kl_estimator(e, em);
         t.dl = dpg + o.beta * (-em);
     } else {
         t.kl = 0.0f;

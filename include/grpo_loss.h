@@ -14,7 +14,8 @@
  *   lo, hi = fl32(1 - eps_low), fl32(1 + eps_high)      (clip bounds)
  *   clipped = (A_i > 0 and r > hi) or (A_i < 0 and r < lo)
  *   pg     = -A_i * (clipped ? (A_i > 0 ? hi : lo) : r)  = max(-A r, -A clip(r, lo, hi))
- *   kl     = expm1(ref - logp) - (ref - logp)          (= exp(d) - d - 1, d = ref - logp)
+ *   kl     = exp(d) - d - 1, d = ref - logp: for |d| < 1 as d^2 times the Taylor series
+ *            of (e^d - 1 - d) / d^2 through d^11 / 13! (no cancellation), else expm1(d) - d
  *   d pg / d logp = clipped ? 0 : -A_i r ;  d kl / d logp = -expm1(ref - logp)
  * Inactive tokens (mask == 0) and A_i == 0 tokens add nothing to pg; inactive tokens get a
  * zero gradient.  Reductions:

@@ -6,10 +6,8 @@ Tolerances (float32 kernels against the float64 oracle):
     bound may take either branch (a last-bit difference in exp moves them across), so for
     them either branch's gradient is accepted.
   * sums (per-sequence pg_sum / kl_sum, the reduced losses): 4e-6 of the sum of absolute
-    terms, plus 1e-30 (float32 sums of up to a few thousand terms, each within ~2^-21).  The
-    KL term expm1(d) - d, d = ref - logp, cancels in float32 when |d| is small (it is about
-    d^2 / 2 while the error of expm1(d) is about 2^-23 |d|), so the KL sums also allow
-    2^-21 (|expm1(d)| + |d|) per active token.
+    terms, plus 1e-30 (float32 sums of up to a few thousand terms, each within ~2^-21; the
+    KL term is formed without cancellation for small |d|, so this holds for it too).
   * token counts exact; clipped counts within the number of ambiguous tokens; clip_frac
     within that count over the tokens plus its own float32 rounding (2^-24 of its value).
 """
@@ -80,12 +78,7 @@ def check_against_oracle(b, T, mode, beta, eps_low=0.2, eps_high=0.28, use_ref=T
     kl_abs = np.abs(t["kl"]).sum(1)
     assert np.all(np.abs(S["pg_sum"] - o["seq_pg_sum"]) <= 4e-6 * pg_abs + 1e-30 +
                   (amb * np.abs(t["pg"])).sum(1) * 1e-6)
-    if use_ref:
-        d_abs = np.abs(host(b["ref"], T).astype(np.float64) - host(b["lp"], T))
-        kl_cancel = np.where(t["active"], np.abs(t["dkl"]) + d_abs, 0.0).sum(1)
-    else:
-        kl_cancel = np.zeros_like(kl_abs)
-    kl_bound = 4e-6 * kl_abs + 2.0 ** -21 * kl_cancel
+    kl_bound = 4e-6 * kl_abs
     assert np.all(np.abs(S["kl_sum"] - o["seq_kl_sum"]) <= kl_bound + 1e-30)
     # reduced losses
     n_i = np.maximum(o["seq_tokens"], 1)
@@ -154,6 +147,35 @@ def test_grpo_large_ratios_and_clip_edges():
     for mode in grpo.MODES:
         L, o = check_against_oracle(b, 2000, mode, 0.04)
         assert 0.3 < o["clip_frac"] < 0.9
+
+
+def test_kl_term_small_differences():
+    """One token per sequence with ref - logp = d from 0.49 down to 1e-7: each sequence's KL
+    sum is the token's exp(d) - d - 1 to within 4 float32 units relative (expm1(d) - d in
+    float32 would be off by about 2^-23 / |d| relative: 1e-2 at d = 1e-5).  The oracle's
+    float64 expm1(d) - d is itself within 2^-52 / |d| relative, 2e-9 at the smallest d."""
+    from oracle import grpo_oracle as O
+    d = np.array([0.49, -0.49, 0.1, -0.1, 1e-2, -1e-2, 1e-3, -1e-3, 1e-5, -1e-5, 1e-7, -1e-7,
+                  0.7, -0.7, 3.0, 0.0], dtype=np.float32)
+    n = d.size
+    lp = np.full((n, 1), -2.0, dtype=np.float32)
+    ref = (lp + d[:, None]).astype(np.float32)
+    e = ref.astype(np.float64) - lp  # exact: the float32 difference the kernel forms
+    adv = np.linspace(-1.0, 1.0, n).astype(np.float32)
+    t = {k: torch.from_numpy(v).to(DEV) for k, v in dict(lp=lp, ref=ref, adv=adv).items()}
+    say("KL term at small ref - logp")
+    _, st, _ = grpo.grpo_loss(t["lp"], t["lp"], t["adv"], ref_logp=t["ref"],
+                              mode="seq_sum_token_mean", beta=0.1)
+    torch.cuda.synchronize()
+    got = grpo.partial_fields(st)["kl_sum"].cpu().numpy().astype(np.float64)
+    o = O.loss(lp, lp, ref, adv, None, mode="seq_sum_token_mean", beta=0.1)
+    want = o["seq_kl_sum"]
+    assert np.allclose(want, np.expm1(e[:, 0]) - e[:, 0], rtol=0, atol=0)
+    rel = np.abs(got - want) / np.where(want > 0, want, 1.0)
+    assert got[-1] == 0.0 and np.all(got >= 0)
+    assert np.all(rel <= 4 * 2.0 ** -24 + 2.0 ** -52 / np.maximum(np.abs(e[:, 0]), 1e-300)), \
+        list(zip(d.tolist(), rel.tolist()))
+    say(f"KL relative errors: max {rel.max():.3e}")
 
 
 def expected_identity_grad(adv, mask, mode):
