@@ -4,8 +4,8 @@ the FP64 oracle and the bitwise contract.
 Every case draws its configuration from its own seed (numpy PCG64): for the logp path the
 logits dtype (BF16, FP16, FP32), rows, real and padded vocabulary (with a share of tile-edge
 widths), the row stride, the temperature, the logit scale and the shares of ignored, bad and
-inactive targets; for linear_logp the rows, hidden size, real and padded vocabulary and
-temperature.  Checks, with the tolerances of the dedicated tests (test_gpu_dtypes.py,
+inactive targets; for linear_logp the rows, hidden size, real and padded vocabulary,
+temperature, logit scale and share of inactive rows.  Checks, with the tolerances of the dedicated tests (test_gpu_dtypes.py,
 test_gpu_linear.py):
   - logp forward and backward against the oracle on every row (the correctly-rounded share
     of dlogits counted over the non-target entries: at V = 7 and scores of spread 20 a
@@ -110,17 +110,24 @@ def linear_config(seed: int) -> dict:
     Vp = V + (0 if rng.random() < 0.5 else int(rng.integers(1, 2 * T)))
     return dict(rng=rng, n=int(rng.integers(1, 300)),
                 H=int(8 * rng.integers(1, 80)), V=V, Vp=Vp,
-                inv_t=float(rng.choice([1.0, 1 / 0.7, 2.0])))
+                inv_t=float(rng.choice([1.0, 1 / 0.7, 2.0])),
+                scale=float(rng.choice([0.5, 2.0, 10.0, 40.0])),
+                inactive=float(rng.choice([0.0, 0.0, 0.3])))
 
 
 @pytest.mark.parametrize("seed", range(16))
 def test_linear_random_case(seed):
     c = linear_config(seed)
     rng, n, H, V, Vp, inv_t = (c[k] for k in ("rng", "n", "H", "V", "Vp", "inv_t"))
-    say(f"linear sweep seed={seed}: n={n} H={H} V={V}/{Vp} inv_t={inv_t:.4g}")
-    h, W, y = make(n, H, V, Vp, seed=3000 + seed, scale=2.0, pad_value=float("nan"))
-    res, got = check(h, W, y, V, Vp, inv_t=inv_t)
-    ref = linear.linear_logp_forward(h, W, y, V, Vp, inv_temperature=inv_t, balance=False)
+    say(f"linear sweep seed={seed}: n={n} H={H} V={V}/{Vp} inv_t={inv_t:.4g} "
+        f"scale={c['scale']} inactive={c['inactive']}")
+    h, W, y = make(n, H, V, Vp, seed=3000 + seed, scale=c["scale"], pad_value=float("nan"))
+    active = None
+    if c["inactive"] > 0:
+        active = torch.from_numpy((rng.random(n) >= c["inactive"]).astype(np.uint8)).to(DEV)
+    res, got = check(h, W, y, V, Vp, active=active, inv_t=inv_t)
+    ref = linear.linear_logp_forward(h, W, y, V, Vp, active=active, inv_temperature=inv_t,
+                                     balance=False)
     torch.cuda.synchronize()
     assert all(same_bits(u, w) for u, w in zip(got, ref))
 
@@ -130,15 +137,17 @@ def test_linear_random_case(seed):
     c0 = 0
     for tiles in layout:
         c1 = min(Vp, c0 + tiles * T)
-        linear.linear_logp_partials(h, W[c0:c1], y, V, Vp, c0, c1, partials,
+        linear.linear_logp_partials(h, W[c0:c1], y, V, Vp, c0, c1, partials, active=active,
                                     inv_temperature=inv_t)
         c0 = c1
-    merged = dst.logp_merge(partials, y, V)
+    merged = dst.logp_merge(partials, y, V, active=active)
     assert all(same_bits(u, w) for u, w in zip(got, merged)), layout
 
-    g, _, dh, dW, _ = bwd_run(h, W, y, V, Vp, inv_t=inv_t, chunk=T, seed=seed)
-    bref = bwd_reference(h, W, y, g, V, inv_t=inv_t)
+    g, _, dh, dW, _ = bwd_run(h, W, y, V, Vp, active=active, inv_t=inv_t, chunk=T, seed=seed)
+    bref = bwd_reference(h, W, y, g, V, active=active, inv_t=inv_t)
     bres = check_bwd(h, W, y, g, dh, dW, V, bref)
+    if active is not None:
+        assert torch.all(dh[active == 0] == 0)
     say(f"seed={seed}: {res} {bres}")
 
 
