@@ -225,6 +225,34 @@ def test_run_to_run_bitwise():
             assert torch.equal(u, w)
 
 
+def test_side_stream_is_bitwise():
+    """The loss's kernels (counts, normalizer, per-sequence pass, reduce) all run on the stream
+    they are given: a side stream reproduces the default stream's bits while the default
+    stream is kept busy."""
+    b = make_batch(40, 3000, seed=41, empty_rows=(3,))
+    say("grpo on a side stream")
+
+    def run():
+        loss, st, d = grpo.grpo_loss(b["lp"], b["old"], b["adv"], ref_logp=b["ref"],
+                                     mask=b["mask"], mode="seq_mean", beta=0.04)
+        return loss, st, d
+
+    ref = run()
+    torch.cuda.synchronize()
+    busy = torch.randn((4096, 4096), device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for _ in range(8):
+        busy = torch.tanh(busy @ busy.t() * 1e-3)  # keeps the default stream occupied
+    with torch.cuda.stream(s):
+        got = run()
+    s.synchronize()
+    torch.cuda.synchronize()
+    for u, w in zip(ref, got):
+        assert torch.equal(u.contiguous().view(torch.int32) if u.dtype == torch.float32 else u,
+                           w.contiguous().view(torch.int32) if w.dtype == torch.float32 else w)
+
+
 @pytest.mark.parametrize("mode", list(grpo.MODES))
 def test_data_parallel_split_is_bitwise(mode):
     """Sequences split over 'ranks' with the global normalizers: the concatenated per-sequence

@@ -586,3 +586,36 @@ def test_linear_balanced_partials_are_bitwise(n, H, V, Vp, view, inv_t):
         torch.cuda.synchronize()
         for u, v in zip(a, b):
             assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
+def test_linear_side_stream_is_bitwise():
+    """Every kernel of a call runs on the stream it is given: the balanced forward (per-tile,
+    split and fold kernels) and the FP32 and BF16 backward (transposes, dz, products) give
+    the default stream's bits on a side stream while the default stream is kept busy."""
+    n, H, V, Vp = 700, 256, 30000, 32768
+    h, W, y = make(n, H, V, Vp, seed=77, scale=2.0)
+    g = (torch.randn(n, generator=torch.Generator().manual_seed(78)) * 0.5).to(DEV)
+    say("linear_logp on a side stream")
+
+    def run():
+        lp, ls, st = linear.linear_logp_forward(h, W, y, V, Vp, inv_temperature=1 / 0.7)
+        d32 = linear.linear_logp_backward(h, W, y, g, st, V, Vp, inv_temperature=1 / 0.7,
+                                          chunk_cols=2 * T)
+        d16 = linear.linear_logp_backward(h, W, y, g, st, V, Vp, inv_temperature=1 / 0.7,
+                                          chunk_cols=2 * T, out_dtype=torch.bfloat16)
+        return (lp, ls, st) + tuple(d32) + tuple(d16)
+
+    ref = run()
+    torch.cuda.synchronize()
+    busy = torch.randn((4096, 4096), device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for _ in range(8):
+        busy = torch.tanh(busy @ busy.t() * 1e-3)  # keeps the default stream occupied
+    with torch.cuda.stream(s):
+        got = run()
+    s.synchronize()
+    torch.cuda.synchronize()
+    for u, w in zip(ref, got):
+        view = {4: torch.int32, 2: torch.int16}[u.element_size()]
+        assert torch.equal(u.contiguous().view(view), w.contiguous().view(view))
