@@ -19,7 +19,9 @@ Also in the default run, each under config: batch invariance of headline rows re
 smaller batches; one tensor-parallel rank's share (5 of 38 tiles of the headline rows);
 the mid-size workload (N=4096, padded vocabulary, 5% inactive rows); the vocab-shard
 workload (N=8192, 39 tiles, 1/2/4 shards + merge against the fused forward); N=131072; and
-the headline shape on the pages' bench inputs (sigma 1, g = 1).  The oracle leg runs the
+the headline shape on the pages' bench inputs (sigma 1, g = 1); and linear_logp (forward and
+BF16 backward at 8192 x 4096 x 151936, against the matrix-core ceiling measured in the same
+run).  The oracle leg runs the
 FP64 oracle on the headline rows and on the pages' inputs, compares the GPU's logp, LSE
 and dlogits with it block by block (top-level "accuracy") and reports its own rate
 ("cpu_baseline").
@@ -899,6 +901,27 @@ def time_linear_backward(dst, stream, steps: int, n: int = 8192, hidden: int = 4
     return out
 
 
+def time_linear_default(dst, stream) -> dict:
+    """The default run's linear_logp entry: the forward with its balancing workspace and the
+    BF16-output backward at 8192 x 4096 x 151936, each as TFLOP/s and as a fraction of the
+    dense BF16 matrix-core ceiling measured in the same run (no oracle leg; --variants has the
+    full set)."""
+    import torch
+
+    fwd = time_linear(dst, stream, 3, cpu_baseline=False)
+    bwd = time_linear_backward(dst, stream, 2, out_dtype=torch.bfloat16, cpu_baseline=False)
+    mc = mfma_ceiling(stream, reps=3)
+    return {"workload": "h [8192, 4096] x W [151936, 4096] BF16, unit temperature",
+            "forward": {"ms": fwd["partials_ms"], "merge_ms": fwd["merge_ms"],
+                        "tflops": fwd["tflops"], "frac_of_bf16_peak": fwd["frac_of_bf16_peak"],
+                        "frac_of_measured_mfma_ceiling": round(fwd["tflops"] / mc["tflops"], 4)},
+            "backward_bf16_out": {"ms": bwd["ms"], "tflops": bwd["tflops"],
+                                  "frac_of_bf16_peak": bwd["frac_of_bf16_peak"],
+                                  "frac_of_measured_mfma_ceiling": round(
+                                      bwd["tflops"] / mc["tflops"], 4)},
+            "mfma_bf16_ceiling_tflops": mc["tflops"]}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1055,6 +1078,9 @@ def main() -> int:
                                      "dlogits over the sampled rows' N x V elements"}
             cpu = cpu_baseline(leg, case, threads)
         del pages, pages_out
+        torch.cuda.empty_cache()
+        print("bench: linear_logp (matrix cores)", file=sys.stderr, flush=True)
+        extra["linear_logp"] = time_linear_default(dst, stream)
         torch.cuda.empty_cache()
     if args.variants:
         extra["variants"] = time_variants(dst, case, stream, args.steps)
