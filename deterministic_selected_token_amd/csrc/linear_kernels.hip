@@ -655,15 +655,16 @@ __global__ __launch_bounds__(kThreads) void linear_dz_kernel(
     }
 }
 
-// Where gemm_tn_kernel's FP32 block results go.  The BF16 forms round to nearest even once,
-// after the FP32 value is complete; kOutAddBf16 forms that value exactly as kOutAddF32 does
-// (one FP32 add of the stored partial sum and the block's result), so its bits are the
+// Where gemm_tn_kernel's FP32 block results go.  The accumulating forms start the accumulator
+// from the stored partial sum, so a chunk's products are added onto it one MFMA k-step at a
+// time, in k order.  The BF16 forms round to nearest even once, after the FP32 value is
+// complete; kOutAddBf16 forms that value exactly as kOutAddF32 does, so its bits are the
 // rounding of what the FP32 forms would have stored.
 enum GemmOut : int {
-    kOutF32 = 0,     // c32 = acc
-    kOutAddF32 = 1,  // c32 = c32 + acc
-    kOutBf16 = 2,    // c16 = RNE_bf16(acc)
-    kOutAddBf16 = 3, // c16 = RNE_bf16(c32 + acc); c32 is read, not written
+    kOutF32 = 0,     // c32 = a b^T
+    kOutAddF32 = 1,  // c32 = (c32 + a b^T), the products added onto c32 in k order
+    kOutBf16 = 2,    // c16 = RNE_bf16(a b^T)
+    kOutAddBf16 = 3, // c16 = RNE_bf16(c32 + a b^T) as kOutAddF32 forms it; c32 is not written
 };
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
@@ -685,12 +686,23 @@ __global__ __launch_bounds__(kThreads) void gemm_tn_kernel(
     const int lane = lane_id(), wave = wave_id();
     const int wm = wave / kWN, wn = wave % kWN;
     f32x16 acc[kTM][kTN];
+    // the accumulating forms start from the stored partial sum (its loads overlap the first
+    // stages' loads), the others from zero
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kTN; ++j)
+        for (int j = 0; j < kTN; ++j) {
+            const int64_t col = col0 + wn * (kTN * 32) + j * 32 + (lane & 31);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row =
+                    row0 + wm * (kTM * 32) + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+                float c = 0.0f;
+                if constexpr (OUT == kOutAddF32 || OUT == kOutAddBf16)
+                    if (row < m_real && col < n_real) c = c32[row * ld32 + col];
+                acc[i][j][r] = c;
+            }
+        }
     block_product(sm, a + row0 * lda, static_cast<uint32_t>(lda), kBM, b + col0 * ldb,
                   static_cast<uint32_t>(ldb), kBN, K, 0, K / kBK, wm, wn, lane, acc);
 #pragma unroll
@@ -707,12 +719,11 @@ __global__ __launch_bounds__(kThreads) void gemm_tn_kernel(
                     if constexpr (OUT == kOutF32) {
                         c32[row * ld32 + col] = v;
                     } else if constexpr (OUT == kOutAddF32) {
-                        float* p = c32 + row * ld32 + col;
-                        *p = *p + v;
+                        c32[row * ld32 + col] = v;
                     } else if constexpr (OUT == kOutBf16) {
                         c16[row * ld16 + col] = bf16_bits(v);
                     } else {
-                        c16[row * ld16 + col] = bf16_bits(c32[row * ld32 + col] + v);
+                        c16[row * ld16 + col] = bf16_bits(v);
                     }
                 }
             }

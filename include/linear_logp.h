@@ -130,10 +130,10 @@ LOGP_API logp_status_t linear_logp_partials_ws(float inv_temperature, const uint
  *   dhidden[t, :] = sum over this shard's columns v of dz[t, v] W[v, :]   (FP32, overwritten);
  *   dweight[v - col_begin, :] = sum over rows t of dz[t, v] h[t, :]      (FP32, overwritten;
  *     rows of padding columns are 0).
- * Both sums run on the matrix cores with FP32 accumulation in a fixed order: dhidden adds the
- * chunks of chunk_cols columns in column order, each a fixed-order product over its columns, so
- * a row's dhidden does not depend on the other rows of the batch; dweight sums the rows in
- * index order.  Vocab-parallel ranks each produce their shard's dhidden; the caller adds them
+ * Both sums run on the matrix cores with FP32 accumulation in a fixed order: dhidden's
+ * accumulator runs through the chunks of chunk_cols columns in column order, each chunk's
+ * products added onto it in column order, so a row's dhidden does not depend on the other rows
+ * of the batch; dweight sums the rows in index order.  Vocab-parallel ranks each produce their shard's dhidden; the caller adds them
  * in a fixed rank order.  Run to run the results are bitwise identical.
  *   hidden, weight, targets, active, ignore_index, vocab_real, vocab_padded, col_begin,
  *   col_end, inv_temperature   as in linear_logp_partials_ex (weight points at row col_begin).
