@@ -37,6 +37,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 T = dst.TILE_COLS
 EDGE_WIDTHS = [1, 7, T - 1, T, T + 1, 2 * T, 3 * T - 8, 5 * T + 3]
+SMALL_SAMPLE = 20000  # dlogits entries below which 2 misrounded ones are allowed
 
 
 def say(msg: str):
@@ -76,6 +77,13 @@ def test_logp_random_case(seed):
                    ignore_frac=c["ignore"], bad_target_frac=c["bad"],
                    inactive_frac=c["inactive"])
     ulps, min_cr = (16.0, 0.0) if dtype == "f32" else (1.0, None)
+    if dtype != "f32" and n * vr < SMALL_SAMPLE:
+        # the correctly-rounded bar is a population share: a sample this small may hold a
+        # rare misrounded entry (per entry at most 2^-13 for BF16, 2^-10 for FP16, from the
+        # ~4 FP32 units of the value rounded), so up to 2 are allowed; every entry is still
+        # held to one spacing of its dtype
+        bar = {"bf16": 0.9999, "f16": 1.0 - 2.0 ** -10}[dtype]
+        min_cr = min(bar, 1.0 - 2.0 / (n * vr))
     (logp, lse, stats, d), fwd, bwd = check_ex(case, inv_t=inv_t, ulps=ulps, min_cr=min_cr,
                                                cr_skip_targets=True)
     say(f"seed={seed}: {fwd} {bwd}")
