@@ -14,8 +14,10 @@
 //   partials kernel one wave per (sequence, tile) of a token range: the same tile code,
 //                   written out (context-parallel shards).
 //   merge kernel    one wave per sequence over its tile partials: the same merge code.
-//   count / norm    active tokens per sequence, then the batch normalizer (only needed when a
-//                   mask makes them unknown on the host).
+//   count / norm    active tokens per sequence, then the batch normalizer, each launched only
+//                   when a mask makes them unknown on the host and the reduction needs them
+//                   before the pass (n_i for seq_mean and seq_sum_token_mean, the sums for a
+//                   local normalizer).
 //   reduce kernel   one workgroup over the batch's sequences: the same merge order again.
 //   advantages      one wave per reward group.
 #include <hip/hip_runtime.h>
@@ -221,18 +223,19 @@ struct RowPartials {
 
 // ----------------------------------------------------------------------------- kernels
 
-// One workgroup per sequence.  `counts` (stride 4 ints = one grpo_partial_t) holds n_i when
-// `counted`; otherwise every sequence has tk.width active tokens.  The normalizer D is
-// `norm_dev[0]` when given (computed on the device from the counts), else `norm_host`.
+// One workgroup per sequence.  With `counted`, seq_stats[].tokens holds each sequence's
+// active-token count n_i (the count kernel's); otherwise every sequence has tk.width active
+// tokens, or the reduction does not use n_i.  The normalizer D is `norm_dev[0]` when given
+// (formed on the device from the counts), else `norm_host`.
 __global__ __launch_bounds__(kSeqMaxWaves* kWave) void grpo_seq_kernel(
-    Tokens tk, Objective o, const int64_t* norm_dev, int64_t norm_host,
+    Tokens tk, Objective o, int counted, const int64_t* norm_dev, int64_t norm_host,
     grpo_partial_t* __restrict__ seq_stats, float* dlogp) {
     extern __shared__ grpo_partial_t slots[];  // one slot per tile of the sequence
     const int64_t row = blockIdx.x;
     const int lane = lane_id(), wave = wave_id();
     const int waves = static_cast<int>(blockDim.x) / kWave;
     const float A = tk.adv[row];
-    const int64_t n_i = norm_dev != nullptr ? seq_stats[row].tokens : tk.width;
+    const int64_t n_i = counted ? seq_stats[row].tokens : tk.width;
     const int64_t D = norm_dev != nullptr ? norm_dev[0] : norm_host;
     const float scale = grpo_scale(o.mode, n_i, D);
     const int tiles = (tk.width + kTokTile - 1) / kTokTile;
@@ -570,10 +573,16 @@ logp_status_t grpo_loss(const float* logp, const float* old_logp, const float* r
     int32_t mode = params->mode;
     float beta = o.beta;
     if (n_seqs > 0) {
+        // Launched only as the reduction needs them before the pass: the counts (a mask makes
+        // them unknown on the host) for n_i (seq_mean, seq_sum_token_mean) or a local
+        // normalizer; the normalizer kernel only for a local normalizer.  token_mean with a
+        // given normalizer needs neither: its counts come out of the pass itself.
+        const bool local_norm = (mode == GRPO_TOKEN_MEAN && nt <= 0) ||
+                                (mode == GRPO_SEQ_MEAN && ns <= 0);
+        int counted = mask != nullptr && (mode != GRPO_TOKEN_MEAN || nt <= 0) ? 1 : 0;
         const int64_t* norm_dev = nullptr;
-        int64_t norm_host = 0;
-        if (mask != nullptr) {
-            // active counts first (into seq_stats[].tokens), then the normalizer on the device
+        int64_t norm_host = grpo_norm(mode, nt, ns, n_seqs * seq_len, seq_len > 0 ? n_seqs : 0);
+        if (counted) {
             const uint8_t* m = mask;
             int width = static_cast<int>(seq_len);
             int32_t* counts = &seq_stats[0].tokens;
@@ -582,15 +591,15 @@ logp_status_t grpo_loss(const float* logp, const float* old_logp, const float* r
             st = launch(count_kernel(m, ld), dim3(static_cast<uint32_t>(n_seqs)),
                         dim3(kCountThreads), ca, 0, stream);
             if (st != LOGP_OK) return st;
-            void* na[] = {&seq_stats, &n_seqs, &mode, &nt, &ns, &loss};
-            st = launch(reinterpret_cast<const void*>(&grpo_norm_kernel), dim3(1),
-                        dim3(kCountThreads), na, 0, stream);
-            if (st != LOGP_OK) return st;
-            norm_dev = &loss->norm;
-        } else {
-            norm_host = grpo_norm(mode, nt, ns, n_seqs * seq_len, seq_len > 0 ? n_seqs : 0);
+            if (local_norm) {
+                void* na[] = {&seq_stats, &n_seqs, &mode, &nt, &ns, &loss};
+                st = launch(reinterpret_cast<const void*>(&grpo_norm_kernel), dim3(1),
+                            dim3(kCountThreads), na, 0, stream);
+                if (st != LOGP_OK) return st;
+                norm_dev = &loss->norm;
+            }
         }
-        void* sa[] = {&tk, &o, &norm_dev, &norm_host, &seq_stats, &dlogp};
+        void* sa[] = {&tk, &o, &counted, &norm_dev, &norm_host, &seq_stats, &dlogp};
         const int64_t tiles = ceil_div(seq_len, kTokTile);
         const size_t lds = static_cast<size_t>(tiles) * sizeof(grpo_partial_t);
         const int waves = static_cast<int>(std::min<int64_t>(kSeqMaxWaves, std::max<int64_t>(1,
