@@ -27,7 +27,7 @@ and dlogits with it block by block (top-level "accuracy") and reports its own ra
 ("cpu_baseline").
 
 Extra flags: --headline-only (the timed headline step alone), --variants (FP16, FP32,
-temperature, GRPO, linear_logp), --profile-copy (a 4 GiB copy of known size at the end, for
+temperature, GRPO, linear_logp, the matrix-core and LDS probes), --profile-copy (a 4 GiB copy of known size at the end, for
 scaling the hardware byte counters).
 """
 
@@ -113,6 +113,7 @@ CEILING_LIB = os.path.join(ROOT, "tests", "probes", "libhbm_ceiling.so")
 READ_SHAPES = ((2, 4), (4, 8), (8, 4), (16, 4), (16, 16), (32, 8))
 COPY_SHAPES = ((8, 16), (16, 16), (16, 8), (32, 8))
 MFMA_CEILING_LIB = os.path.join(ROOT, "tests", "probes", "libmfma_ceiling.so")
+LDS_CEILING_LIB = os.path.join(ROOT, "tests", "probes", "liblds_ceiling.so")
 
 
 def load_ceiling_library():
@@ -219,6 +220,63 @@ def mfma_ceiling(stream, reps: int = 5) -> dict:
                       f"per wave, {'switching' if toggle else 'fixed'} operands"] = round(tf, 1)
         key = "tflops" if toggle else "static_operands_tflops"
         out[key] = max(out[key], round(tf, 1))
+    return out
+
+
+def lds_rates(stream, groups: int = 256) -> dict:
+    """Per-CU LDS rates in bytes per core clock (tests/probes/lds_ceiling.hip; one workgroup
+    per CU, cycles read in the kernel with s_memtime, median over the workgroups): LDS reads of
+    4, 8 and 16 bytes per lane (the block product's fragment reads are 16-byte), and
+    direct-to-LDS buffer loads from a 2 MiB source that stays in L2 (the block product's stage
+    loads), with a workgroup on every CU and on one CU in eight (the L2 of each XCD is shared by
+    its CUs)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(LDS_CEILING_LIB)  # built by __graft_entry__.build() with the probes
+    lib.lds_read.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lds_read.restype = ctypes.c_int
+    lib.lds_dma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lds_dma.restype = ctypes.c_int
+    lib.lds_read_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.lds_read_bytes.restype = ctypes.c_double
+    lib.lds_dma_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.lds_dma_bytes.restype = ctypes.c_double
+    dev = torch.device("cuda", 0)
+    sink = torch.empty(groups * 16 * 64, dtype=torch.int32, device=dev)
+    cycles = torch.empty(groups, dtype=torch.int64, device=dev)
+    src = torch.randint(0, 256, (2 << 20,), dtype=torch.uint8, device=dev)
+    out = {"kernels": "tests/probes/lds_ceiling.hip (lds_read, lds_dma)",
+           "unit": "bytes per core clock per CU", "read": {}, "dma_from_l2": {}}
+
+    def median_rate(call, nbytes, g=groups):
+        for _ in range(2):  # the second launch is the one read
+            if call():
+                raise RuntimeError("lds probe failed")
+        torch.cuda.synchronize()
+        return round(nbytes / float(cycles[:g].double().median().item()), 1)
+
+    for width in (4, 8, 16):
+        for waves in (4, 8, 16):
+            iters = 16000 // waves
+            rate = median_rate(
+                lambda: lib.lds_read(waves, groups, iters, width, sink.data_ptr(),
+                                     cycles.data_ptr(), stream.cuda_stream),
+                lib.lds_read_bytes(waves, iters, width))
+            out["read"][f"{width}-byte reads, {waves} waves"] = rate
+    for g in (groups, groups // 8):  # every CU loading, or one in eight
+        for waves in (4, 8):
+            iters = 4000 // waves
+
+            def call():
+                return lib.lds_dma(waves, g, iters, src.data_ptr(), src.numel(),
+                                   sink.data_ptr(), cycles.data_ptr(), stream.cuda_stream)
+
+            rate = median_rate(call, lib.lds_dma_bytes(waves, iters), g)
+            out["dma_from_l2"][f"{waves} waves, {g} workgroups"] = rate
     return out
 
 
@@ -1097,6 +1155,7 @@ def main() -> int:
         mc = mfma_ceiling(stream)
         extra["variants"]["mfma_bf16_ceiling"] = mc
         extra["variants"]["vendor_gemm_reference"] = vendor_gemm_reference(stream)
+        extra["variants"]["lds_rates"] = lds_rates(stream)
         for key in ("linear_logp_fwd", "linear_logp_fwd_temperature_0.7", "linear_logp_bwd",
                     "linear_logp_bwd_bf16_out"):
             v = extra["variants"][key]

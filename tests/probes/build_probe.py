@@ -1,6 +1,7 @@
 """Build the probe libraries next to this file (hipcc, gfx950): libexp2_probe.so (the tests'
-hardware-exp2 check), libhbm_ceiling.so (the bench's read and copy ceilings) and
-libmfma_ceiling.so (the bench's dense BF16 matrix-core ceiling)."""
+hardware-exp2 check), libhbm_ceiling.so (the bench's read and copy ceilings),
+libmfma_ceiling.so (the bench's dense BF16 matrix-core ceiling) and liblds_ceiling.so (the LDS
+read and direct-to-LDS load rates per CU)."""
 
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ sys.path.insert(0, ROOT)
 from deterministic_selected_token_amd import build as lib_build  # noqa: E402
 
 PROBES = {"libexp2_probe.so": "exp2_probe.hip", "libhbm_ceiling.so": "hbm_ceiling.hip",
-          "libmfma_ceiling.so": "mfma_ceiling.hip"}
+          "libmfma_ceiling.so": "mfma_ceiling.hip", "liblds_ceiling.so": "lds_ceiling.hip"}
 OUT = os.path.join(HERE, "libexp2_probe.so")
 CEILING = os.path.join(HERE, "libhbm_ceiling.so")
 MFMA_CEILING = os.path.join(HERE, "libmfma_ceiling.so")
