@@ -1158,8 +1158,8 @@ def main() -> int:
         extra["variants"]["lds_rates"] = lds_rates(stream)
         for key in ("linear_logp_fwd", "linear_logp_fwd_temperature_0.7", "linear_logp_bwd",
                     "linear_logp_bwd_bf16_out"):
-            v = extra["variants"][key]
-            v["frac_of_measured_mfma_ceiling"] = round(v["tflops"] / mc["tflops"], 4)
+            entry = extra["variants"][key]
+            entry["frac_of_measured_mfma_ceiling"] = round(entry["tflops"] / mc["tflops"], 4)
     if args.profile_copy:
         lib = load_ceiling_library()
         nbytes = 4 << 30
