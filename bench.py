@@ -678,8 +678,11 @@ def time_grpo(dst, case, stream, steps: int) -> dict:
     """The GRPO rows: (1) one GRPO training step on the headline logits viewed as 32
     sequences x 1024 tokens -- logp_forward, grpo_loss (seq_mean, KL 0.04, 10% of tokens
     masked), logp_backward fed with d loss / d logp; (2) grpo_loss alone on 1024 sequences x
-    4096 tokens, against its algorithmic bytes (logp, old_logp, ref_logp 4 B, mask 1 B read
-    once, dlogp 4 B written; 4 B of advantage and 16 B of sums per sequence)."""
+    4096 tokens (token_mean with a local normalizer: 4 launches), against its algorithmic
+    bytes (logp, old_logp, ref_logp 4 B, mask 1 B read once, dlogp 4 B written; 4 B of
+    advantage and 16 B of sums per sequence): calls issued back to back (GPU time per call,
+    and the host's time per call through the Python binding), and one call bracketed on an
+    idle GPU (which includes the host's launch work)."""
     import torch
 
     from deterministic_selected_token_amd import grpo
@@ -764,10 +767,26 @@ def time_grpo(dst, case, stream, steps: int) -> dict:
             ev[1].record(stream)
             ev[2].record(stream)
 
-    ms, _ = timed(loss_only)
+    single_ms, _ = timed(loss_only)
+    # back to back, as a training loop issues them: the host runs ahead of the GPU, so the
+    # per-call time is the GPU's (the bracketed single call above includes the host's work)
+    calls = max(50, 10 * steps)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(calls):
+        loss_only()
+    b.record(stream)
+    host_us = (time.perf_counter() - t0) / calls * 1e6
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / calls
     nbytes = B * T * (4 * 3 + 1 + 4) + B * (4 + 16) + 48
     out["grpo_loss_1024x4096"] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes,
                                   "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                  "calls_back_to_back": calls,
+                                  "host_us_per_call": round(host_us, 1),
+                                  "ms_single_call_idle_gpu": round(single_ms, 4),
                                   "launches": 4, "cpu_baseline": grpo_oracle_rate(
                                       lp, old, ref, adv, mask, nbytes)}
     return out
