@@ -125,13 +125,19 @@ def load_ceiling_library():
     lib.hbm_read.restype = I32
     lib.hbm_copy.argtypes = [P, P, I64, I32, I32, P]
     lib.hbm_copy.restype = I32
+    lib.hbm_copy_nt.argtypes = [P, P, I64, P]
+    lib.hbm_copy_nt.restype = I32
+    lib.hbm_write.argtypes = [P, I64, ctypes.c_uint32, P]
+    lib.hbm_write.restype = I32
     return lib
 
 
 def hbm_ceiling(stream, gib: int = 10, reps: int = 6) -> dict:
     """Measured HBM ceilings: a plain streaming read of `gib` GiB and a plain copy of `gib`
-    GiB each way (tests/probes/hbm_ceiling.hip, non-temporal 16-byte accesses), in several
-    wave shapes; GB/s counts the bytes read (read) or read + written (copy)."""
+    GiB each way (tests/probes/hbm_ceiling.hip, non-temporal 16-byte loads, the backward's
+    `sc1 nt` 16-byte stores), in several wave shapes; GB/s counts the bytes read (read) or
+    read + written (copy).  Beside them, for the record: a write-only fill (`write_gbs`) and
+    the backward's copy shape with non-temporal-only stores."""
     import torch
 
     lib = load_ceiling_library()
@@ -159,8 +165,9 @@ def hbm_ceiling(stream, gib: int = 10, reps: int = 6) -> dict:
         if rc != 0:
             raise RuntimeError(f"hbm ceiling probe failed ({rc})")
 
-    out = {"read_gbs": 0.0, "copy_gbs": 0.0, "bytes": nbytes,
-           "kernels": "tests/probes/hbm_ceiling.hip (hbm_read, hbm_copy)", "shapes": {}}
+    out = {"read_gbs": 0.0, "copy_gbs": 0.0, "write_gbs": 0.0, "bytes": nbytes,
+           "kernels": "tests/probes/hbm_ceiling.hip (hbm_read, hbm_copy, hbm_copy_nt, "
+                      "hbm_write)", "shapes": {}}
     for nv, waves in READ_SHAPES:
         ms = timed(lambda: check(lib.hbm_read(src.data_ptr(), nbytes, nv, waves, 0x9E3779B9,
                                               sink.data_ptr(), h)))
@@ -173,6 +180,12 @@ def hbm_ceiling(stream, gib: int = 10, reps: int = 6) -> dict:
         gbs = 2 * nbytes / (ms * 1e-3) / 1e9
         out["shapes"][f"copy {nv} KiB/wave, {waves} waves/group"] = round(gbs, 1)
         out["copy_gbs"] = max(out["copy_gbs"], round(gbs, 1))
+    ms = timed(lambda: check(lib.hbm_copy_nt(src.data_ptr(), dst.data_ptr(), nbytes, h)))
+    out["shapes"]["copy 16 KiB/wave, 16 waves/group, nt-only stores"] = \
+        round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    ms = timed(lambda: check(lib.hbm_write(dst.data_ptr(), nbytes, 0x5BD1E995, h)))
+    out["write_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    out["shapes"]["write 16 KiB/wave, 16 waves/group"] = out["write_gbs"]
     del src, dst
     torch.cuda.empty_cache()
     return out

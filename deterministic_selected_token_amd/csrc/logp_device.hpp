@@ -178,6 +178,21 @@ __device__ __forceinline__ void load_tile(const typename DtInfo<D>::Storage* __r
     for (int k = 0; k < kLoads; ++k) unpack8<D>(r[k], &t.v[k * kVec]);
 }
 
+// A 16-byte streaming store of the gradient: non-temporal at device scope (`sc1 nt`).  The
+// gradient is written once and not read again by this kernel; with the device-scope bit its
+// lines leave L2 for memory as they are written.  Plain copies of 4 GiB move 6.25 TB/s with
+// it against 6.11 with the non-temporal bit alone (16 KiB per wave), and the headline
+// backward runs 2.4% faster; the stored bits are the same.  A store of more than 8 bytes
+// reads its data registers after it issues, and on this family a VALU write to them needs 2
+// wait states first: the compiler keeps that distance for the stores it emits but does not
+// look inside an asm statement, so the `s_nop 1` (2 wait states) is part of it.  The clobber
+// keeps the compiler from moving other memory accesses across it (an in-place backward reads
+// each element before this store overwrites it).
+__device__ __forceinline__ void store_stream16(u32x4* p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1" : : "v"(p), "v"(v)
+                 : "memory");
+}
+
 // Round 8 gradients to the output dtype (nearest, ties to even) and store them at view
 // columns [c, c+8) of an output row: 16-byte stores when VEC and all 8 lie inside `width`,
 // element stores for the columns below `width` otherwise.
@@ -206,9 +221,8 @@ __device__ __forceinline__ void store8(typename DtInfo<D>::Storage* out, int c, 
     }
     if (VEC && c + kVec <= width) {
         u32x4* p = reinterpret_cast<u32x4*>(out + c);
-        __builtin_nontemporal_store(u32x4{q[0], q[1], q[2], q[3]}, p);
-        if constexpr (D == Dt::F32)
-            __builtin_nontemporal_store(u32x4{q[4], q[5], q[6], q[7]}, p + 1);
+        store_stream16(p, u32x4{q[0], q[1], q[2], q[3]});
+        if constexpr (D == Dt::F32) store_stream16(p + 1, u32x4{q[4], q[5], q[6], q[7]});
         return;
     }
 #pragma unroll

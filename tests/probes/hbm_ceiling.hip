@@ -6,9 +6,11 @@
 //             (lane l holds vectors 64 k + l, so each load instruction covers 1 KiB of
 //             contiguous memory), non-temporal 16-byte loads, all NV issued before any is
 //             used -- the forward's pattern (4 waves per workgroup, 8 KiB per wave per tile).
-//   hbm_copy  the same chunks read and written to a second buffer with non-temporal 16-byte
-//             stores -- the backward's pattern (one read and one write per element;
-//             16 KiB per wave, 16 waves per workgroup).
+//   hbm_copy  the same chunks read and written to a second buffer with 16-byte stores,
+//             non-temporal at device scope (`sc1 nt`) -- the backward's pattern (one read
+//             and one write per element; 16 KiB per wave, 16 waves per workgroup);
+//             hbm_copy_nt the same with the non-temporal bit alone on the stores.
+//   hbm_write fills the chunks with `sc1 nt` stores and reads nothing.
 // Both are plain data movement: no arithmetic beyond an xor that keeps the loads alive.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,6 +38,40 @@ __global__ __launch_bounds__(WAVES * kWave) void read_kernel(const u32x4* __rest
     if (acc == key) sink[0] = acc;  // practically never taken; keeps the loads
 }
 
+// 16-byte store, non-temporal at device scope; the s_nop gives the 2 wait states a VALU needs
+// before it may write the store's data registers (the compiler does not look inside asm).
+__device__ __forceinline__ void store_sc1_nt(u32x4* p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1" : : "v"(p), "v"(v)
+                 : "memory");
+}
+
+template <int NV, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void write_kernel(u32x4* __restrict__ dst,
+                                                              int64_t chunks, uint32_t key) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t chunk = int64_t(blockIdx.x) * WAVES + (threadIdx.x / kWave);
+    if (chunk >= chunks) return;
+    const int64_t base = chunk * (kWave * NV) + lane;
+    const u32x4 v = {key, uint32_t(base), uint32_t(chunk), key ^ uint32_t(lane)};
+#pragma unroll
+    for (int k = 0; k < NV; ++k) store_sc1_nt(dst + base + kWave * k, v);
+}
+
+template <int NV, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void copy_nt_kernel(const u32x4* __restrict__ src,
+                                                                u32x4* __restrict__ dst,
+                                                                int64_t chunks) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t chunk = int64_t(blockIdx.x) * WAVES + (threadIdx.x / kWave);
+    if (chunk >= chunks) return;
+    const int64_t base = chunk * (kWave * NV) + lane;
+    u32x4 v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = __builtin_nontemporal_load(src + base + kWave * k);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) __builtin_nontemporal_store(v[k], dst + base + kWave * k);
+}
+
 template <int NV, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void copy_kernel(const u32x4* __restrict__ src,
                                                              u32x4* __restrict__ dst,
@@ -48,7 +84,7 @@ __global__ __launch_bounds__(WAVES * kWave) void copy_kernel(const u32x4* __rest
 #pragma unroll
     for (int k = 0; k < NV; ++k) v[k] = __builtin_nontemporal_load(src + base + kWave * k);
 #pragma unroll
-    for (int k = 0; k < NV; ++k) __builtin_nontemporal_store(v[k], dst + base + kWave * k);
+    for (int k = 0; k < NV; ++k) store_sc1_nt(dst + base + kWave * k, v[k]);
 }
 
 template <int NV, int WAVES>
@@ -122,4 +158,28 @@ CEILING_API int hbm_copy(const void* src, void* dst, int64_t bytes, int vectors_
 #undef COPY_CASE
     if (e == hipErrorInvalidValue) return 1;
     return e == hipSuccess ? 0 : 2;
+}
+
+// The 16 KiB-per-wave, 16-wave shape only; arguments and returns as for hbm_copy.
+CEILING_API int hbm_copy_nt(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+    if (src == nullptr || dst == nullptr || !aligned16(src) || !aligned16(dst)) return 1;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + uint64_t(bytes) && b < a + uint64_t(bytes)) return 1;  // overlapping buffers
+    const int64_t chunks = chunk_count(bytes, 16, 16);
+    if (chunks < 0) return 1;
+    hipLaunchKernelGGL((copy_nt_kernel<16, 16>), dim3(unsigned((chunks + 15) / 16)),
+                       dim3(16 * kWave), 0, stream, static_cast<const u32x4*>(src),
+                       static_cast<u32x4*>(dst), chunks);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The 16 KiB-per-wave, 16-wave shape only: dst (bytes, a multiple of 16 KiB) is overwritten
+// with values derived from key.  Returns as for hbm_copy.
+CEILING_API int hbm_write(void* dst, int64_t bytes, uint32_t key, hipStream_t stream) {
+    if (dst == nullptr || !aligned16(dst)) return 1;
+    const int64_t chunks = chunk_count(bytes, 16, 16);
+    if (chunks < 0) return 1;
+    hipLaunchKernelGGL((write_kernel<16, 16>), dim3(unsigned((chunks + 15) / 16)),
+                       dim3(16 * kWave), 0, stream, static_cast<u32x4*>(dst), chunks, key);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
 }

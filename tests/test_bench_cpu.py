@@ -91,8 +91,9 @@ def test_oracle_leg_counts_against_known_outputs():
 
 
 def test_ceiling_probes_validate_arguments_on_the_host():
-    """The bench's ceiling probes refuse bad arguments before any launch (code 1), and the
-    matrix-core probe's flop count is its MFMA count times 2 x 32 x 32 x 16."""
+    """The bench's ceiling probes refuse bad arguments before any launch (code 1), the
+    matrix-core probe's flop count is its MFMA count times 2 x 32 x 32 x 16, and the LDS
+    probe's byte counts are its accesses times their widths."""
     import ctypes
     import os
 
@@ -118,3 +119,26 @@ def test_ceiling_probes_validate_arguments_on_the_host():
     assert hbm.hbm_read(a, 1 << 20, 7, 4, 0, b, None) == 1      # no such shape
     assert hbm.hbm_read(a, 1000, 8, 4, 0, b, None) == 1         # not whole chunks
     assert hbm.hbm_copy(a, ctypes.c_void_p(0x10010), 1 << 20, 8, 4, None) == 1  # overlap
+    hbm.hbm_copy_nt.argtypes = [P, P, I64, P]
+    hbm.hbm_write.argtypes = [P, I64, ctypes.c_uint32, P]
+    assert hbm.hbm_copy_nt(a, ctypes.c_void_p(0x10010), 1 << 20, None) == 1      # overlap
+    assert hbm.hbm_copy_nt(a, b, 1000, None) == 1                                # not whole chunks
+    assert hbm.hbm_write(None, 1 << 20, 0, None) == 1
+    assert hbm.hbm_write(ctypes.c_void_p(0x10008), 1 << 20, 0, None) == 1      # misaligned
+    assert hbm.hbm_write(a, (16 << 10) + 16, 0, None) == 1                      # not whole chunks
+    lds = ctypes.CDLL(os.path.join(here, "liblds_ceiling.so"))
+    lds.lds_read.argtypes = [I32, I64, I32, I32, P, P, P]
+    lds.lds_dma.argtypes = [I32, I64, I32, P, I64, P, P, P]
+    lds.lds_read_bytes.argtypes = [I32, I32, I32]
+    lds.lds_read_bytes.restype = ctypes.c_double
+    lds.lds_dma_bytes.argtypes = [I32, I32]
+    lds.lds_dma_bytes.restype = ctypes.c_double
+    assert lds.lds_read_bytes(8, 10, 16) == 8 * 10 * 16 * 64 * 16
+    assert lds.lds_dma_bytes(4, 10) == 4 * 10 * 8 * 1024
+    assert lds.lds_read_bytes(8, 10, 12) == -1.0 and lds.lds_dma_bytes(16, 10) == -1.0
+    assert lds.lds_read(8, 1, 1, 12, b, b, None) == 1                # no such width
+    assert lds.lds_read(6, 1, 1, 16, b, b, None) == 1                # no such wave count
+    assert lds.lds_read(8, 1, 1, 16, None, b, None) == 1
+    assert lds.lds_dma(8, 1, 1, a, 4096, b, b, None) == 1            # source under 8 KiB
+    assert lds.lds_dma(8, 1, 1, a, 8192 + 512, b, b, None) == 1      # not whole KiB
+    assert lds.lds_dma(16, 1, 1, a, 8192, b, b, None) == 1           # 16 waves do not fit
