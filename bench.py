@@ -991,15 +991,77 @@ def time_linear_backward(dst, stream, steps: int, n: int = 8192, hidden: int = 4
     return out
 
 
+def time_linear_kept(dst, stream, steps: int, n: int = 8192, hidden: int = 4096,
+                     vocab: int = 151936, chunk_cols: int = 16384) -> dict:
+    """linear_logp with kept logits on the same LM-head shape: the balanced forward that also
+    writes the scored logits (linear_logp_partials_save, 4 bytes per logit) and the
+    BF16-output backward that reads them (linear_logp_backward_saved: dh and dW on the matrix
+    cores, 4 n V H flops, dz from the kept logits), each timed over ``steps`` calls."""
+    import torch
+
+    from deterministic_selected_token_amd import linear
+
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev).manual_seed(13)
+    h = torch.randn((n, hidden), generator=gen, device=dev).to(torch.bfloat16)
+    W = (torch.randn((vocab, hidden), generator=gen, device=dev) * (3.0 / hidden ** 0.5)) \
+        .to(torch.bfloat16)
+    y = torch.randint(0, vocab, (n,), generator=gen, device=dev)
+    g = torch.randn((n,), generator=gen, device=dev) * 0.01
+    z = torch.empty((n, vocab), dtype=torch.float32, device=dev)
+    P = torch.empty((n, dst.logp_num_tiles(vocab), 3), dtype=torch.float32, device=dev)
+    wsf = torch.empty(max(1, linear.linear_logp_partials_workspace(n, vocab, 0, vocab)),
+                      dtype=torch.uint8, device=dev)
+    dh = torch.empty((n, hidden), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((vocab, hidden), dtype=torch.bfloat16, device=dev)
+    wsb = torch.empty(linear.linear_logp_backward_workspace(n, hidden, chunk_cols,
+                                                            torch.bfloat16),
+                      dtype=torch.uint8, device=dev)
+
+    def fwd():
+        linear.linear_logp_partials(h, W, y, vocab, vocab, 0, vocab, P, stream=stream,
+                                    workspace=wsf, logits=z)
+
+    fwd()
+    _, _, stats = dst.logp_merge(P, y, vocab, stream=stream)
+
+    def bwd():
+        linear.linear_logp_backward(h, W, y, g, stats, vocab, vocab, chunk_cols=chunk_cols,
+                                    dhidden=dh, dweight=dW, workspace=wsb, stream=stream,
+                                    out_dtype=torch.bfloat16, logits=z)
+
+    def timed(fn):
+        fn()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+    fwd_ms, bwd_ms = timed(fwd), timed(bwd)
+    del h, W, z, dW, wsb
+    torch.cuda.empty_cache()
+    return {"logits_bytes": 4 * n * vocab, "forward_keeping_logits_ms": round(fwd_ms, 4),
+            "backward_bf16_out_from_kept_logits_ms": round(bwd_ms, 4),
+            "backward_tflops": round(4.0 * n * vocab * hidden / (bwd_ms * 1e-3) / 1e12, 1)}
+
+
 def time_linear_default(dst, stream) -> dict:
     """The default run's linear_logp entry: the forward with its balancing workspace and the
     BF16-output backward at 8192 x 4096 x 151936, each as TFLOP/s and as a fraction of the
-    dense BF16 matrix-core ceiling measured in the same run (no oracle leg; --variants has the
-    full set)."""
+    dense BF16 matrix-core ceiling measured in the same run, and the same pair with kept
+    logits (no oracle leg; --variants has the full set)."""
     import torch
 
     fwd = time_linear(dst, stream, 3, cpu_baseline=False)
     bwd = time_linear_backward(dst, stream, 2, out_dtype=torch.bfloat16, cpu_baseline=False)
+    kept = time_linear_kept(dst, stream, 2)
+    kept["forward_plus_backward_ms"] = round(kept["forward_keeping_logits_ms"]
+                                             + kept["backward_bf16_out_from_kept_logits_ms"], 4)
+    kept["recomputing_forward_plus_backward_ms"] = round(fwd["partials_ms"] + bwd["ms"], 4)
     mc = mfma_ceiling(stream, reps=3)
     return {"workload": "h [8192, 4096] x W [151936, 4096] BF16, unit temperature",
             "forward": {"ms": fwd["partials_ms"], "merge_ms": fwd["merge_ms"],
@@ -1009,6 +1071,7 @@ def time_linear_default(dst, stream) -> dict:
                                   "frac_of_bf16_peak": bwd["frac_of_bf16_peak"],
                                   "frac_of_measured_mfma_ceiling": round(
                                       bwd["tflops"] / mc["tflops"], 4)},
+            "kept_logits": kept,
             "mfma_bf16_ceiling_tflops": mc["tflops"]}
 
 

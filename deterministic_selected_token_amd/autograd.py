@@ -57,18 +57,25 @@ class LinearLogp(torch.autograd.Function):
     """logp [n] (float32) of ``targets`` under the logits hidden W^T (BF16 hidden [n, H] and
     LM-head weight [V, H]), scored as fl32(acc * inv_temperature); gradients with respect to
     hidden and weight from linear_logp_backward_bf16: accumulated in FP32 and rounded once to
-    BF16, the inputs' dtype, inside the library."""
+    BF16, the inputs' dtype, inside the library.  keep_logits: the forward keeps the scored
+    logits (4 bytes each) and the backward reads them instead of forming them again (the same
+    bits)."""
 
     @staticmethod
     def forward(ctx, hidden, weight, targets, vocab_real, active, ignore_index,
-                inv_temperature, chunk_cols):
+                inv_temperature, chunk_cols, keep_logits=False):
         from .linear import linear_logp_forward
+        z = None
+        if keep_logits:
+            z = torch.empty((hidden.shape[0], weight.shape[0]), dtype=torch.float32,
+                            device=hidden.device)
         logp, _, stats = linear_logp_forward(hidden, weight, targets, vocab_real,
                                              weight.shape[0], active=active,
                                              ignore_index=ignore_index,
-                                             inv_temperature=inv_temperature)
+                                             inv_temperature=inv_temperature, logits=z)
         ctx.save_for_backward(hidden, weight, targets, stats)
         ctx.active = active
+        ctx.logits = z
         ctx.args = (vocab_real, ignore_index, inv_temperature, chunk_cols)
         return logp
 
@@ -83,15 +90,18 @@ class LinearLogp(torch.autograd.Function):
                                       weight.shape[0], active=ctx.active,
                                       ignore_index=ignore_index,
                                       inv_temperature=inv_temperature, chunk_cols=chunk_cols,
-                                      out_dtype=torch.bfloat16)
-        return dh, dw, None, None, None, None, None, None
+                                      out_dtype=torch.bfloat16, logits=ctx.logits)
+        ctx.logits = None
+        return dh, dw, None, None, None, None, None, None, None
 
 
 def linear_logp(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
                 vocab_real: Optional[int] = None, active=None, ignore_index: int = -100,
-                inv_temperature: float = 1.0, chunk_cols: int = 4 * 4096) -> torch.Tensor:
+                inv_temperature: float = 1.0, chunk_cols: int = 4 * 4096,
+                keep_logits: bool = False) -> torch.Tensor:
     """logp[t] = log softmax(hidden[t] W^T)[targets[t]] on the matrix cores, differentiable with
-    respect to hidden and weight (rows of W at or past vocab_real are padding)."""
+    respect to hidden and weight (rows of W at or past vocab_real are padding).  keep_logits
+    trades 4 bytes per logit of memory for a backward that does not form the logits again."""
     vr = weight.shape[0] if vocab_real is None else int(vocab_real)
     return LinearLogp.apply(hidden, weight, targets, vr, active, ignore_index,
-                            inv_temperature, chunk_cols)
+                            inv_temperature, chunk_cols, keep_logits)

@@ -304,12 +304,17 @@ __device__ __forceinline__ void fold_subblock(float& m, float& s, float mb, floa
 // on_sel(r, z) with the target's scored logit when the row's target column in the tile
 // (y_rel[r]) lies in this sub-block, and on_stats(r, mb, ls) with the sub-block's max and
 // sum-exp, both from one thread.  col_tile0: the sub-block's first column in the tile;
-// lim_tile: the tile's real columns (columns at or past it are masked).
-template <bool SCALED, typename OnSel, typename OnStats>
+// lim_tile: the tile's real columns (columns at or past it are masked).  on_z(r, c, x), when
+// given, receives every scored logit once, four at a time: columns c .. c + 3 of the sub-block
+// in row r (masked columns as -inf).
+struct NoZ {
+    __device__ void operator()(int, int, const float4&) const {}
+};
+template <bool SCALED, typename OnSel, typename OnStats, typename OnZ = NoZ>
 __device__ __forceinline__ void reduce_subblock(Smem& sm, f32x16 (&acc)[kTM][kTN], int wm,
                                                 int wn, int lane, float inv_t, int col_tile0,
                                                 int lim_tile, const int* y_rel, OnSel on_sel,
-                                                OnStats on_stats) {
+                                                OnStats on_stats, OnZ on_z = OnZ()) {
     float* red = reinterpret_cast<float*>(&sm.a[0][0]);
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
@@ -338,6 +343,7 @@ __device__ __forceinline__ void reduce_subblock(Smem& sm, f32x16 (&acc)[kTM][kTN
             for (int q = 0; q < kRedCols / 4; ++q) {
                 const float4 x = *reinterpret_cast<const float4*>(src + kRedThreads * 4 * q);
                 mb = fmaxf(fmaxf(mb, x.x), fmaxf(x.y, fmaxf(x.z, x.w)));
+                on_z(row, kRedThreads * 4 * q + 4 * part, x);
             }
             // the selected logit: the thread whose columns hold the target picks it up
             if (yr >= 0 && yr < kBN && ((yr >> 2) & (kRedThreads - 1)) == part)
@@ -364,6 +370,30 @@ __device__ __forceinline__ void reduce_subblock(Smem& sm, f32x16 (&acc)[kTM][kTN
     }
 }
 
+// Where the forward writes the scored logits when asked to keep them: z (FP32) with row stride
+// ld_z, view column 0 first; rows at or past n and columns at or past width are not written.
+struct ZOut {
+    float* z;
+    int64_t ld_z, n;
+    int width;
+};
+
+// Four scored logits of row `row` at view columns [vc, vc + 4) (vc a multiple of 4; z 16-byte
+// aligned and ld_z a multiple of 4, so whole groups go out as one 16-byte store).  They are
+// read back by a later launch, not by this one: non-temporal stores.
+__device__ __forceinline__ void store_z4(const ZOut& o, int64_t row, int vc, const float4& x) {
+    if (row >= o.n || vc >= o.width) return;
+    float* p = o.z + row * o.ld_z + vc;
+    if (vc + 4 <= o.width) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4*>(p));
+        return;
+    }
+    p[0] = x.x;
+    if (vc + 1 < o.width) p[1] = x.y;
+    if (vc + 2 < o.width) p[2] = x.z;
+}
+
 // Row constants of one (row block, tile): y_rel[t] = the target's column inside the tile for a
 // valid row whose target lies in it, else -1.
 // Used by the fold kernel only: in a kernel with a block product, calling it (rather than
@@ -386,14 +416,15 @@ __device__ __forceinline__ int tile_target(int64_t row, int64_t n, const int64_t
 // 8 waves per workgroup (148 KB of LDS, one workgroup per CU): two waves per SIMD cover each
 // other's global-load latency.
 // SCALED = false is the unit temperature: the multiply by inv_t (exact at 1) is left out, as
-// it lengthens the epilogue, which no matrix-core work overlaps.
-template <bool SCALED>
+// it lengthens the epilogue, which no matrix-core work overlaps.  SAVE: the scored logits are
+// also written to zo (zo is not read otherwise).
+template <bool SCALED, bool SAVE>
 __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
     const uint16_t* __restrict__ w, int64_t ld_w, int lim, int row_blocks, int64_t col_begin,
     int64_t vocab_real, float inv_t, const int64_t* __restrict__ targets,
     const uint8_t* __restrict__ active, int64_t ignore_index,
-    logp_partial_t* __restrict__ partials, int64_t ldp) {
+    logp_partial_t* __restrict__ partials, int64_t ldp, ZOut zo) {
     __shared__ Smem sm;
     const int rb_idx = static_cast<int>(blockIdx.x % static_cast<uint32_t>(row_blocks));
     const int tile = static_cast<int>(blockIdx.x / static_cast<uint32_t>(row_blocks));
@@ -441,7 +472,10 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
         reduce_subblock<SCALED>(
             sm, acc, wm, wn, lane, inv_t, col0, lim_here, sm.y_rel,
             [&](int row, float z) { sm.sel[row] = z; },
-            [&](int row, float mb, float ls) { fold_subblock(sm.m[row], sm.s[row], mb, ls); });
+            [&](int row, float mb, float ls) { fold_subblock(sm.m[row], sm.s[row], mb, ls); },
+            [&](int row, int c, const float4& x) {
+                if constexpr (SAVE) store_z4(zo, row0 + row, tile_col0 + col0 + c, x);
+            });
         // the next sub-block's first barrier orders these LDS updates before any reuse
     }
     __syncthreads();
@@ -474,13 +508,13 @@ __global__ __launch_bounds__(kThreads) void linear_partials_kernel(
 // fewer than kSubBlocks, and its pairs come last).  Workgroup g takes tasks g, g + grid, ...
 // With row blocks fastest, the tasks in flight share sub-blocks of W the way the workgroups
 // of linear_partials_kernel share tiles.
-template <bool SCALED>
+template <bool SCALED, bool SAVE>
 __global__ __launch_bounds__(kThreads) void linear_split_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
     const uint16_t* __restrict__ w, int64_t ld_w, int lim, int row_blocks, int64_t col_begin,
     int64_t vocab_real, float inv_t, const int64_t* __restrict__ targets,
     const uint8_t* __restrict__ active, int64_t ignore_index, int tile0, int tasks,
-    float2* __restrict__ ws_stats, float* __restrict__ ws_sel) {
+    float2* __restrict__ ws_stats, float* __restrict__ ws_sel, ZOut zo) {
     __shared__ Smem sm;
     const int lane = lane_id(), wave = wave_id();
     const int wm = wave / kWN, wn = wave % kWN;
@@ -522,7 +556,10 @@ __global__ __launch_bounds__(kThreads) void linear_split_kernel(
         reduce_subblock<SCALED>(
             sm, acc, wm, wn, lane, inv_t, col0, lim_here, sm.y_rel,
             [&](int row, float z) { se[row] = z; },
-            [&](int row, float mb, float ls) { st[row] = make_float2(mb, ls); });
+            [&](int row, float mb, float ls) { st[row] = make_float2(mb, ls); },
+            [&](int row, int c, const float4& x) {
+                if constexpr (SAVE) store_z4(zo, row0 + row, tile_col0 + col0 + c, x);
+            });
     }
 }
 
@@ -567,9 +604,81 @@ __global__ __launch_bounds__(kBM) void linear_fold_kernel(
 // transposed into the workspace first.  Every operand in the workspace is zero-padded to whole
 // 256 x 256 blocks, so the products need no load bounds.
 
-// Row constants of dz in LDS: sm.m = M, sm.s = -g'/S, sm.sel = that times 2^-64, g' = g inv_t
-// in `gsc`, and sm.y_rel = the target's column inside this sub-block, -1 when elsewhere, -2
-// for a row without gradient (padding, masked, ignored, out-of-range target, M = -inf).
+// Row constants of dz, for row t of the block at row0: m = M, s = -g'/S, sel = that times
+// 2^-64, gsc = g' = g inv_t, and y_rel = the target's column inside the sub-block at chunk
+// column col0, -1 when elsewhere, -2 for a row without gradient (padding, masked, ignored,
+// out-of-range target, M = -inf).
+template <bool SCALED>
+__device__ __forceinline__ void dz_row_constants(
+    int t, int64_t row0, int col0, int64_t n, int64_t chunk_col0, int64_t vocab_real,
+    float inv_t, const int64_t* __restrict__ targets, const uint8_t* __restrict__ active,
+    int64_t ignore_index, const float* __restrict__ grad, const logp_stats_t* __restrict__ stats,
+    int* y_rel, float* m, float* s, float* sel, float* gsc) {
+    const int64_t row = row0 + t;
+    int yr = -2;
+    float M = 0.0f, nc = 0.0f, gs = 0.0f;
+    if (row < n) {
+        int64_t y;
+        const logp_stats_t st = stats[row];
+        if (row_valid(targets, active, ignore_index, vocab_real, row, y) && st.max != kNegInf) {
+            gs = SCALED ? grad[row] * inv_t : grad[row];  // d z / d x = inv_t
+            M = st.max;
+            nc = -(gs / st.sumexp);
+            const int64_t c = y - chunk_col0 - col0;
+            yr = (c >= 0 && c < kBN) ? static_cast<int>(c) : -1;
+        }
+    }
+    y_rel[t] = yr;
+    m[t] = M;
+    s[t] = nc;
+    sel[t] = nc * 0x1p-64f;
+    gsc[t] = gs;
+}
+
+// dz of one 256 x 256 block (rows at row0, chunk columns at col0; lim: the chunk's real
+// columns) from the scored logits held in the accumulator layout of block_product: z =
+// fl32(acc inv_t) when SCALE, else acc holds z itself.  Written in BF16 to dz [row][column]
+// and to dzt [column][row]; rows without gradient and masked columns get 0.
+template <bool SCALE>
+__device__ __forceinline__ void dz_block_out(
+    const f32x16 (&acc)[kTM][kTN], float inv_t, int wm, int wn, int lane, int64_t row0,
+    int col0, int lim, const int* y_rel, const float* m, const float* s, const float* sel,
+    const float* gsc, uint16_t* __restrict__ dz, int64_t ldz, uint16_t* __restrict__ dzt,
+    int64_t ldzt) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int lc = col0 + wn * (kTN * 32) + j * 32 + (lane & 31);  // in the chunk
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int lr0 = wm * (kTM * 32) + i * 32 + 8 * q + 4 * (lane >> 5);
+                uint16_t out[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int lr = lr0 + e;
+                    const int yr = y_rel[lr];
+                    float d = 0.0f;
+                    if (yr != -2 && lc < lim) {
+                        const float acc_v = acc[i][j][4 * q + e];
+                        const float z = SCALE ? acc_v * inv_t : acc_v;
+                        d = bwd_term_deep<true>(z, m[lr], s[lr], sel[lr]);
+                        if (lc - col0 == yr) d = gsc[lr] + d;  // g' (1 - p)
+                    }
+                    out[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(d));
+                    dz[(row0 + lr) * ldz + lc] = out[e];
+                }
+                // the 4 rows are consecutive: one 8-byte store into the transposed copy
+                *reinterpret_cast<uint2*>(&dzt[int64_t(lc) * ldzt + row0 + lr0]) =
+                    make_uint2(uint32_t(out[0]) | (uint32_t(out[1]) << 16),
+                               uint32_t(out[2]) | (uint32_t(out[3]) << 16));
+            }
+        }
+    }
+}
+
+// dz of one (row block, 256-column sub-block) of the chunk at chunk_col0, the logits
+// recomputed by block_product: bit for bit the forward's.
 template <bool SCALED>
 __global__ __launch_bounds__(kThreads) void linear_dz_kernel(
     const uint16_t* __restrict__ h, int64_t ld_h, int64_t n, int H,
@@ -587,29 +696,11 @@ __global__ __launch_bounds__(kThreads) void linear_dz_kernel(
     const int lane = lane_id(), wave = wave_id();
     const int wm = wave / kWN, wn = wave % kWN;
 
-    if (threadIdx.x < kBM) {
-        const int t = threadIdx.x;
-        const int64_t row = row0 + t;
-        int yr = -2;
-        float M = 0.0f, nc = 0.0f, gs = 0.0f;
-        if (row < n) {
-            int64_t y;
-            const logp_stats_t st = stats[row];
-            if (row_valid(targets, active, ignore_index, vocab_real, row, y) &&
-                st.max != kNegInf) {
-                gs = SCALED ? grad[row] * inv_t : grad[row];  // d z / d x = inv_t
-                M = st.max;
-                nc = -(gs / st.sumexp);
-                const int64_t c = y - chunk_col0 - col0;
-                yr = (c >= 0 && c < kBN) ? static_cast<int>(c) : -1;
-            }
-        }
-        sm.y_rel[t] = yr;
-        sm.m[t] = M;
-        sm.s[t] = nc;
-        sm.sel[t] = nc * 0x1p-64f;
-        gsc[t] = gs;
-    }
+    // block_product's barriers order these LDS writes before the epilogue reads them
+    if (threadIdx.x < kBM)
+        dz_row_constants<SCALED>(threadIdx.x, row0, col0, n, chunk_col0, vocab_real, inv_t,
+                                 targets, active, ignore_index, grad, stats, sm.y_rel, sm.m,
+                                 sm.s, sm.sel, gsc);
 
     f32x16 acc[kTM][kTN];
 #pragma unroll
@@ -622,37 +713,52 @@ __global__ __launch_bounds__(kThreads) void linear_dz_kernel(
     block_product(sm, h + row0 * ld_h, static_cast<uint32_t>(ld_h), n_here, w,
                   static_cast<uint32_t>(ld_w), lim, H, col0, (H + kBK - 1) / kBK, wm, wn, lane,
                   acc);
+    dz_block_out<SCALED>(acc, inv_t, wm, wn, lane, row0, col0, lim, sm.y_rel, sm.m, sm.s, sm.sel,
+                         gsc, dz, ldz, dzt, ldzt);
+}
 
+// The same dz from scored logits the forward kept (z [row][chunk column], FP32, row stride
+// ld_z, the chunk's column 0 first): each value is read where the accumulator layout holds
+// it, so dz_block_out applies the same arithmetic to the same z and the bits are those of
+// linear_dz_kernel.  Memory-bound: 4 bytes read and 4 written per logit.
+template <bool SCALED>
+__global__ __launch_bounds__(kThreads) void linear_dz_saved_kernel(
+    const float* __restrict__ z, int64_t ld_z, int64_t n, int lim, int row_blocks,
+    int64_t chunk_col0, int64_t vocab_real, float inv_t, const int64_t* __restrict__ targets,
+    const uint8_t* __restrict__ active, int64_t ignore_index, const float* __restrict__ grad,
+    const logp_stats_t* __restrict__ stats, uint16_t* __restrict__ dz, int64_t ldz,
+    uint16_t* __restrict__ dzt, int64_t ldzt) {
+    __shared__ int y_rel[kBM];
+    __shared__ float m[kBM], s[kBM], sel[kBM], gsc[kBM];
+    const int rb_idx = static_cast<int>(blockIdx.x % static_cast<uint32_t>(row_blocks));
+    const int sb = static_cast<int>(blockIdx.x / static_cast<uint32_t>(row_blocks));
+    const int64_t row0 = int64_t(rb_idx) * kBM;
+    const int col0 = sb * kBN;
+    const int lane = lane_id(), wave = wave_id();
+    const int wm = wave / kWN, wn = wave % kWN;
+    if (threadIdx.x < kBM)
+        dz_row_constants<SCALED>(threadIdx.x, row0, col0, n, chunk_col0, vocab_real, inv_t,
+                                 targets, active, ignore_index, grad, stats, y_rel, m, s, sel,
+                                 gsc);
+    __syncthreads();
+    f32x16 acc[kTM][kTN];
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
-            const int lc = col0 + wn * (kTN * 32) + j * 32 + (lane & 31);  // in the chunk
+            const int lc = col0 + wn * (kTN * 32) + j * 32 + (lane & 31);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int lr0 = wm * (kTM * 32) + i * 32 + 8 * q + 4 * (lane >> 5);
-                uint16_t out[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int lr = lr0 + e;
-                    const int yr = sm.y_rel[lr];
-                    float d = 0.0f;
-                    if (yr != -2 && lc < lim) {
-                        const float acc_v = acc[i][j][4 * q + e];
-                        const float z = SCALED ? acc_v * inv_t : acc_v;
-                        d = bwd_term_deep<true>(z, sm.m[lr], sm.s[lr], sm.sel[lr]);
-                        if (lc - col0 == yr) d = gsc[lr] + d;  // g' (1 - p)
-                    }
-                    out[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(d));
-                    dz[(row0 + lr) * ldz + lc] = out[e];
-                }
-                // the 4 rows are consecutive: one 8-byte store into the transposed copy
-                *reinterpret_cast<uint2*>(&dzt[int64_t(lc) * ldzt + row0 + lr0]) =
-                    make_uint2(uint32_t(out[0]) | (uint32_t(out[1]) << 16),
-                               uint32_t(out[2]) | (uint32_t(out[3]) << 16));
+            for (int r = 0; r < 16; ++r) {
+                const int lr = wm * (kTM * 32) + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+                // only the logits dz_block_out uses: rows with a gradient, real columns
+                acc[i][j][r] = (y_rel[lr] != -2 && lc < lim)
+                                   ? __builtin_nontemporal_load(&z[(row0 + lr) * ld_z + lc])
+                                   : 0.0f;
             }
         }
     }
+    dz_block_out<false>(acc, inv_t, wm, wn, lane, row0, col0, lim, y_rel, m, s, sel, gsc, dz,
+                        ldz, dzt, ldzt);
 }
 
 // Where gemm_tn_kernel's FP32 block results go.  The accumulating forms start the accumulator
@@ -841,7 +947,8 @@ logp_status_t backward_impl(
     int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
     int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, void* dhidden,
     int64_t ld_dh, void* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
-    int64_t chunk_cols, hipStream_t stream, bool use_scratch, bool bf16_out) {
+    int64_t chunk_cols, hipStream_t stream, bool use_scratch, bool bf16_out,
+    const float* saved = nullptr, int64_t ld_saved = 0) {
     if (!(inv_temperature > 0.0f) || !std::isfinite(inv_temperature)) return LOGP_ERR_ARG;
     if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
         vocab_padded > (int64_t(1) << 31) - 1 - kTile || n > LINEAR_LOGP_BWD_MAX_ROWS)
@@ -873,6 +980,11 @@ logp_status_t backward_impl(
     if (!aligned16(hidden) || (weight != nullptr && !aligned16(weight)) ||
         (!use_scratch && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
         return LOGP_ERR_SHAPE;
+    // saved scored logits (optional): [n, ld_saved] FP32, the view's real columns read
+    if (saved != nullptr && (ld_saved < width || ld_saved > LINEAR_LOGP_MAX_SAVED_LD ||
+                             n > (int64_t(1) << 40) / std::max<int64_t>(ld_saved, 1) ||
+                             (reinterpret_cast<uintptr_t>(saved) & 3u) != 0))
+        return LOGP_ERR_SHAPE;
     const int64_t staging = linear_logp_backward_workspace(n, H, chunk_cols);
     if (staging < 0) return LOGP_ERR_SHAPE;
     const int64_t need = staging + (bf16_out ? dh_accumulator_bytes(n, H) : 0);
@@ -884,7 +996,8 @@ logp_status_t backward_impl(
                        {targets, uint64_t(n) * 8},
                        {active, active ? uint64_t(n) : 0},
                        {grad_logp, uint64_t(n) * 4},
-                       {stats, uint64_t(n) * sizeof(logp_stats_t)}};
+                       {stats, uint64_t(n) * sizeof(logp_stats_t)},
+                       {saved, saved != nullptr && lim > 0 ? span_bytes(n, ld_saved, lim, 4) : 0}};
     // the static scratch array is not a caller buffer: it cannot overlap one, and it is not
     // checked as one
     const int out_size = bf16_out ? 2 : 4;
@@ -892,7 +1005,7 @@ logp_status_t backward_impl(
                         {dweight, width > 0 ? span_bytes(width, ld_dw, H, out_size) : 0},
                         {use_scratch ? nullptr : workspace, use_scratch ? 0 : uint64_t(need)}};
     int dev = -1;
-    logp_status_t st = check_buffers(in, 6, out, 3, stream, &dev);
+    logp_status_t st = check_buffers(in, 7, out, 3, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
     if (!guard.ok()) return LOGP_ERR_HIP;
@@ -934,6 +1047,9 @@ logp_status_t backward_impl(
     const bool scaled = inv_temperature != 1.0f;
     const void* dz_kernel = scaled ? reinterpret_cast<const void*>(&linear_dz_kernel<true>)
                                    : reinterpret_cast<const void*>(&linear_dz_kernel<false>);
+    const void* dz_saved_kernel =
+        scaled ? reinterpret_cast<const void*>(&linear_dz_saved_kernel<true>)
+               : reinterpret_cast<const void*>(&linear_dz_saved_kernel<false>);
     int row_blocks = static_cast<int>(n_pad / kBM);
     for (int64_t off = 0; off < width; off += chunk_cols) {
         const int64_t cw = std::min(chunk_cols, width - off);     // chunk columns
@@ -949,16 +1065,26 @@ logp_status_t backward_impl(
                         dim3(256), args, 0, stream);
             if (st != LOGP_OK) return st;
         }
-        {  // dz and dz^T
+        {  // dz and dz^T: from the saved logits when given, else the logits recomputed
             int64_t ldz = c_pad, ldzt = n_pad;
             int64_t cc0 = chunk_col0;
             float inv_t = inv_temperature;
-            void* args[] = {&hidden, &ld_h, &n,     &Hi,     &wc,          &ld_w,
-                            &lim_c,  &row_blocks,   &cc0,    &vocab_real,  &inv_t,
-                            &targets, &active,      &ignore_index, &grad_logp, &stats,
-                            &dz,     &ldz,          &dzT,    &ldzt};
-            st = launch(dz_kernel, dim3(static_cast<uint32_t>(row_blocks * (c_pad / kBN))),
-                        dim3(kThreads), args, 0, stream);
+            const dim3 grid(static_cast<uint32_t>(row_blocks * (c_pad / kBN)));
+            if (saved != nullptr) {
+                const float* zc = saved + off;
+                int64_t ldzc = ld_saved;
+                void* args[] = {&zc,      &ldzc,   &n,     &lim_c,        &row_blocks,
+                                &cc0,     &vocab_real,     &inv_t,        &targets,
+                                &active,  &ignore_index,   &grad_logp,    &stats,
+                                &dz,      &ldz,    &dzT,   &ldzt};
+                st = launch(dz_saved_kernel, grid, dim3(kThreads), args, 0, stream);
+            } else {
+                void* args[] = {&hidden, &ld_h, &n,     &Hi,     &wc,          &ld_w,
+                                &lim_c,  &row_blocks,   &cc0,    &vocab_real,  &inv_t,
+                                &targets, &active,      &ignore_index, &grad_logp, &stats,
+                                &dz,     &ldz,          &dzT,    &ldzt};
+                st = launch(dz_kernel, grid, dim3(kThreads), args, 0, stream);
+            }
             if (st != LOGP_OK) return st;
         }
         {  // dh (= | +=) dz W: a = dz [n_pad, c_pad], b = W^T [h_pad, c_pad]
@@ -1024,7 +1150,8 @@ logp_status_t partials_impl(float inv_temperature, const uint16_t* hidden, int64
                             int64_t vocab_real, int64_t vocab_padded, int64_t col_begin,
                             int64_t col_end, const int64_t* targets, const uint8_t* active,
                             int64_t ignore_index, logp_partial_t* partials, int64_t ldp,
-                            void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+                            void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                            float* saved = nullptr, int64_t ld_saved = 0) {
     if (!(inv_temperature > 0.0f) || !std::isfinite(inv_temperature)) return LOGP_ERR_ARG;
     if (n < 0 || vocab_real < 1 || vocab_padded < vocab_real ||
         vocab_padded > (int64_t(1) << 31) - 1 - kTile)
@@ -1055,6 +1182,12 @@ logp_status_t partials_impl(float inv_temperature, const uint16_t* hidden, int64
     const int64_t width = col_end - col_begin;
     const int64_t view_tiles = ceil_div(width, kTile);
     if (ldp < view_tiles) return LOGP_ERR_SHAPE;
+    // saved scored logits (optional): [n, ld_saved] FP32, 16-byte aligned rows
+    if (saved != nullptr && (ld_saved < width || ld_saved % 4 != 0 ||
+                             ld_saved > LINEAR_LOGP_MAX_SAVED_LD ||
+                             n > (int64_t(1) << 40) / std::max<int64_t>(ld_saved, 1) ||
+                             !aligned16(saved)))
+        return LOGP_ERR_SHAPE;
     if (n > (int64_t(1) << 40) / ld_h) return LOGP_ERR_SHAPE;
     const int64_t row_blocks = ceil_div(n, kBM);
     if (row_blocks * view_tiles > 0x7FFFFFFF) return LOGP_ERR_SHAPE;
@@ -1063,9 +1196,10 @@ logp_status_t partials_impl(float inv_temperature, const uint16_t* hidden, int64
                        {targets, uint64_t(n) * 8},
                        {active, active ? uint64_t(n) : 0}};
     const Span out[] = {{partials, span_bytes(n, ldp, view_tiles, sizeof(logp_partial_t))},
-                        {workspace, workspace != nullptr ? uint64_t(workspace_bytes) : 0}};
+                        {workspace, workspace != nullptr ? uint64_t(workspace_bytes) : 0},
+                        {saved, saved != nullptr && lim > 0 ? span_bytes(n, ld_saved, lim, 4) : 0}};
     int dev = -1;
-    logp_status_t st = check_buffers(in, 4, out, 2, stream, &dev);
+    logp_status_t st = check_buffers(in, 4, out, 3, stream, &dev);
     if (st != LOGP_OK) return st;
     DeviceGuard guard(dev);
     if (!guard.ok()) return LOGP_ERR_HIP;
@@ -1089,13 +1223,20 @@ logp_status_t partials_impl(float inv_temperature, const uint16_t* hidden, int64
     }
     int Hi = static_cast<int>(H), lim_i = static_cast<int>(lim);
     int rbk = static_cast<int>(row_blocks);
+    // the view's real columns are written: the others are masked, and the split below skips
+    // fully masked sub-blocks
+    ZOut zo{saved, ld_saved, n, lim_i};
+    const bool unit = inv_temperature == 1.0f, save = saved != nullptr;
     if (t0 > 0) {
         void* args[] = {&hidden,    &ld_h,       &n,     &Hi,     &weight,       &ld_w,
                         &lim_i,     &rbk,        &col_begin,     &vocab_real,   &inv_temperature,
-                        &targets,   &active,     &ignore_index,  &partials,     &ldp};
-        const void* kernel = inv_temperature == 1.0f
-                                 ? reinterpret_cast<const void*>(&linear_partials_kernel<false>)
-                                 : reinterpret_cast<const void*>(&linear_partials_kernel<true>);
+                        &targets,   &active,     &ignore_index,  &partials,     &ldp,
+                        &zo};
+        const void* kernel =
+            unit ? (save ? reinterpret_cast<const void*>(&linear_partials_kernel<false, true>)
+                         : reinterpret_cast<const void*>(&linear_partials_kernel<false, false>))
+                 : (save ? reinterpret_cast<const void*>(&linear_partials_kernel<true, true>)
+                         : reinterpret_cast<const void*>(&linear_partials_kernel<true, false>));
         st = launch(kernel, dim3(static_cast<uint32_t>(row_blocks * t0)), dim3(kThreads), args,
                     0, stream);
         if (st != LOGP_OK) return st;
@@ -1108,10 +1249,12 @@ logp_status_t partials_impl(float inv_temperature, const uint16_t* hidden, int64
         void* args[] = {&hidden,  &ld_h,      &n,          &Hi,           &weight,
                         &ld_w,    &lim_i,     &rbk,        &col_begin,    &vocab_real,
                         &inv_temperature, &targets, &active, &ignore_index, &tile0,
-                        &ntask,   &ws_stats,  &ws_sel};
-        const void* kernel = inv_temperature == 1.0f
-                                 ? reinterpret_cast<const void*>(&linear_split_kernel<false>)
-                                 : reinterpret_cast<const void*>(&linear_split_kernel<true>);
+                        &ntask,   &ws_stats,  &ws_sel,     &zo};
+        const void* kernel =
+            unit ? (save ? reinterpret_cast<const void*>(&linear_split_kernel<false, true>)
+                         : reinterpret_cast<const void*>(&linear_split_kernel<false, false>))
+                 : (save ? reinterpret_cast<const void*>(&linear_split_kernel<true, true>)
+                         : reinterpret_cast<const void*>(&linear_split_kernel<true, false>));
         st = launch(kernel, dim3(static_cast<uint32_t>(std::min<int64_t>(cus, tasks))),
                     dim3(kThreads), args, 0, stream);
         if (st != LOGP_OK) return st;
@@ -1151,6 +1294,18 @@ logp_status_t linear_logp_partials_ws(float inv_temperature, const uint16_t* hid
     return partials_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
                          vocab_padded, col_begin, col_end, targets, active, ignore_index,
                          partials, ldp, workspace, workspace_bytes, stream);
+}
+
+logp_status_t linear_logp_partials_save(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, logp_partial_t* partials, int64_t ldp, float* logits,
+    int64_t ld_logits, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    if (logits == nullptr) return LOGP_ERR_NULL;
+    return partials_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
+                         vocab_padded, col_begin, col_end, targets, active, ignore_index,
+                         partials, ldp, workspace, workspace_bytes, stream, logits, ld_logits);
 }
 
 logp_status_t linear_logp_partials_ex(float inv_temperature, const uint16_t* hidden,
@@ -1228,6 +1383,23 @@ logp_status_t linear_logp_backward_noalloc(
                          vocab_padded, col_begin, col_end, targets, active, ignore_index,
                          grad_logp, stats, dhidden, ld_dh, dweight, ld_dw, nullptr, 0, chunk_cols,
                          stream, true, false);
+}
+
+logp_status_t linear_logp_backward_saved(
+    float inv_temperature, const float* logits, int64_t ld_logits, const uint16_t* hidden,
+    int64_t ld_h, int64_t n, int64_t hidden_size, const uint16_t* weight, int64_t ld_w,
+    int64_t vocab_real, int64_t vocab_padded, int64_t col_begin, int64_t col_end,
+    const int64_t* targets, const uint8_t* active, int64_t ignore_index,
+    const float* grad_logp, const logp_stats_t* stats, void* dhidden, int64_t ld_dh,
+    void* dweight, int64_t ld_dw, int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream) {
+    if (out_dtype != LOGP_DTYPE_F32 && out_dtype != LOGP_DTYPE_BF16) return LOGP_ERR_ARG;
+    if (logits == nullptr) return LOGP_ERR_NULL;
+    return backward_impl(inv_temperature, hidden, ld_h, n, hidden_size, weight, ld_w, vocab_real,
+                         vocab_padded, col_begin, col_end, targets, active, ignore_index,
+                         grad_logp, stats, dhidden, ld_dh, dweight, ld_dw, workspace,
+                         workspace_bytes, chunk_cols, stream, false,
+                         out_dtype == LOGP_DTYPE_BF16, logits, ld_logits);
 }
 
 logp_status_t linear_logp_backward(const uint16_t* hidden, int64_t ld_h, int64_t n,

@@ -26,12 +26,14 @@ EXPORTED = ("linear_logp_partials", "linear_logp_partials_ex", "linear_logp_part
             "linear_logp_partials_workspace", "linear_logp_backward",
             "linear_logp_backward_ex", "linear_logp_backward_workspace",
             "linear_logp_backward_noalloc", "linear_logp_backward_bf16",
-            "linear_logp_backward_bf16_workspace")
+            "linear_logp_backward_bf16_workspace", "linear_logp_partials_save",
+            "linear_logp_backward_saved")
 MAX_HIDDEN = 65536
 MAX_LD = 262144
 BWD_MAX_ROWS = 8388608
 BWD_MAX_CHUNK = 1048576
 NOALLOC_SCRATCH_BYTES = 128 << 20
+MAX_SAVED_LD = 1 << 31
 DEFAULT_CHUNK_COLS = 4 * TILE_COLS
 
 _P, _I64 = ctypes.c_void_p, ctypes.c_int64
@@ -60,7 +62,15 @@ _lib.linear_logp_backward_bf16.argtypes = _lib.linear_logp_backward_ex.argtypes
 _lib.linear_logp_backward_bf16.restype = ctypes.c_int32
 _lib.linear_logp_backward_bf16_workspace.argtypes = [_I64, _I64, _I64]
 _lib.linear_logp_backward_bf16_workspace.restype = _I64
+_lib.linear_logp_partials_save.argtypes = (_lib.linear_logp_partials_ex.argtypes[:-1]
+                                           + [_P, _I64, _P, _I64, _P])
+_lib.linear_logp_partials_save.restype = ctypes.c_int32
+_lib.linear_logp_backward_saved.argtypes = ([ctypes.c_float, _P, _I64]
+                                            + _lib.linear_logp_backward.argtypes[:-4]
+                                            + [ctypes.c_int32, _P, _I64, _I64, _P])
+_lib.linear_logp_backward_saved.restype = ctypes.c_int32
 _OUT_DTYPES = (torch.float32, torch.bfloat16)
+_DTYPE_CODE = {torch.float32: 2, torch.bfloat16: 0}  # logp_dtype_t
 
 
 def _bf16_rows(name: str, t: torch.Tensor, device=None) -> torch.Tensor:
@@ -77,6 +87,18 @@ def _row_stride(t: torch.Tensor) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else int(max(t.shape[1], t.stride(0), 8))
 
 
+def _saved_logits(t: torch.Tensor, n: int, width: int, device) -> tuple:
+    """(pointer, row stride) of a float32 [n, >= width] tensor of kept logits with unit column
+    stride on ``device``."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device:
+        raise ValueError(f"logits must be a float32 tensor on {device}")
+    if t.dim() != 2 or t.shape[0] != n or t.shape[1] < width or \
+            (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"logits must be [{n}, >= {width}] with unit column stride")
+    ld = int(t.stride(0)) if n > 1 else int(-(-max(t.shape[1], 4) // 4) * 4)
+    return t.data_ptr(), ld
+
+
 def linear_logp_partials_workspace(n: int, vocab_real: int, col_begin: int,
                                    col_end: int) -> int:
     """Workspace bytes with which linear_logp_partials can always balance its last rounds
@@ -89,13 +111,16 @@ def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: to
                          vocab_real: int, vocab_padded: int, col_begin: int, col_end: int,
                          partials: torch.Tensor, active=None, ignore_index: int = -100,
                          stream=None, inv_temperature: float = 1.0,
-                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         workspace: Optional[torch.Tensor] = None,
+                         logits: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Write the (m, s, sel) partials of vocab columns [col_begin, col_end) of the scored
     logits fl32(h W^T * inv_temperature) into the full ``partials`` buffer; ``weight`` is the
     row slice W[col_begin:col_end].  With a ``workspace`` (a contiguous uint8 GPU tensor,
     linear_logp_partials_workspace bytes always suffice) linear_logp_partials_ws balances the
     launch's last rounds over every CU, with bitwise the same partials; without one,
-    inv_temperature = 1 calls the plain entry point."""
+    inv_temperature = 1 calls the plain entry point.  With ``logits`` (float32 [n, >= col_end -
+    col_begin], 16-byte aligned rows) linear_logp_partials_save also keeps the scored logits
+    of the view's real columns there, for linear_logp_backward(..., logits=)."""
     if not isinstance(hidden, torch.Tensor):
         raise TypeError("hidden must be a torch.Tensor")
     slot = _shard_slot(partials, hidden.shape[0], col_begin, col_end)
@@ -117,11 +142,17 @@ def linear_logp_partials(hidden: torch.Tensor, weight: torch.Tensor, targets: to
     args = (_ptr(hidden), _row_stride(hidden), n, H, _ptr(weight), _row_stride(weight),
             int(vocab_real), int(vocab_padded), int(col_begin), int(col_end), _ptr(targets),
             _ptr(active), int(ignore_index), first.data_ptr(), ldp, _stream(dev, stream))
-    if workspace is not None:
-        if not isinstance(workspace, torch.Tensor) or workspace.device != dev or \
-                workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous uint8 GPU tensor on the same "
-                             "device")
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or
+                                  workspace.device != dev or workspace.dtype != torch.uint8 or
+                                  not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor on the same device")
+    if logits is not None:
+        zp, ldz = _saved_logits(logits, n, int(col_end) - int(col_begin), dev)
+        _check("linear_logp_partials_save", _lib.linear_logp_partials_save(
+            float(inv_temperature), *args[:-1], zp, ldz,
+            _ptr(workspace) if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, args[-1]))
+    elif workspace is not None:
         _check("linear_logp_partials_ws", _lib.linear_logp_partials_ws(
             float(inv_temperature), *args[:-1], _ptr(workspace), workspace.numel(), args[-1]))
     elif inv_temperature == 1.0:
@@ -139,11 +170,13 @@ def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: tor
                         logp: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                         stats: Optional[torch.Tensor] = None, stream=None,
                         inv_temperature: float = 1.0,
-                        workspace: Optional[torch.Tensor] = None, balance: bool = True):
+                        workspace: Optional[torch.Tensor] = None, balance: bool = True,
+                        logits: Optional[torch.Tensor] = None):
     """logp, LSE and (M, S) of the scored logits fl32(h W^T * inv_temperature) over the
     whole vocabulary: linear_logp_partials over all tiles, then logp_merge -> (logp, lse,
     stats).  balance=True (the default) passes a workspace, allocated with torch when none is
-    given, so that the last rounds spread over every CU; the results are the same bits."""
+    given, so that the last rounds spread over every CU; the results are the same bits.
+    ``logits`` (float32 [n, >= vocab_padded]) keeps the scored logits for the backward."""
     vocab_padded = weight.shape[0] if vocab_padded is None else int(vocab_padded)
     vocab_real = vocab_padded if vocab_real is None else int(vocab_real)
     n = hidden.shape[0]
@@ -157,7 +190,7 @@ def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: tor
     linear_logp_partials(hidden, weight, targets, vocab_real, vocab_padded, 0, vocab_padded,
                          partials, active=active, ignore_index=ignore_index, stream=stream,
                          inv_temperature=inv_temperature,
-                         workspace=workspace if balance else None)
+                         workspace=workspace if balance else None, logits=logits)
     return logp_merge(partials, targets, vocab_real, num_tiles=L, active=active,
                       ignore_index=ignore_index, logp=logp, lse=lse, stats=stats,
                       stream=stream)
@@ -184,7 +217,8 @@ def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: to
                          dhidden: Optional[torch.Tensor] = None,
                          dweight: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None,
-                         noalloc: bool = False, out_dtype: torch.dtype = torch.float32):
+                         noalloc: bool = False, out_dtype: torch.dtype = torch.float32,
+                         logits: Optional[torch.Tensor] = None):
     """(dhidden [n, H], dweight [col_end - col_begin, H]) of ``out_dtype``: the gradients of
     sum_t grad_logp[t] logp[t] with respect to hidden and to the weight rows
     W[col_begin:col_end] (``weight`` is that row slice), for the logits of linear_logp_forward
@@ -195,11 +229,16 @@ def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: to
     allocated with torch when none is passed.  noalloc=True (float32 only) calls
     linear_logp_backward_noalloc instead, which stages in the library's static scratch array
     (at most NOALLOC_SCRATCH_BYTES of workspace) and allocates nothing; pass dhidden and
-    dweight as well to keep torch from allocating them."""
+    dweight as well to keep torch from allocating them.  ``logits`` (float32 [n, >= col_end -
+    col_begin], the scored logits linear_logp_partials(..., logits=) kept for this view)
+    calls linear_logp_backward_saved, which reads them instead of forming h W^T again: the
+    same bits, two products instead of three."""
     if out_dtype not in _OUT_DTYPES:
         raise ValueError(f"out_dtype must be one of {_OUT_DTYPES}")
     if noalloc and out_dtype != torch.float32:
         raise ValueError("noalloc writes float32 gradients only")
+    if noalloc and logits is not None:
+        raise ValueError("noalloc recomputes the logits; it takes no saved logits")
     hidden = _bf16_rows("hidden", hidden)
     dev = hidden.device
     weight = _bf16_rows("weight", weight, dev)
@@ -248,7 +287,11 @@ def linear_logp_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: to
     if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 GPU tensor")
     args = head + (_ptr(workspace), workspace.numel(), int(chunk_cols), _stream(dev, stream))
-    if out_dtype == torch.bfloat16:
+    if logits is not None:
+        zp, ldz = _saved_logits(logits, n, width, dev)
+        _check("linear_logp_backward_saved", _lib.linear_logp_backward_saved(
+            float(inv_temperature), zp, ldz, *head, _DTYPE_CODE[out_dtype], *args[-4:]))
+    elif out_dtype == torch.bfloat16:
         _check("linear_logp_backward_bf16",
                _lib.linear_logp_backward_bf16(float(inv_temperature), *args))
     elif inv_temperature == 1.0:

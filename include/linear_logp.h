@@ -43,6 +43,7 @@ extern "C" {
 #define LINEAR_LOGP_MAX_LD 262144      /* largest row stride of hidden and weight (elements) */
 #define LINEAR_LOGP_BWD_MAX_ROWS 8388608    /* largest n of the backward (2^23) */
 #define LINEAR_LOGP_BWD_MAX_CHUNK 1048576   /* largest chunk_cols of the backward (2^20) */
+#define LINEAR_LOGP_MAX_SAVED_LD 2147483648ll  /* largest row stride of kept logits (2^31) */
 
 /* Per-tile partials of the logits h W^T over the vocabulary columns [col_begin, col_end).
  *   hidden        [n, ld_h] BF16 bits; row t at hidden + t*ld_h; H = hidden_size columns used.
@@ -116,6 +117,27 @@ LOGP_API logp_status_t linear_logp_partials_ws(float inv_temperature, const uint
                                                int64_t ignore_index, logp_partial_t* partials,
                                                int64_t ldp, void* workspace,
                                                int64_t workspace_bytes, hipStream_t stream);
+
+/* linear_logp_partials_ws that also keeps the scored logits it forms, so that
+ * linear_logp_backward_saved can read them instead of forming h W^T again: memory for time
+ * (4 bytes per logit, 5.0 GB for 8192 rows of a 151936-column vocabulary).  The same kernels
+ * run, each also writing the scored logits as the forward's reduction reads them, so the
+ * partials are bitwise those of linear_logp_partials_ws.
+ *   logits       [n, ld_logits] FP32, device memory owned by the caller, 16-byte aligned:
+ *                column c of row t receives z = fl32(acc * inv_temperature) of view column c
+ *                for c < vocab_real - col_begin (the view's real columns); no other element
+ *                is written.
+ *   ld_logits    row stride in elements: >= col_end - col_begin, a multiple of 4, at most
+ *                LINEAR_LOGP_MAX_SAVED_LD, and n * ld_logits <= 2^40 (else LOGP_ERR_SHAPE).
+ *   workspace    as in linear_logp_partials_ws; NULL gives the one-kernel launch.
+ * logits must not overlap any other argument (LOGP_ERR_OVERLAP); NULL logits is
+ * LOGP_ERR_NULL.  Every other argument and error as in linear_logp_partials_ws. */
+LOGP_API logp_status_t linear_logp_partials_save(
+    float inv_temperature, const uint16_t* hidden, int64_t ld_h, int64_t n, int64_t hidden_size,
+    const uint16_t* weight, int64_t ld_w, int64_t vocab_real, int64_t vocab_padded,
+    int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
+    int64_t ignore_index, logp_partial_t* partials, int64_t ldp, float* logits,
+    int64_t ld_logits, void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Backward of linear_logp: the gradients of sum over valid rows t of g_t logp_t (logp of the
  * scored logits z = fl32(acc(h W^T) * inv_temperature) of linear_logp_partials_ex) with respect
@@ -196,6 +218,31 @@ LOGP_API logp_status_t linear_logp_backward_bf16(
     int64_t col_begin, int64_t col_end, const int64_t* targets, const uint8_t* active,
     int64_t ignore_index, const float* grad_logp, const logp_stats_t* stats, uint16_t* dhidden,
     int64_t ld_dh, uint16_t* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
+    int64_t chunk_cols, hipStream_t stream);
+/* The backward of linear_logp_backward_ex (out_dtype LOGP_DTYPE_F32) or of
+ * linear_logp_backward_bf16 (LOGP_DTYPE_BF16) from the scored logits that
+ * linear_logp_partials_save kept: dz reads z instead of forming it on the matrix cores again,
+ * so the call runs two of the three products (dh = dz W, dW = dz^T h).  Given the logits the
+ * forward kept for the same hidden, weight, inv_temperature and view, the outputs are bitwise
+ * those of the entry point it stands for, since z is the same value either way.
+ *   logits      [n, ld_logits] FP32, 4-byte aligned: column c of row t holds z of view column
+ *               c (the view's real columns are read); ld_logits >= col_end - col_begin, at
+ *               most LINEAR_LOGP_MAX_SAVED_LD, n * ld_logits <= 2^40 (else LOGP_ERR_SHAPE).
+ *   dhidden, dweight   FP32 (out_dtype LOGP_DTYPE_F32) or BF16 bits (LOGP_DTYPE_BF16), with
+ *               the strides and meaning of the entry point it stands for; any other out_dtype
+ *               is LOGP_ERR_ARG.
+ *   workspace   at least linear_logp_backward_workspace (FP32) or
+ *               linear_logp_backward_bf16_workspace (BF16) bytes for the same n, H and
+ *               chunk_cols.
+ * hidden and weight are still read.  NULL logits is LOGP_ERR_NULL; every other argument and
+ * error as in linear_logp_backward_ex. */
+LOGP_API logp_status_t linear_logp_backward_saved(
+    float inv_temperature, const float* logits, int64_t ld_logits, const uint16_t* hidden,
+    int64_t ld_h, int64_t n, int64_t hidden_size, const uint16_t* weight, int64_t ld_w,
+    int64_t vocab_real, int64_t vocab_padded, int64_t col_begin, int64_t col_end,
+    const int64_t* targets, const uint8_t* active, int64_t ignore_index,
+    const float* grad_logp, const logp_stats_t* stats, void* dhidden, int64_t ld_dh,
+    void* dweight, int64_t ld_dw, int32_t out_dtype, void* workspace, int64_t workspace_bytes,
     int64_t chunk_cols, hipStream_t stream);
 /* linear_logp_backward_ex at inv_temperature = 1. */
 LOGP_API logp_status_t linear_logp_backward(

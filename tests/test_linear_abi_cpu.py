@@ -288,3 +288,70 @@ def test_balanced_partials_workspace_size():
     assert q(0, 100, 0, 4096) == q(1, 100, 0, 4096) == 3072
     assert q(10, 5000, 8192, 12288) == 0                              # an all-padding view
     assert q(-1, 10, 0, 10) == -1 and q(10, 0, 0, 10) == -1 and q(10, 10, 5, 4) == -1
+
+
+def call_save(z=A, ld_z=5000, ws=None, wsb=0, inv_t=1.0, **over):
+    a = dict(h=A, ld_h=64, n=10, H=64, w=A, ld_w=64, vr=5000, vp=5000, c0=0, c1=5000, y=A,
+             act=None, ign=-100, p=A, ldp=2)
+    a.update(over)
+    return lib.linear_logp_partials_save(inv_t, a["h"], a["ld_h"], a["n"], a["H"], a["w"],
+                                         a["ld_w"], a["vr"], a["vp"], a["c0"], a["c1"], a["y"],
+                                         a["act"], a["ign"], a["p"], a["ldp"], z, ld_z, ws, wsb,
+                                         None)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(n=-1), SHAPE), (dict(c0=100), SHARD), (dict(h=None), NULL), (dict(w=U), SHAPE),
+    (dict(ldp=1), SHAPE), (dict(n=0), OK)], ids=lambda v: str(v))
+def test_saving_partials_validate_like_the_plain_entry(over, want):
+    assert call_save(**over) == want == call(**over)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(z=None), NULL), (dict(ld_z=4999), SHAPE), (dict(ld_z=5002), SHAPE),
+    (dict(z=ctypes.c_void_p(0x10008)), SHAPE), (dict(ld_z=(1 << 31) + 4), SHAPE),
+    (dict(ld_z=1 << 31, n=1 << 10), SHAPE), (dict(inv_t=0.0), ARG)], ids=lambda v: str(v))
+def test_saving_partials_check_the_logits_buffer(kw, want):
+    """The kept logits: non-NULL, 16-byte aligned, a row stride of at least the view's width,
+    a multiple of 4, at most LINEAR_LOGP_MAX_SAVED_LD and with n * ld_logits <= 2^40; all
+    checked before any device query (a valid call fails only at the device check here)."""
+    assert call_save(**kw) == want
+    assert call_save() == DEVICE
+
+
+def call_saved_bwd(z=A, ld_z=5000, dt=2, inv_t=1.0, **over):
+    a = dict(h=A, ld_h=64, n=10, H=64, w=A, ld_w=64, vr=5000, vp=5000, c0=0, c1=5000, y=A,
+             act=None, ign=-100, g=A, st=A, dh=A, ld_dh=64, dw=A, ld_dw=64, ws=A,
+             wsb=1 << 40, chunk=4096)
+    a.update(over)
+    return lib.linear_logp_backward_saved(
+        inv_t, z, ld_z, a["h"], a["ld_h"], a["n"], a["H"], a["w"], a["ld_w"], a["vr"], a["vp"],
+        a["c0"], a["c1"], a["y"], a["act"], a["ign"], a["g"], a["st"], a["dh"], a["ld_dh"],
+        a["dw"], a["ld_dw"], dt, a["ws"], a["wsb"], a["chunk"], None)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(n=-1), SHAPE), (dict(c0=100), SHARD), (dict(chunk=4000), SHAPE), (dict(n=0), OK),
+    (dict(h=None), NULL), (dict(dw=None), NULL), (dict(ws=W16), SHAPE), (dict(wsb=1000), SHAPE),
+], ids=lambda v: str(v))
+def test_saved_backward_validates_like_the_workspace_entry(over, want):
+    assert call_saved_bwd(**over) == want == call_bwd(**over)
+    assert call_saved_bwd(dt=0, **over) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(z=None), NULL), (dict(ld_z=4999), SHAPE), (dict(z=ctypes.c_void_p(0x10002)), SHAPE),
+    (dict(ld_z=(1 << 31) + 1), SHAPE), (dict(dt=1), ARG), (dict(dt=7), ARG),
+    (dict(inv_t=float("nan")), ARG)], ids=lambda v: str(v))
+def test_saved_backward_checks_the_logits_and_dtype(kw, want):
+    """The saved logits may be any 4-byte aligned rows (row stride >= the view's width, at
+    most LINEAR_LOGP_MAX_SAVED_LD); out_dtype is FP32 or BF16."""
+    assert call_saved_bwd(**kw) == want
+    assert call_saved_bwd(ld_z=5001) == DEVICE  # any stride >= the width
+    assert call_saved_bwd(dt=0) == DEVICE
+
+
+def test_saved_ld_constant():
+    text = open(os.path.join(ROOT, "include", "linear_logp.h")).read()
+    assert int(re.search(r"#define LINEAR_LOGP_MAX_SAVED_LD (\d+)ll", text).group(1)) == \
+        linear.MAX_SAVED_LD
