@@ -132,6 +132,37 @@ def test_linear_logp_capture():
     check_capture(step, [partials, logp, lse, st, dh, dW])
 
 
+def test_linear_logp_kept_logits_capture():
+    n, H, V = 600, 512, 40000
+    g = torch.Generator(device=DEV).manual_seed(7)
+    h = torch.randn((n, H), generator=g, device=DEV).to(torch.bfloat16)
+    W = (torch.randn((V, H), generator=g, device=DEV) * (2.0 / H ** 0.5)).to(torch.bfloat16)
+    y = torch.randint(0, V, (n,), generator=g, device=DEV)
+    gr = torch.randn(n, generator=g, device=DEV)
+    L = dst.logp_num_tiles(V)
+    partials = torch.empty((n, L, 3), device=DEV)
+    z = torch.empty((n, V), device=DEV)
+    logp, lse = torch.empty(n, device=DEV), torch.empty(n, device=DEV)
+    st = torch.empty((n, 2), device=DEV)
+    ws_f = torch.empty(max(1, linear.linear_logp_partials_workspace(n, V, 0, V)),
+                       dtype=torch.uint8, device=DEV)
+    chunk = 2 * dst.TILE_COLS
+    ws_b = torch.empty(linear.linear_logp_backward_workspace(n, H, chunk, torch.bfloat16),
+                       dtype=torch.uint8, device=DEV)
+    dh = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
+    dW = torch.empty((V, H), dtype=torch.bfloat16, device=DEV)
+    say("linear_logp with kept logits (forward + BF16 backward) under capture")
+
+    def step():
+        linear.linear_logp_forward(h, W, y, V, partials=partials, logp=logp, lse=lse, stats=st,
+                                   workspace=ws_f, logits=z)
+        linear.linear_logp_backward(h, W, y, gr, st, V, chunk_cols=chunk, dhidden=dh,
+                                    dweight=dW, workspace=ws_b, out_dtype=torch.bfloat16,
+                                    logits=z)
+
+    check_capture(step, [partials, logp, lse, st, dh, dW])
+
+
 def test_grpo_loss_capture():
     n, T = 256, 3000
     g = torch.Generator(device=DEV).manual_seed(6)

@@ -14,8 +14,8 @@ test_gpu_linear.py):
   - a random tile-aligned shard layout of the partials merged back bitwise to the forward,
     and the backward of a random column range bitwise equal to that range of the full one;
   - linear_logp's forward against the oracle on every row, the balanced launch bitwise equal
-    to the one-kernel launch, a random shard layout merged back bitwise, and the backward's
-    dh and dW against the oracle;
+    to the one-kernel launch, a random shard layout merged back bitwise, the backward's dh and
+    dW against the oracle, and the kept-logits forward and backward bitwise equal to those;
   - the GRPO loss (random sequences, lengths, row strides, reductions, clip bounds, KL weight,
     ratio spread, masks with empty sequences, global normalizers) against its oracle.
 """
@@ -151,11 +151,25 @@ def test_linear_random_case(seed):
     merged = dst.logp_merge(partials, y, V, active=active)
     assert all(same_bits(u, w) for u, w in zip(got, merged)), layout
 
-    g, _, dh, dW, _ = bwd_run(h, W, y, V, Vp, active=active, inv_t=inv_t, chunk=T, seed=seed)
+    g, stats, dh, dW, ws = bwd_run(h, W, y, V, Vp, active=active, inv_t=inv_t, chunk=T,
+                                   seed=seed)
     bref = bwd_reference(h, W, y, g, V, active=active, inv_t=inv_t)
     bres = check_bwd(h, W, y, g, dh, dW, V, bref)
     if active is not None:
         assert torch.all(dh[active == 0] == 0)
+
+    # kept logits: the same partials, and the backward from them the same bits
+    # rows of the kept logits: a stride that is a multiple of 4 floats (16-byte aligned rows)
+    z = torch.empty((n, (Vp + 3) // 4 * 4), dtype=torch.float32, device=DEV)[:, :Vp]
+    Pz = torch.full((n, L, 3), float("nan"), dtype=torch.float32, device=DEV)
+    linear.linear_logp_partials(h, W, y, V, Vp, 0, Vp, Pz, active=active, inv_temperature=inv_t,
+                                logits=z)
+    assert all(same_bits(u, w) for u, w in zip(got, dst.logp_merge(Pz, y, V, active=active)))
+    dh2, dW2 = linear.linear_logp_backward(h, W, y, g, stats, V, Vp, active=active,
+                                           inv_temperature=inv_t, chunk_cols=T, workspace=ws,
+                                           logits=z)
+    torch.cuda.synchronize()
+    assert same_bits(dh, dh2) and same_bits(dW, dW2)
     say(f"seed={seed}: {res} {bres}")
 
 
