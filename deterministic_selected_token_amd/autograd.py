@@ -66,10 +66,9 @@ class LinearLogp(torch.autograd.Function):
                 inv_temperature, chunk_cols, keep_logits=False):
         from .linear import linear_logp_forward
         z = None
-        if keep_logits:  # rows 16-byte aligned: a row stride that is a multiple of 4 floats
-            V = weight.shape[0]
-            z = torch.empty((hidden.shape[0], (V + 3) // 4 * 4), dtype=torch.float32,
-                            device=hidden.device)[:, :V]
+        if keep_logits:
+            from .linear import kept_logits_buffer
+            z = kept_logits_buffer(hidden.shape[0], weight.shape[0], hidden.device)
         logp, _, stats = linear_logp_forward(hidden, weight, targets, vocab_real,
                                              weight.shape[0], active=active,
                                              ignore_index=ignore_index,

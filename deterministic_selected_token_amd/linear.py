@@ -87,6 +87,13 @@ def _row_stride(t: torch.Tensor) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else int(max(t.shape[1], t.stride(0), 8))
 
 
+def kept_logits_buffer(n: int, width: int, device=None) -> torch.Tensor:
+    """An uninitialised float32 [n, width] tensor laid out as linear_logp_partials(...,
+    logits=) needs: rows 16-byte aligned (a row stride that is a multiple of 4 floats)."""
+    return torch.empty((n, (int(width) + 3) // 4 * 4), dtype=torch.float32,
+                       device=device)[:, :int(width)]
+
+
 def _saved_logits(t: torch.Tensor, n: int, width: int, device) -> tuple:
     """(pointer, row stride) of a float32 [n, >= width] tensor of kept logits with unit column
     stride on ``device``."""
@@ -176,7 +183,8 @@ def linear_logp_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: tor
     whole vocabulary: linear_logp_partials over all tiles, then logp_merge -> (logp, lse,
     stats).  balance=True (the default) passes a workspace, allocated with torch when none is
     given, so that the last rounds spread over every CU; the results are the same bits.
-    ``logits`` (float32 [n, >= vocab_padded]) keeps the scored logits for the backward."""
+    ``logits`` (float32 [n, >= vocab_padded], rows 16-byte aligned: kept_logits_buffer(n,
+    vocab_padded)) keeps the scored logits for the backward."""
     vocab_padded = weight.shape[0] if vocab_padded is None else int(vocab_padded)
     vocab_real = vocab_padded if vocab_real is None else int(vocab_real)
     n = hidden.shape[0]
