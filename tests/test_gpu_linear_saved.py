@@ -163,3 +163,29 @@ def test_autograd_keep_logits_is_bitwise(V):
         grads.append((logp.detach(), h.grad, W.grad))
     for a, b in zip(*grads):
         assert torch.equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("inv_t", [1.0, 1 / 0.7])
+def test_saved_forward_on_vocab_shards(inv_t):
+    """Each tile-aligned shard keeps the logits of its own columns, with column 0 of its
+    buffer at the shard's first column: bitwise the full forward's columns, and the shard's
+    partials bitwise those of the non-keeping call."""
+    n, H, V, Vp = 200, 136, 21000, 21504
+    say(f"saved forward on shards inv_t={inv_t:.3g}")
+    h, W, y = make(n, H, V, Vp, seed=77)
+    zfull = linear.kept_logits_buffer(n, Vp, DEV)
+    P = torch.empty((n, dst.logp_num_tiles(Vp), 3), device=DEV)
+    linear.linear_logp_partials(h, W, y, V, Vp, 0, Vp, P, inv_temperature=inv_t, logits=zfull)
+    for c0, c1 in ((0, T), (T, 3 * T), (3 * T, Vp)):
+        zs = linear.kept_logits_buffer(n, c1 - c0, DEV)
+        zs.fill_(float("nan"))
+        P0 = torch.full_like(P, float("nan"))
+        P1 = torch.full_like(P, float("nan"))
+        linear.linear_logp_partials(h, W[c0:c1], y, V, Vp, c0, c1, P0, inv_temperature=inv_t)
+        linear.linear_logp_partials(h, W[c0:c1], y, V, Vp, c0, c1, P1, inv_temperature=inv_t,
+                                    logits=zs)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(P0), bits(P1)), (c0, c1)
+        real = max(0, min(c1, V) - c0)
+        assert torch.equal(bits(zs[:, :real]), bits(zfull[:, c0:c0 + real])), (c0, c1)
+        assert torch.all(torch.isnan(zs[:, real:])), (c0, c1)
