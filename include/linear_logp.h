@@ -118,7 +118,8 @@ LOGP_API logp_status_t linear_logp_partials_ws(float inv_temperature, const uint
                                                int64_t ldp, void* workspace,
                                                int64_t workspace_bytes, hipStream_t stream);
 
-/* linear_logp_partials_ws that also keeps the scored logits it forms, so that
+/* linear_logp_partials_ws (same source passages as linear_logp_partials: PR #495's Summary
+ * names the fused LM-head logp) that also keeps the scored logits it forms, so that
  * linear_logp_backward_saved can read them instead of forming h W^T again: memory for time
  * (4 bytes per logit, 5.0 GB for 8192 rows of a 151936-column vocabulary).  The same kernels
  * run, each also writing the scored logits as the forward's reduction reads them, so the
@@ -220,7 +221,9 @@ LOGP_API logp_status_t linear_logp_backward_bf16(
     int64_t ld_dh, uint16_t* dweight, int64_t ld_dw, void* workspace, int64_t workspace_bytes,
     int64_t chunk_cols, hipStream_t stream);
 /* The backward of linear_logp_backward_ex (out_dtype LOGP_DTYPE_F32) or of
- * linear_logp_backward_bf16 (LOGP_DTYPE_BF16) from the scored logits that
+ * linear_logp_backward_bf16 (LOGP_DTYPE_BF16) -- the same derivative, from the same passages
+ * (PR #495 "zero-workspace backward for generic CUDA fused logp", Summary) -- from the scored
+ * logits that
  * linear_logp_partials_save kept: dz reads z instead of forming it on the matrix cores again,
  * so the call runs two of the three products (dh = dz W, dW = dz^T h).  Given the logits the
  * forward kept for the same hidden, weight, inv_temperature and view, the outputs are bitwise
