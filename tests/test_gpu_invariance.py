@@ -203,3 +203,25 @@ def test_batch_invariance_sweep(seed):
         f"dlogits {differing_dlogits}")
     assert comparisons == 744
     assert differing_logp == 0 and differing_dlogits == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("inv_t", [1.0, 1 / 0.7])
+@pytest.mark.parametrize("V", [20480, 3001])  # the flat backward grid, the (row, tile) one
+def test_backward_run_to_run_every_dtype_and_path(dtype, inv_t, V):
+    """The backward twice into fresh (uninitialised) buffers, and once in place: the same bits
+    for every logits dtype, with and without temperature, on both backward kernels -- the
+    check that catches a store whose data registers are overwritten before it reads them."""
+    n = 64
+    g = torch.Generator(device=DEV).manual_seed(31)
+    x = (torch.randn((n, V), generator=g, device=DEV) * 3).to(dtype)
+    y = torch.randint(0, V, (n,), generator=g, device=DEV)
+    y[::9] = -100
+    gr = torch.randn(n, generator=g, device=DEV)
+    say(f"backward run to run {dtype} inv_t={inv_t:.3g} V={V}")
+    _, _, st = dst.logp_forward_ex(x, y, inv_temperature=inv_t)
+    outs = [dst.logp_backward_ex(x, y, gr, st, inv_temperature=inv_t) for _ in range(2)]
+    xi = x.clone()
+    dst.logp_backward_ex(xi, y, gr, st, inv_temperature=inv_t, dlogits=xi)
+    torch.cuda.synchronize()
+    assert same_bits(outs[0], outs[1]) and same_bits(outs[0], xi)
